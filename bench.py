@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Throughput of the fused RMSNorm + MRoPE hot path on one MI355X.
+
+One step = one rmsnorm_mrope_qk call over the whole workload (cos/sin from
+positions, per-head RMSNorm, rotation of every q and k head), inputs resident
+in HBM.  Default workload: Omni-like text prefill, q[32768,32,128] and
+k[32768,4,128] bf16, interleaved [24,20,20], theta 1e6, RMSNorm eps 1e-6.
+
+Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
+kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
+bounded sample of the same workload (cpu_baseline).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calib BYTES   # plain device copy, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor peak
+DEFAULT_WORKLOAD = "omni_text_prefill"
+KERNEL_SOURCES = ["vlm_multimodal_rotary_amd/csrc/mrope_kernels.hip",
+                  "vlm_multimodal_rotary_amd/csrc/mrope_api.cpp",
+                  "vlm_multimodal_rotary_amd/csrc/mrope_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, budget_s: float = 12.0):
+    """The oracle as it stands, on consecutive 64-token windows of the same
+    workload, until about budget_s of CPU time; single thread."""
+    from oracle import mrope_oracle as O
+    T = wl.T
+    chunk = 64
+    done = 0
+    start = time.perf_counter()
+    t0 = 0
+    while True:
+        sl = slice(t0, t0 + chunk)
+        O.rmsnorm_mrope_qk(inp["q"][sl], inp["k"][sl], inp["pos"][:, sl],
+                           rotary_dim=wl.rotary_dim, theta=wl.theta, section=wl.section,
+                           layout=wl.layout, wq=inp["wq"] if wl.norm else None,
+                           wk=inp["wk"] if wl.norm else None, eps=wl.eps, dtype=wl.dtype)
+        done += chunk
+        t0 = (t0 + chunk) % (T - chunk + 1)
+        elapsed = time.perf_counter() - start
+        if elapsed >= budget_s:
+            break
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} tokens ({done // chunk} windows of {chunk} consecutive tokens, "
+                      f"all {wl.hq}+{wl.hk} heads) of {wl.name}, {elapsed:.1f} s, one thread"}
+
+
+def copy_calib(nbytes: int, steps: int):
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "steps": steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this hot path has no exchange step, and "
+              "every run here uses a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calib(args.copy_calib, args.steps)
+        return
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import vlm_multimodal_rotary_amd as M
+
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl)
+
+    def dev(a):
+        if a is None:
+            return None
+        if wl.dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    q, k, pos = dev(inp["q"]), dev(inp["k"]), dev(inp["pos"])
+    wq, wk = dev(inp["wq"]), dev(inp["wk"])
+    q_out, k_out = torch.empty_like(q), torch.empty_like(k)
+
+    def step():
+        M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
+                           wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps          # one kernel launch per step
+
+    alg_bytes = wl.algorithmic_bytes()
+    achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+    line = {
+        "metric": "Q+K tokens/s, fused RMSNorm+MRoPE (rmsnorm_mrope_qk)",
+        "value": wl.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normal q/k, N(1,0.1) weights, workload position tables)",
+        "config": {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
+                   "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
+                   "section": list(wl.section), "rmsnorm": wl.norm},
+        "hbm_gbps": achieved_gbps,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "kernel": "qk_kernel<bf16,8,positions,norm>" if wl.dtype == "bf16"
+                     else "qk_kernel<f32,4,positions>"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

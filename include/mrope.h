@@ -1,0 +1,194 @@
+/*
+ * mrope.h — C ABI of the MI355X (gfx950) multimodal rotary position embedding
+ * library: RMSNorm + MRoPE over query/key heads, as used by Qwen3-VL,
+ * Qwen3.5 and Qwen3-Omni style attention.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [RoPE]  "Interleaved Rotary Position Embedding" (RoPE post): the inv_freq
+ *          listing, rotate_half / apply_rotary_pos_emb with partial rotary,
+ *          the interleaved axis selection, get_rope_index.
+ *  [M01]   "M01 · RMSNorm and multimodal RoPE (interleaved / chunked)": the
+ *          function list and shapes, RMSNorm numeric conventions, the
+ *          interleaved rule and the chunked layout, the shape trace.
+ *  [QVL]   "Qwen3-VL" annotated source: the text rotary embedding (fp32
+ *          angles, cat(f, f), cos/sin) and the vision 2-D rotary
+ *          (rot_pos_emb, apply_rotary_pos_emb_vision).
+ *  [Q3V]   cortiq-engine qwen3vis.rs: rope_angles and the split-half
+ *          rotation over the whole vision head.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are token-major, x[T][heads][D] ([M01] shape list: q/k as
+ *    [T, heads, D]).  Heads of one token are contiguous (head stride D); the
+ *    token stride is an argument (in elements, >= heads*D) so views into
+ *    packed buffers work.
+ *  - dtype: MROPE_DTYPE_F32 (binary32) or MROPE_DTYPE_BF16 (bfloat16).
+ *    RMSNorm weights have the dtype of x.  cos/sin tables are binary32.
+ *  - Positions are int32 [n_axes][T] with axis stride pos_axis_stride (in
+ *    elements; 0 broadcasts one 1-D position row to every axis).  |p| must
+ *    be below 2^24 so float(p) is exact.
+ *  - Device buffers are owned by the caller.  The library allocates nothing
+ *    and keeps no state between calls; small tables (section, inv_freq) are
+ *    host pointers copied into kernel arguments.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without synchronising.
+ *  - Outputs may alias their own input exactly (in place).  Any other overlap
+ *    between an output and any input or the other output is MROPE_EINVAL.
+ *  - T == 0 (or no heads) is a valid no-op returning MROPE_OK.
+ *  - Arguments are checked before any HIP call; on a non-zero return nothing
+ *    has been enqueued and mrope_last_error() describes the failure.  There is
+ *    no host fallback.
+ */
+#ifndef MROPE_H_
+#define MROPE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes */
+#define MROPE_OK            0
+#define MROPE_EINVAL       (-1)  /* bad argument: null pointer, shape, section, overlap */
+#define MROPE_EUNSUPPORTED (-2)  /* valid but unsupported: dtype, alignment, size limits */
+#define MROPE_EHIP         (-3)  /* a HIP call failed (launch error, no device) */
+
+/* Frequency-column layouts ([M01] layout table) */
+#define MROPE_LAYOUT_CHUNKED     0  /* TTTT..HHH..WWW: consecutive ranges of section[a] columns */
+#define MROPE_LAYOUT_INTERLEAVED 1  /* THWTHW..TT: j%3==1 && j<3*s_h -> H, j%3==2 && j<3*s_w -> W */
+#define MROPE_LAYOUT_VISION_2D   2  /* first half/2 columns read the row, the rest the column */
+
+#define MROPE_DTYPE_F32  0
+#define MROPE_DTYPE_BF16 1
+
+/* Largest rotary_dim the kernels accept (the per-column table travels as a
+ * kernel argument). */
+#define MROPE_MAX_ROTARY_DIM 512
+
+/*
+ * mrope_inv_freq — inv[i] = theta^(-2i/dim) for i < dim/2, evaluated in
+ * double and rounded once to binary32 ([RoPE] inv_freq listing; [M01]
+ * rope_inv_freq).  Text layouts use dim = rotary_dim (frequencies of the
+ * rotated slice only, [RoPE] partial rotary); the vision layout uses
+ * dim = head_dim/2 ([Q3V] rope_angles: 18 frequencies for a 72-dim head).
+ *   out: host array of dim/2 floats, written.
+ * Host-only: makes no HIP call.  EINVAL if dim <= 0, dim odd, theta <= 0 or
+ * not finite, or out == NULL.
+ */
+int mrope_inv_freq(int dim, double theta, float* out);
+
+/*
+ * mrope_axis_table — the axis each frequency column j < half reads
+ * (0 = T / row, 1 = H / column, 2 = W), per `layout` ([M01] interleaved rule
+ * and chunked table; [QVL] apply_interleaved_mrope; [Q3V] rope_angles).
+ *   section: host array of n_sections ints (chunked: 1..3 entries summing to
+ *            half; interleaved: exactly 3 entries summing to half; vision:
+ *            ignored, may be NULL).
+ *   axis_out: host array of half bytes, written.
+ * Host-only.  EINVAL if half <= 0 or > MROPE_MAX_ROTARY_DIM/2, a section entry
+ * is negative, the section does not sum to half, the interleaved rule cannot
+ * give an axis its section count (3*(s_h-1)+1 >= half or 3*(s_w-1)+2 >= half),
+ * the vision half is odd, or a pointer is NULL.
+ */
+int mrope_axis_table(int half, const int* section, int n_sections, int layout,
+                     uint8_t* axis_out);
+
+/*
+ * mrope_cos_sin — cos/sin tables of shape [T][rotary_dim], binary32
+ * ([M01] mrope_cos_sin(inv_freq, positions[3,T], section, interleaved) and
+ * shape-trace rows 4-7): for column j < half, angle = fl32(float(p) * inv),
+ * p = pos[axis[j]][t]; cos = fl32(cos(angle)), sin = fl32(sin(angle)) with
+ * cos/sin evaluated in double; columns j and j+half hold the same values
+ * (cat(f, f)).
+ *   pos:       device int32, [n_axes][T] with axis stride pos_axis_stride.
+ *   n_axes:    3 (interleaved), 2 (vision), or len(section) (chunked).
+ *   inv_freq:  host binary32, half entries (text layouts) or half/2 entries
+ *              (vision), taken as given (inv = ones runs the axis probe).
+ *   cos_out, sin_out: device binary32, [T][rotary_dim] with token stride
+ *              cs_tok_stride (elements, >= rotary_dim).
+ * EINVAL on a bad section/layout/axes combination, rotary_dim odd or <= 0
+ * or > MROPE_MAX_ROTARY_DIM, null pointers, or overlapping outputs.
+ */
+int mrope_cos_sin(const int32_t* pos, int64_t pos_axis_stride, int n_axes, int64_t T,
+                  const float* inv_freq, const int* section, int n_sections, int layout,
+                  int rotary_dim, float* cos_out, float* sin_out, int64_t cs_tok_stride,
+                  void* stream);
+
+/*
+ * rms_norm — per-head RMSNorm over the last dimension ([M01] numeric
+ * conventions): r = fl32(1/sqrt(sum(x^2)/D + eps)) with the sum of squares
+ * accumulated in double; n = fl32(x*r); cast n to the dtype of x; multiply by
+ * w (one weight vector [D] shared by all heads); cast to the dtype of x.
+ *   x:   device, [T][heads][D], token stride x_tok_stride.
+ *   w:   device, [D], dtype of x.
+ *   out: device, [T][heads][D], token stride out_tok_stride (may equal x).
+ * EINVAL on null pointers, D <= 0 or odd, strides below heads*D, overlap.
+ * EUNSUPPORTED if D is too large for one wavefront per row or the buffers are
+ * not element-aligned.
+ */
+int rms_norm(const void* x, int64_t x_tok_stride, int64_t T, int heads, int D,
+             const void* w, float eps, int dtype, void* out, int64_t out_tok_stride,
+             void* stream);
+
+/*
+ * apply_rotary_qk — split-half rotation of q and k with given cos/sin
+ * ([RoPE] rotate_half / apply_rotary_pos_emb; [M01] apply_rotary with cos/sin
+ * broadcast over heads as [T, 1, D]):
+ *   out[j]      = x[j]*cos[j]      - x[j+h]*sin[j]        (j < h = rotary_dim/2)
+ *   out[j+h]    = x[j+h]*cos[j+h]  + x[j]*sin[j+h]
+ *   out[j]      = x[j]                                    (rotary_dim <= j < D)
+ * computed in double from the stored inputs and the binary32 tables, rounded
+ * once to binary32 and then (bf16) to bfloat16.
+ *   q: device [T][hq][D], token stride q_tok_stride; k likewise with hk heads
+ *      (k may be NULL when hk == 0).
+ *   cos, sin: device binary32 [T][rotary_dim], token stride cs_tok_stride.
+ *   q_out, k_out: device, same shapes, own token strides (may equal q / k).
+ * EINVAL on bad shapes (rotary_dim odd, <= 0 or > D), null pointers, overlap.
+ */
+int apply_rotary_qk(const void* q, int64_t q_tok_stride, int hq,
+                    const void* k, int64_t k_tok_stride, int hk,
+                    int64_t T, int D, int rotary_dim,
+                    const float* cos, const float* sin, int64_t cs_tok_stride,
+                    int dtype,
+                    void* q_out, int64_t q_out_tok_stride,
+                    void* k_out, int64_t k_out_tok_stride,
+                    void* stream);
+
+/*
+ * rmsnorm_mrope_qk — the fused hot path: optional per-head RMSNorm (as
+ * rms_norm, with wq for q heads and wk for k heads), then MRoPE on the first
+ * rotary_dim dims of every q and k head with cos/sin computed in the kernel
+ * from the positions (as mrope_cos_sin with inv_freq = mrope_inv_freq(
+ * rotary_dim, theta) for text layouts, mrope_inv_freq(rotary_dim/2, theta)
+ * reused for row and column for the vision layout), and the rest of each head
+ * passed through ([RoPE] Qwen3.5 attention: q/k norm, then
+ * apply_rotary_pos_emb; [M01] "Where it sits"; [QVL] the vision rotary).
+ * cos/sin are formed once per (token, column) and shared by all hq + hk heads.
+ * The result is bit-identical to rms_norm followed by mrope_cos_sin and
+ * apply_rotary_qk.
+ *   wq, wk: device [D] weights of the dtype; both NULL = no normalisation.
+ *   Other arguments as in the functions above.
+ * EINVAL as above, or if exactly one of wq / wk is NULL.
+ */
+int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq,
+                     const void* k, int64_t k_tok_stride, int hk,
+                     int64_t T, int D, int rotary_dim,
+                     const int32_t* pos, int64_t pos_axis_stride, int n_axes,
+                     const int* section, int n_sections, int layout, double theta,
+                     const void* wq, const void* wk, float eps, int dtype,
+                     void* q_out, int64_t q_out_tok_stride,
+                     void* k_out, int64_t k_out_tok_stride,
+                     void* stream);
+
+/*
+ * mrope_last_error — message for the last non-zero return on this thread
+ * (empty string if none).  The pointer stays valid until the next call on
+ * the same thread.
+ */
+const char* mrope_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MROPE_H_ */

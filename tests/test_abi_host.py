@@ -1,0 +1,211 @@
+"""Host side of the C ABI, on the CPU: the library loads, exports every
+declared entry point, its host tables match the oracle bit for bit, and bad
+arguments are rejected before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import mrope_oracle as O
+import workloads as W
+from vlm_multimodal_rotary_amd import _lib
+import vlm_multimodal_rotary_amd as M
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "mrope.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert declared == sorted(_lib.SIGNATURES), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("dim,theta", [(16, 1e4), (128, 1e6), (64, 1e7), (36, 1e4), (8, 1e4),
+                                       (6, 100.0), (256, 5e5), (512, 1e4), (2, 3.0)])
+def test_inv_freq_matches_oracle_bitwise(dim, theta):
+    assert np.array_equal(M.mrope_inv_freq(dim, theta).view(np.uint32),
+                          O.inv_freq(dim, theta).view(np.uint32))
+
+
+def _valid_interleaved_sections(half):
+    out = []
+    for sh in range(0, half + 1):
+        for sw in range(0, half + 1 - sh):
+            st = half - sh - sw
+            try:
+                O.axis_table(half, (st, sh, sw), "interleaved")
+            except AssertionError:
+                continue
+            out.append((st, sh, sw))
+    return out
+
+
+def test_axis_table_matches_oracle_for_every_valid_interleaved_section():
+    for half in (2, 5, 8, 10, 32, 36, 64):
+        secs = _valid_interleaved_sections(half)
+        assert secs
+        for sec in secs:
+            assert np.array_equal(M.mrope_axis_table(half, sec, "interleaved"),
+                                  O.axis_table(half, sec, "interleaved")), (half, sec)
+
+
+def test_axis_table_rejects_what_the_oracle_rejects():
+    for half in (8, 10, 32):
+        for sh in range(0, half + 1):
+            for sw in range(0, half + 1 - sh):
+                sec = (half - sh - sw, sh, sw)
+                try:
+                    O.axis_table(half, sec, "interleaved")
+                    oracle_ok = True
+                except AssertionError:
+                    oracle_ok = False
+                if oracle_ok:
+                    continue
+                with pytest.raises(_lib.MropeError) as e:
+                    M.mrope_axis_table(half, sec, "interleaved")
+                assert e.value.code == _lib.MROPE_EINVAL
+
+
+def test_axis_table_chunked_and_vision():
+    for half, sec in [(64, (16, 24, 24)), (10, (4, 3, 3)), (8, (8,)), (8, (3, 5))]:
+        assert np.array_equal(M.mrope_axis_table(half, sec, "chunked"),
+                              O.axis_table(half, sec, "chunked"))
+    assert np.array_equal(M.mrope_axis_table(36, None, "vision_2d"),
+                          O.axis_table(36, None, "vision_2d"))
+    with pytest.raises(_lib.MropeError):
+        M.mrope_axis_table(8, (4, 3, 3), "chunked")          # sum != half
+    with pytest.raises(_lib.MropeError):
+        M.mrope_axis_table(7, None, "vision_2d")             # odd half
+
+
+# -- argument checks of the device entry points (rejected before any HIP call) --
+
+FAKE = 0x10000000  # never dereferenced: every call below fails its checks first
+
+
+def _no_gpu():
+    """The fake-pointer calls below must never reach a launch; on a machine
+    with a visible GPU they are skipped outright."""
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except ImportError:
+        return True
+
+
+fake_ptr_test = pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: CPU-only check")
+
+
+def _fused(**kw):
+    args = dict(q=FAKE, q_ts=32 * 128, hq=32, k=FAKE + 0x4000000, k_ts=4 * 128, hk=4, T=16,
+                D=128, rd=128, pos=FAKE + 0x8000000, pos_stride=16, n_axes=3,
+                section=(24, 20, 20), layout=_lib.LAYOUT_INTERLEAVED, theta=1e6,
+                wq=FAKE + 0xC000000, wk=FAKE + 0xC001000, eps=1e-6, dtype=_lib.DTYPE_BF16,
+                qo=FAKE + 0x20000000, qo_ts=32 * 128, ko=FAKE + 0x24000000, ko_ts=4 * 128)
+    args.update(kw)
+    a = args
+    sec = list(a["section"]) if a["section"] is not None else []
+    return _lib.load().rmsnorm_mrope_qk(
+        a["q"], a["q_ts"], a["hq"], a["k"], a["k_ts"], a["hk"], a["T"], a["D"], a["rd"],
+        a["pos"], a["pos_stride"], a["n_axes"], _lib.int_array(sec), len(sec), a["layout"],
+        a["theta"], a["wq"], a["wk"], a["eps"], a["dtype"], a["qo"], a["qo_ts"], a["ko"],
+        a["ko_ts"], None)
+
+
+@fake_ptr_test
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.MROPE_EUNSUPPORTED),
+    (dict(rd=127), _lib.MROPE_EINVAL),
+    (dict(rd=256), _lib.MROPE_EINVAL),               # > D
+    (dict(D=127, rd=126), _lib.MROPE_EINVAL),        # odd D
+    (dict(section=(24, 20, 21)), _lib.MROPE_EINVAL), # sum != half
+    (dict(section=(4, 40, 20)), _lib.MROPE_EINVAL),  # rule cannot place 40 H columns
+    (dict(n_axes=2), _lib.MROPE_EINVAL),
+    (dict(layout=9), _lib.MROPE_EINVAL),
+    (dict(q=0), _lib.MROPE_EINVAL),
+    (dict(pos=0), _lib.MROPE_EINVAL),
+    (dict(wk=0), _lib.MROPE_EINVAL),                 # one weight only
+    (dict(q_ts=100), _lib.MROPE_EINVAL),             # token stride < heads*D
+    (dict(theta=0.0), _lib.MROPE_EINVAL),
+    (dict(theta=float("nan")), _lib.MROPE_EINVAL),
+    (dict(eps=-1.0), _lib.MROPE_EINVAL),
+    (dict(T=-1), _lib.MROPE_EINVAL),
+    (dict(hq=-2), _lib.MROPE_EINVAL),
+    (dict(qo=FAKE + 64), _lib.MROPE_EINVAL),         # q_out partially overlaps q
+    (dict(ko=FAKE + 16), _lib.MROPE_EINVAL),         # k_out overlaps q
+    (dict(ko=FAKE + 0x20000000 + 256), _lib.MROPE_EINVAL),   # k_out overlaps q_out
+    (dict(qo=FAKE + 0x8000000), _lib.MROPE_EINVAL),  # q_out overlaps positions
+    (dict(q=FAKE + 1, qo=FAKE + 0x20000001), _lib.MROPE_EUNSUPPORTED),  # odd address, bf16
+    (dict(rd=1024, D=1024), _lib.MROPE_EUNSUPPORTED),
+    # vision layout with an odd number of frequency columns (half = 35)
+    (dict(layout=_lib.LAYOUT_VISION_2D, n_axes=2, section=None, D=70, rd=70, q_ts=32 * 70,
+          k_ts=4 * 70, qo_ts=32 * 70, ko_ts=4 * 70), _lib.MROPE_EINVAL),
+])
+def test_fused_rejects_bad_arguments(kw, code):
+    rc = _fused(**kw)
+    assert rc == code, (rc, _lib.load().mrope_last_error())
+    assert _lib.load().mrope_last_error()
+
+
+@fake_ptr_test
+def test_fused_T_zero_is_a_noop():
+    assert _fused(T=0) == _lib.MROPE_OK
+    assert _fused(T=0, q=0, k=0, qo=0, ko=0, pos=0) == _lib.MROPE_OK
+
+
+@fake_ptr_test
+def test_in_place_alias_is_allowed_by_the_checks():
+    # exact alias passes every check; with T = 0 nothing is launched
+    assert _fused(T=0, qo=FAKE, ko=FAKE + 0x4000000) == _lib.MROPE_OK
+
+
+@fake_ptr_test
+def test_rms_norm_and_apply_rotary_reject_bad_arguments():
+    lib = _lib.load()
+    rc = lib.rms_norm(FAKE, 128, 4, 1, 128, None, 1e-6, _lib.DTYPE_BF16, FAKE + 0x100000, 128, None)
+    assert rc == _lib.MROPE_EINVAL                     # no weight
+    rc = lib.rms_norm(FAKE, 128, 4, 1, 127, FAKE + 0x200000, 1e-6, _lib.DTYPE_BF16,
+                      FAKE + 0x100000, 127, None)
+    assert rc == _lib.MROPE_EINVAL                     # odd D
+    rc = lib.apply_rotary_qk(FAKE, 128, 1, None, 0, 0, 4, 128, 128, None, None, 128,
+                             _lib.DTYPE_F32, FAKE + 0x100000, 128, None, 0, None)
+    assert rc == _lib.MROPE_EINVAL                     # no cos/sin
+    rc = lib.apply_rotary_qk(FAKE, 128, 1, None, 0, 0, 4, 128, 128, FAKE + 0x300000,
+                             FAKE + 0x100000, 128, _lib.DTYPE_F32, FAKE + 0x100000, 128, None,
+                             0, None)
+    assert rc == _lib.MROPE_EINVAL                     # q_out overlaps sin
+
+
+@fake_ptr_test
+def test_cos_sin_rejects_bad_arguments():
+    lib = _lib.load()
+    inv = _lib.float_array([1.0] * 4)
+    sec = _lib.int_array([4, 2, 2])
+    rc = lib.mrope_cos_sin(FAKE, 16, 2, 16, inv, sec, 3, _lib.LAYOUT_INTERLEAVED, 16,
+                           FAKE + 0x1000, FAKE + 0x2000, 16, None)
+    assert rc == _lib.MROPE_EINVAL                     # n_axes != 3
+    rc = lib.mrope_cos_sin(FAKE, 16, 3, 16, inv, sec, 3, _lib.LAYOUT_INTERLEAVED, 16,
+                           FAKE + 0x1000, FAKE + 0x1010, 16, None)
+    assert rc == _lib.MROPE_EINVAL                     # cos and sin overlap
+    rc = lib.mrope_cos_sin(FAKE, 16, 3, 0, inv, sec, 3, _lib.LAYOUT_INTERLEAVED, 16,
+                           FAKE + 0x1000, FAKE + 0x2000, 16, None)
+    assert rc == _lib.MROPE_OK                         # T = 0: nothing to do
+
+
+def test_binding_builds_no_cpu_path():
+    # The binding has no CPU implementation to fall back on: a CPU tensor is
+    # handed to the library as a host pointer only through these wrappers,
+    # which always call the HIP entry points.
+    import inspect
+    src = inspect.getsource(M)
+    assert "oracle" not in src and "numpy.cos" not in src and "np.cos" not in src

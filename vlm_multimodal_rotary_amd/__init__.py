@@ -1,0 +1,152 @@
+"""Python binding of the MI355X multimodal rotary library (libmrope.so).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI in include/mrope.h.  Tensors are torch device tensors, token-major
+[T, heads, D] with contiguous heads (any token stride); work is enqueued on
+torch's current stream.  There is no CPU path: calling these without the
+built library or without a GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, MropeError, check, float_array,  # noqa: F401
+                   int_array, load)
+
+__all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "rms_norm",
+           "apply_rotary_qk", "rmsnorm_mrope_qk", "MropeError", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise MropeError(_lib.MROPE_EUNSUPPORTED, f"unsupported dtype {t.dtype}")
+
+
+def _layout_code(layout) -> int:
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _heads_view(x, name):
+    """Check a [T, heads, D] view with contiguous heads; return its token stride."""
+    if x.dim() != 3:
+        raise MropeError(_lib.MROPE_EINVAL, f"{name} must be [T, heads, D], got {tuple(x.shape)}")
+    T, H, D = x.shape
+    if D > 0 and x.stride(2) != 1 and D > 1:
+        raise MropeError(_lib.MROPE_EINVAL, f"{name} last dim must be contiguous")
+    if H > 1 and x.stride(1) != D:
+        raise MropeError(_lib.MROPE_EINVAL, f"{name} heads must be contiguous (stride D)")
+    return x.stride(0) if T > 1 else H * D
+
+
+def mrope_inv_freq(dim: int, theta: float) -> np.ndarray:
+    """theta^(-2i/dim) for i < dim/2 as float32 (host)."""
+    out = np.zeros(max(1, dim // 2), dtype=np.float32)
+    check(load().mrope_inv_freq(int(dim), float(theta),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return out[: dim // 2]
+
+
+def mrope_axis_table(half: int, section, layout) -> np.ndarray:
+    """Axis (0/1/2) read by each frequency column j < half (host)."""
+    out = np.zeros(max(1, half), dtype=np.uint8)
+    sec = list(section) if section is not None else []
+    check(load().mrope_axis_table(int(half), int_array(sec), len(sec), _layout_code(layout),
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
+    return out[:half]
+
+
+def mrope_cos_sin(pos, inv_freq, section, layout, rotary_dim: int, cos_out=None, sin_out=None):
+    """cos, sin [T, rotary_dim] float32 on pos's device from int32 positions [n_axes, T]."""
+    torch = _torch()
+    n_axes, T = pos.shape
+    if pos.dtype != torch.int32:
+        raise MropeError(_lib.MROPE_EINVAL, "positions must be int32")
+    if cos_out is None:
+        cos_out = torch.empty((T, rotary_dim), dtype=torch.float32, device=pos.device)
+    if sin_out is None:
+        sin_out = torch.empty((T, rotary_dim), dtype=torch.float32, device=pos.device)
+    sec = list(section) if section is not None else []
+    inv = float_array(np.asarray(inv_freq, dtype=np.float32).reshape(-1))
+    pos_stride = pos.stride(0) if n_axes > 1 else T
+    if T > 0 and pos.stride(1) != 1:
+        raise MropeError(_lib.MROPE_EINVAL, "positions must be contiguous along T")
+    check(load().mrope_cos_sin(_ptr(pos), pos_stride, n_axes, T, inv, int_array(sec), len(sec),
+                               _layout_code(layout), int(rotary_dim), _ptr(cos_out),
+                               _ptr(sin_out), cos_out.stride(0) if T > 0 else rotary_dim,
+                               _stream(pos)))
+    return cos_out, sin_out
+
+
+def rms_norm(x, w, eps: float, out=None):
+    """Per-head RMSNorm of x [T, heads, D] with weight w [D] (dtype of x)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    T, H, D = x.shape
+    check(load().rms_norm(_ptr(x), _heads_view(x, "x"), T, H, D, _ptr(w), float(eps),
+                          _dtype_code(x), _ptr(out), _heads_view(out, "out"), _stream(x)))
+    return out
+
+
+def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, q_out=None, k_out=None):
+    """Split-half rotation of q [T, hq, D] and k [T, hk, D] with cos/sin [T, rotary_dim]."""
+    torch = _torch()
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    T, hq, D = q.shape
+    hk = k.shape[1]
+    check(load().apply_rotary_qk(_ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"),
+                                 hk, T, D, int(rotary_dim), _ptr(cos), _ptr(sin),
+                                 cos.stride(0) if T > 0 else rotary_dim, _dtype_code(q),
+                                 _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out),
+                                 _heads_view(k_out, "k_out"), _stream(q)))
+    return q_out, k_out
+
+
+def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
+                     wq=None, wk=None, eps: float = 1e-6, q_out=None, k_out=None):
+    """Fused per-head RMSNorm (if weights are given) + MRoPE on q and k.
+
+    pos: int32 [n_axes, T] on the device (3 axes for interleaved, 2 for
+    vision_2d, len(section) for chunked).
+    """
+    torch = _torch()
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    T, hq, D = q.shape
+    hk = k.shape[1]
+    n_axes = pos.shape[0]
+    if pos.dtype != torch.int32:
+        raise MropeError(_lib.MROPE_EINVAL, "positions must be int32")
+    if T > 0 and pos.stride(1) != 1:
+        raise MropeError(_lib.MROPE_EINVAL, "positions must be contiguous along T")
+    pos_stride = pos.stride(0) if n_axes > 1 else T
+    sec = list(section) if section is not None else []
+    check(load().rmsnorm_mrope_qk(
+        _ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"), hk, T, D,
+        int(rotary_dim), _ptr(pos), pos_stride, n_axes, int_array(sec), len(sec),
+        _layout_code(layout), float(theta), _ptr(wq), _ptr(wk), float(eps), _dtype_code(q),
+        _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out), _heads_view(k_out, "k_out"),
+        _stream(q)))
+    return q_out, k_out

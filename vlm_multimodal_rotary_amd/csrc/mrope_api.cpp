@@ -1,0 +1,488 @@
+// C-ABI entry points: argument checking, the per-column frequency/axis table,
+// launch geometry, and the kernel launches.  Every check runs before the first
+// HIP call, so an invalid call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "mrope_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MROPE_OK;
+}
+
+// Byte extent of a [T][heads][D] view with the given token stride.
+struct Extent {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+Extent extent_of(const void* base, int64_t T, int64_t tok_stride, int64_t row_elems,
+                 int elem_bytes) {
+  Extent e;
+  if (base == nullptr || T <= 0 || row_elems <= 0) return e;
+  e.lo = reinterpret_cast<uintptr_t>(base);
+  e.hi = e.lo + (uintptr_t)(((T - 1) * tok_stride + row_elems) * elem_bytes);
+  return e;
+}
+
+bool overlaps(const Extent& a, const Extent& b) {
+  if (a.empty() || b.empty()) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// An output may equal its own input exactly (same base and stride); any other
+// overlap is rejected.
+bool bad_alias(const Extent& out, const Extent& in, bool same_view) {
+  return overlaps(out, in) && !same_view;
+}
+
+int elem_bytes_of(int dtype) { return dtype == MROPE_DTYPE_BF16 ? 2 : 4; }
+
+int check_dtype(int dtype) {
+  if (dtype != MROPE_DTYPE_F32 && dtype != MROPE_DTYPE_BF16)
+    return fail(MROPE_EUNSUPPORTED, "dtype %d is not MROPE_DTYPE_F32 (0) or MROPE_DTYPE_BF16 (1)",
+                dtype);
+  return MROPE_OK;
+}
+
+// inv[i] = theta^(-2i/dim), double evaluation rounded once.
+void fill_inv(int dim, double theta, float* out) {
+  for (int i = 0; i < dim / 2; ++i) out[i] = (float)std::pow(theta, -(2.0 * i) / (double)dim);
+}
+
+int build_axis(int half, const int* section, int n_sections, int layout, uint8_t* axis) {
+  if (half <= 0 || half > mrope::kMaxHalf)
+    return fail(MROPE_EINVAL, "half = %d outside [1, %d]", half, mrope::kMaxHalf);
+  if (layout == MROPE_LAYOUT_VISION_2D) {
+    if (half % 2 != 0) return fail(MROPE_EINVAL, "vision layout needs an even half, got %d", half);
+    for (int j = 0; j < half; ++j) axis[j] = (uint8_t)(j < half / 2 ? 0 : 1);
+    return MROPE_OK;
+  }
+  if (layout != MROPE_LAYOUT_CHUNKED && layout != MROPE_LAYOUT_INTERLEAVED)
+    return fail(MROPE_EINVAL, "unknown layout %d", layout);
+  if (section == nullptr) return fail(MROPE_EINVAL, "section is NULL");
+  if (layout == MROPE_LAYOUT_INTERLEAVED && n_sections != 3)
+    return fail(MROPE_EINVAL, "interleaved layout needs 3 section entries, got %d", n_sections);
+  if (n_sections < 1 || n_sections > 3)
+    return fail(MROPE_EINVAL, "chunked layout needs 1..3 section entries, got %d", n_sections);
+  int sum = 0;
+  for (int a = 0; a < n_sections; ++a) {
+    if (section[a] < 0) return fail(MROPE_EINVAL, "section[%d] = %d is negative", a, section[a]);
+    sum += section[a];
+  }
+  if (sum != half)
+    return fail(MROPE_EINVAL, "section sums to %d, rotary_dim/2 is %d", sum, half);
+  if (layout == MROPE_LAYOUT_CHUNKED) {
+    int j = 0;
+    for (int a = 0; a < n_sections; ++a)
+      for (int c = 0; c < section[a]; ++c) axis[j++] = (uint8_t)a;
+    return MROPE_OK;
+  }
+  // Interleaved: H on j % 3 == 1 below 3*s_h, W on j % 3 == 2 below 3*s_w,
+  // T elsewhere.  The rule places every H and W column only if the last one
+  // falls inside [0, half).
+  const int sh = section[1], sw = section[2];
+  if (sh > 0 && 3 * (sh - 1) + 1 >= half)
+    return fail(MROPE_EINVAL, "interleaved section [%d,%d,%d]: H column %d is past half = %d",
+                section[0], sh, sw, 3 * (sh - 1) + 1, half);
+  if (sw > 0 && 3 * (sw - 1) + 2 >= half)
+    return fail(MROPE_EINVAL, "interleaved section [%d,%d,%d]: W column %d is past half = %d",
+                section[0], sh, sw, 3 * (sw - 1) + 2, half);
+  for (int j = 0; j < half; ++j) {
+    uint8_t a = 0;
+    if (j % 3 == 1 && j < 3 * sh) a = 1;
+    else if (j % 3 == 2 && j < 3 * sw) a = 2;
+    axis[j] = a;
+  }
+  return MROPE_OK;
+}
+
+int expected_axes(int layout, int n_sections) {
+  if (layout == MROPE_LAYOUT_INTERLEAVED) return 3;
+  if (layout == MROPE_LAYOUT_VISION_2D) return 2;
+  return n_sections;
+}
+
+// Column table of the fused path: inverse frequency per column and its axis.
+int build_table(int rotary_dim, double theta, const int* section, int n_sections, int layout,
+                const float* inv_given, mrope::ColTable& tab) {
+  const int half = rotary_dim / 2;
+  int rc = build_axis(half, section, n_sections, layout, tab.axis);
+  if (rc) return rc;
+  if (inv_given != nullptr) {
+    for (int j = 0; j < half; ++j)
+      tab.inv[j] = layout == MROPE_LAYOUT_VISION_2D ? inv_given[j % (half / 2)] : inv_given[j];
+    return MROPE_OK;
+  }
+  if (layout == MROPE_LAYOUT_VISION_2D) {
+    float inv[mrope::kMaxHalf / 2];
+    fill_inv(half, theta, inv);
+    for (int j = 0; j < half; ++j) tab.inv[j] = inv[j % (half / 2)];
+  } else {
+    fill_inv(rotary_dim, theta, tab.inv);
+  }
+  return MROPE_OK;
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+// Largest chunk (elements) that keeps every access aligned and the lane
+// mapping exact: rotary chunks tile [0, half), pass-through lanes own two
+// chunks of [rd, D).
+int pick_vec(int dtype, int D, int rd, const void* const* ptrs, int nptrs,
+             const int64_t* strides, int nstrides) {
+  const int es = elem_bytes_of(dtype);
+  const int max_v = 16 / es;
+  const int half = rd / 2;
+  for (int v = max_v; v >= 1; v /= 2) {
+    if (D % (2 * v) != 0) continue;
+    if (half % v != 0) continue;
+    if ((D - rd) % (2 * v) != 0) continue;
+    if (D / (2 * v) > mrope::kWaveSize) continue;
+    bool good = true;
+    for (int i = 0; i < nptrs && good; ++i)
+      if (ptrs[i] != nullptr && (reinterpret_cast<uintptr_t>(ptrs[i]) % (uintptr_t)(v * es)) != 0)
+        good = false;
+    for (int i = 0; i < nstrides && good; ++i)
+      if (strides[i] % v != 0) good = false;
+    if (good) return v;
+  }
+  return 0;
+}
+
+struct QKArgs {
+  const void* x[2];
+  int64_t x_ts[2];
+  int heads[2];
+  void* y[2];
+  int64_t y_ts[2];
+  const void* w[2];
+  int64_t T;
+  int D, rd, dtype;
+};
+
+int check_qk_tensors(const QKArgs& a, bool need_rd) {
+  int rc = check_dtype(a.dtype);
+  if (rc) return rc;
+  if (a.T < 0) return fail(MROPE_EINVAL, "T = %lld is negative", (long long)a.T);
+  if (a.D <= 0 || a.D % 2 != 0) return fail(MROPE_EINVAL, "D = %d must be positive and even", a.D);
+  if (need_rd) {
+    if (a.rd <= 0 || a.rd % 2 != 0 || a.rd > a.D)
+      return fail(MROPE_EINVAL, "rotary_dim = %d must be even, positive and <= D = %d", a.rd, a.D);
+    if (a.rd > MROPE_MAX_ROTARY_DIM)
+      return fail(MROPE_EUNSUPPORTED, "rotary_dim = %d exceeds %d", a.rd, MROPE_MAX_ROTARY_DIM);
+  }
+  const char* nm[2] = {"q", "k"};
+  for (int s = 0; s < 2; ++s) {
+    if (a.heads[s] < 0) return fail(MROPE_EINVAL, "%s heads = %d is negative", nm[s], a.heads[s]);
+    if (a.heads[s] == 0 || a.T == 0) continue;
+    if (a.x[s] == nullptr) return fail(MROPE_EINVAL, "%s input is NULL", nm[s]);
+    if (a.y[s] == nullptr) return fail(MROPE_EINVAL, "%s output is NULL", nm[s]);
+    const int64_t row = (int64_t)a.heads[s] * a.D;
+    if (a.x_ts[s] < row)
+      return fail(MROPE_EINVAL, "%s token stride %lld < heads*D = %lld", nm[s],
+                  (long long)a.x_ts[s], (long long)row);
+    if (a.y_ts[s] < row)
+      return fail(MROPE_EINVAL, "%s output token stride %lld < heads*D = %lld", nm[s],
+                  (long long)a.y_ts[s], (long long)row);
+  }
+  // Overlap rules.
+  const int es = elem_bytes_of(a.dtype);
+  Extent xin[2], yout[2];
+  for (int s = 0; s < 2; ++s) {
+    const bool live = a.heads[s] > 0 && a.T > 0;
+    const int64_t row = (int64_t)a.heads[s] * a.D;
+    if (live) {
+      xin[s] = extent_of(a.x[s], a.T, a.x_ts[s], row, es);
+      yout[s] = extent_of(a.y[s], a.T, a.y_ts[s], row, es);
+    }
+  }
+  for (int s = 0; s < 2; ++s) {
+    const bool same = a.x[s] == a.y[s] && a.x_ts[s] == a.y_ts[s];
+    if (bad_alias(yout[s], xin[s], same))
+      return fail(MROPE_EINVAL, "%s output partially overlaps its input", nm[s]);
+    if (overlaps(yout[s], xin[1 - s]))
+      return fail(MROPE_EINVAL, "%s output overlaps the %s input", nm[s], nm[1 - s]);
+  }
+  if (overlaps(yout[0], yout[1])) return fail(MROPE_EINVAL, "q and k outputs overlap");
+  for (int s = 0; s < 2; ++s) {
+    if (a.w[s] == nullptr) continue;
+    Extent we = extent_of(a.w[s], 1, a.D, a.D, es);
+    for (int o = 0; o < 2; ++o)
+      if (overlaps(yout[o], we)) return fail(MROPE_EINVAL, "an output overlaps a weight vector");
+  }
+  return MROPE_OK;
+}
+
+// Launch geometry and the remaining per-launch fields.
+int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
+           const int32_t* pos, int64_t pos_stride, const float* cos, const float* sin,
+           int64_t cs_ts, float eps, void* stream, const Extent* extra, int n_extra) {
+  const int es = elem_bytes_of(a.dtype);
+  const void* ptrs[6] = {a.x[0], a.x[1], a.y[0], a.y[1], a.w[0], a.w[1]};
+  int64_t strides[4] = {a.x_ts[0], a.x_ts[1], a.y_ts[0], a.y_ts[1]};
+  const int v = pick_vec(a.dtype, a.D, a.rd, ptrs, 6, strides, 4);
+  if (v == 0)
+    return fail(MROPE_EUNSUPPORTED,
+                "no vector width fits D = %d, rotary_dim = %d and the buffer alignment "
+                "(need element-aligned pointers and D/2 lanes or fewer per row)",
+                a.D, a.rd);
+  for (int i = 0; i < n_extra; ++i)
+    for (int o = 0; o < 2; ++o)
+      if (a.heads[o] > 0 &&
+          overlaps(extent_of(a.y[o], a.T, a.y_ts[o], (int64_t)a.heads[o] * a.D, es), extra[i]))
+        return fail(MROPE_EINVAL, "an output overlaps a positions or cos/sin buffer");
+  if (a.T == 0 || a.heads[0] + a.heads[1] == 0) return ok();
+
+  mrope::QKParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int s = 0; s < 2; ++s) {
+    p.x[s] = a.x[s];
+    p.y[s] = a.y[s];
+    p.w[s] = a.w[s];
+    p.x_ts[s] = a.x_ts[s];
+    p.y_ts[s] = a.y_ts[s];
+    p.heads[s] = a.heads[s];
+  }
+  p.T = a.T;
+  p.D = a.D;
+  p.rd = a.rd;
+  p.half = a.rd / 2;
+  p.lpr = a.D / (2 * v);
+  p.rpw = mrope::kWaveSize / p.lpr;
+  p.lrot = p.half / v;
+  p.pos = pos;
+  p.pos_stride = pos_stride;
+  p.cos = cos;
+  p.sin = sin;
+  p.cs_ts = cs_ts;
+  p.eps = eps;
+  p.inv_d = 1.0 / (double)a.D;
+
+  // Tokens per tile: enough wavefronts to fill the chip (16 per CU), at most
+  // 1024 / half tokens so a wavefront's cos/sin slice stays within 8 KB.
+  const int64_t target_waves = (int64_t)device_cu_count() * 16;
+  int64_t nt = (a.T + target_waves - 1) / target_waves;
+  int64_t nt_max = p.half > 0 ? 1024 / p.half : 64;
+  if (nt_max < 1) nt_max = 1;
+  if (nt_max > 64) nt_max = 64;
+  if (nt > nt_max) nt = nt_max;
+  if (nt < 1) nt = 1;
+  p.nt = (int)nt;
+  p.ntiles = (a.T + nt - 1) / nt;
+  const int64_t blocks = (p.ntiles + mrope::kWavesPerBlock - 1) / mrope::kWavesPerBlock;
+  const int grid = (int)(blocks < 1048576 ? blocks : 1048576);
+  const int lds = cs_mode == mrope::kCsFromPositions
+                      ? mrope::kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(float)
+                      : 0;
+  const int hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, p, tab, grid, lds, stream);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mrope_inv_freq(int dim, double theta, float* out) {
+  if (out == nullptr) return fail(MROPE_EINVAL, "out is NULL");
+  if (dim <= 0 || dim % 2 != 0) return fail(MROPE_EINVAL, "dim = %d must be positive and even", dim);
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(MROPE_EINVAL, "theta must be positive and finite");
+  fill_inv(dim, theta, out);
+  return ok();
+}
+
+int mrope_axis_table(int half, const int* section, int n_sections, int layout,
+                     uint8_t* axis_out) {
+  if (axis_out == nullptr) return fail(MROPE_EINVAL, "axis_out is NULL");
+  const int rc = build_axis(half, section, n_sections, layout, axis_out);
+  return rc ? rc : ok();
+}
+
+int mrope_cos_sin(const int32_t* pos, int64_t pos_axis_stride, int n_axes, int64_t T,
+                  const float* inv_freq, const int* section, int n_sections, int layout,
+                  int rotary_dim, float* cos_out, float* sin_out, int64_t cs_tok_stride,
+                  void* stream) {
+  if (T < 0) return fail(MROPE_EINVAL, "T is negative");
+  if (rotary_dim <= 0 || rotary_dim % 2 != 0)
+    return fail(MROPE_EINVAL, "rotary_dim = %d must be positive and even", rotary_dim);
+  if (rotary_dim > MROPE_MAX_ROTARY_DIM)
+    return fail(MROPE_EUNSUPPORTED, "rotary_dim = %d exceeds %d", rotary_dim, MROPE_MAX_ROTARY_DIM);
+  if (inv_freq == nullptr) return fail(MROPE_EINVAL, "inv_freq is NULL");
+  mrope::ColTable tab;
+  int rc = build_table(rotary_dim, 0.0, section, n_sections, layout, inv_freq, tab);
+  if (rc) return rc;
+  if (n_axes != expected_axes(layout, n_sections))
+    return fail(MROPE_EINVAL, "n_axes = %d does not match the layout (%d)", n_axes,
+                expected_axes(layout, n_sections));
+  if (pos_axis_stride < 0) return fail(MROPE_EINVAL, "pos_axis_stride is negative");
+  if (cs_tok_stride < rotary_dim)
+    return fail(MROPE_EINVAL, "cs_tok_stride %lld < rotary_dim %d", (long long)cs_tok_stride,
+                rotary_dim);
+  if (T == 0) return ok();
+  if (pos == nullptr || cos_out == nullptr || sin_out == nullptr)
+    return fail(MROPE_EINVAL, "pos, cos_out and sin_out must be non-NULL");
+  const Extent ce = extent_of(cos_out, T, cs_tok_stride, rotary_dim, 4);
+  const Extent se = extent_of(sin_out, T, cs_tok_stride, rotary_dim, 4);
+  const Extent pe = extent_of(pos, n_axes, pos_axis_stride, T, 4);
+  if (overlaps(ce, se) || overlaps(ce, pe) || overlaps(se, pe))
+    return fail(MROPE_EINVAL, "cos_out, sin_out and pos must not overlap");
+  mrope::CosSinParams p;
+  p.pos = pos;
+  p.pos_stride = pos_axis_stride;
+  p.T = T;
+  p.half = rotary_dim / 2;
+  p.rd = rotary_dim;
+  p.cos = cos_out;
+  p.sin = sin_out;
+  p.cs_ts = cs_tok_stride;
+  const int hrc = mrope::launch_cos_sin(p, tab, stream);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
+}
+
+int rms_norm(const void* x, int64_t x_tok_stride, int64_t T, int heads, int D, const void* w,
+             float eps, int dtype, void* out, int64_t out_tok_stride, void* stream) {
+  QKArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x[0] = x;
+  a.x_ts[0] = x_tok_stride;
+  a.heads[0] = heads;
+  a.y[0] = out;
+  a.y_ts[0] = out_tok_stride;
+  a.w[0] = w;
+  a.T = T;
+  a.D = D;
+  a.rd = 0;
+  a.dtype = dtype;
+  int rc = check_qk_tensors(a, false);
+  if (rc) return rc;
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(MROPE_EINVAL, "eps must be finite and >= 0");
+  if (T > 0 && heads > 0 && w == nullptr) return fail(MROPE_EINVAL, "w is NULL");
+  mrope::ColTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  return run_qk(a, mrope::kCsNone, true, tab, nullptr, 0, nullptr, nullptr, 0, eps, stream,
+                nullptr, 0);
+}
+
+int apply_rotary_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
+                    int64_t k_tok_stride, int hk, int64_t T, int D, int rotary_dim,
+                    const float* cos, const float* sin, int64_t cs_tok_stride, int dtype,
+                    void* q_out, int64_t q_out_tok_stride, void* k_out,
+                    int64_t k_out_tok_stride, void* stream) {
+  QKArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x[0] = q;
+  a.x[1] = k;
+  a.x_ts[0] = q_tok_stride;
+  a.x_ts[1] = k_tok_stride;
+  a.heads[0] = hq;
+  a.heads[1] = hk;
+  a.y[0] = q_out;
+  a.y[1] = k_out;
+  a.y_ts[0] = q_out_tok_stride;
+  a.y_ts[1] = k_out_tok_stride;
+  a.T = T;
+  a.D = D;
+  a.rd = rotary_dim;
+  a.dtype = dtype;
+  int rc = check_qk_tensors(a, true);
+  if (rc) return rc;
+  if (cs_tok_stride < rotary_dim)
+    return fail(MROPE_EINVAL, "cs_tok_stride %lld < rotary_dim %d", (long long)cs_tok_stride,
+                rotary_dim);
+  if (T > 0 && hq + hk > 0 && (cos == nullptr || sin == nullptr))
+    return fail(MROPE_EINVAL, "cos and sin must be non-NULL");
+  Extent extra[2] = {extent_of(cos, T, cs_tok_stride, rotary_dim, 4),
+                     extent_of(sin, T, cs_tok_stride, rotary_dim, 4)};
+  mrope::ColTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  return run_qk(a, mrope::kCsFromTable, false, tab, nullptr, 0, cos, sin, cs_tok_stride, 0.0f,
+                stream, extra, 2);
+}
+
+int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
+                     int64_t k_tok_stride, int hk, int64_t T, int D, int rotary_dim,
+                     const int32_t* pos, int64_t pos_axis_stride, int n_axes,
+                     const int* section, int n_sections, int layout, double theta,
+                     const void* wq, const void* wk, float eps, int dtype, void* q_out,
+                     int64_t q_out_tok_stride, void* k_out, int64_t k_out_tok_stride,
+                     void* stream) {
+  QKArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x[0] = q;
+  a.x[1] = k;
+  a.x_ts[0] = q_tok_stride;
+  a.x_ts[1] = k_tok_stride;
+  a.heads[0] = hq;
+  a.heads[1] = hk;
+  a.y[0] = q_out;
+  a.y[1] = k_out;
+  a.y_ts[0] = q_out_tok_stride;
+  a.y_ts[1] = k_out_tok_stride;
+  a.w[0] = wq;
+  a.w[1] = wk;
+  a.T = T;
+  a.D = D;
+  a.rd = rotary_dim;
+  a.dtype = dtype;
+  int rc = check_qk_tensors(a, true);
+  if (rc) return rc;
+  if ((wq == nullptr) != (wk == nullptr))
+    return fail(MROPE_EINVAL, "wq and wk must both be given or both be NULL");
+  const bool norm = wq != nullptr;
+  if (norm && (!std::isfinite(eps) || eps < 0.0f))
+    return fail(MROPE_EINVAL, "eps must be finite and >= 0");
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(MROPE_EINVAL, "theta must be positive and finite");
+  mrope::ColTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  rc = build_table(rotary_dim, theta, section, n_sections, layout, nullptr, tab);
+  if (rc) return rc;
+  if (n_axes != expected_axes(layout, n_sections))
+    return fail(MROPE_EINVAL, "n_axes = %d does not match the layout (%d)", n_axes,
+                expected_axes(layout, n_sections));
+  if (pos_axis_stride < 0) return fail(MROPE_EINVAL, "pos_axis_stride is negative");
+  if (T > 0 && hq + hk > 0 && pos == nullptr) return fail(MROPE_EINVAL, "pos is NULL");
+  Extent extra[1] = {extent_of(pos, n_axes, pos_axis_stride, T, 4)};
+  return run_qk(a, mrope::kCsFromPositions, norm, tab, pos, pos_axis_stride, nullptr, nullptr, 0,
+                eps, stream, extra, 1);
+}
+
+const char* mrope_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

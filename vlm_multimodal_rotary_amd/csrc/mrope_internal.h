@@ -1,0 +1,74 @@
+// Internal types shared by the host entry points and the HIP kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/mrope.h"
+
+namespace mrope {
+
+constexpr int kMaxHalf = MROPE_MAX_ROTARY_DIM / 2;
+constexpr int kWaveSize = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
+
+// Per frequency column j < half: the binary32 inverse frequency it multiplies
+// and the position axis it reads.  Passed by value as a kernel argument; the
+// kernels index it per lane, which the compiler turns into vector loads from
+// the kernel-argument segment.
+struct ColTable {
+  float inv[kMaxHalf];
+  uint8_t axis[kMaxHalf];
+};
+
+// How the cos/sin of a row's token are obtained.
+enum CsMode : int {
+  kCsFromPositions = 0,  // computed per tile from positions (fused path)
+  kCsFromTable = 1,      // read from caller cos/sin tables [T][rotary_dim]
+  kCsNone = 2,           // no rotation (RMSNorm only)
+};
+
+// One launch processes up to two tensors (slot 0 = q, slot 1 = k) that share
+// T, D, rotary_dim and the per-token cos/sin.
+struct QKParams {
+  const void* x[2];
+  void* y[2];
+  const void* w[2];      // RMSNorm weights (dtype of x) or null
+  int64_t x_ts[2];       // token strides, elements
+  int64_t y_ts[2];
+  int heads[2];
+  int64_t T;
+  int D;
+  int rd;                // rotary dim (0 for RMSNorm only)
+  int half;              // rd / 2
+  int lpr;               // lanes per head row: D / (2 * V)
+  int rpw;               // rows per wavefront instruction: 64 / lpr
+  int lrot;              // rotary lanes per row: half / V
+  int nt;                // tokens per tile (one tile per wavefront step)
+  int64_t ntiles;
+  const int32_t* pos;
+  int64_t pos_stride;
+  const float* cos;
+  const float* sin;
+  int64_t cs_ts;
+  float eps;
+  double inv_d;          // 1.0 / D
+};
+
+struct CosSinParams {
+  const int32_t* pos;
+  int64_t pos_stride;
+  int64_t T;
+  int half;
+  int rd;
+  float* cos;
+  float* sin;
+  int64_t cs_ts;
+};
+
+// Launchers (mrope_kernels.hip).  Return a hipError_t value as int.
+int launch_qk(int dtype, int vec, int cs_mode, bool norm, const QKParams& p,
+              const ColTable& tab, int grid, int lds_bytes, void* stream);
+int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
+
+}  // namespace mrope

@@ -199,14 +199,15 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
-def make_inputs(wl: Workload | str, T: int | None = None, seed: int | None = None) -> dict:
+def make_inputs(wl: Workload | str, T: int | None = None, seed: int | None = None,
+                pos_offset: int = 0) -> dict:
     """Seeded inputs for a workload.
 
-    ``T`` (optional) truncates the token count for small parity runs: the
+    ``T`` (optional) shrinks the token count for small parity runs: the
     random tensors are then drawn at the smaller shape, and positions are the
-    first T columns of the full table (tiny_mrope draws its own).  Returns a
-    dict with q, k (uint16 bf16 bits or float32), wq, wk (or None), pos
-    (int32 [n_axes, T]) and the workload record.
+    columns [pos_offset, pos_offset + T) of the full table (tiny_mrope draws
+    its own).  Returns a dict with q, k (uint16 bf16 bits or float32), wq, wk
+    (or None), pos (int32 [n_axes, T]) and the workload record.
     """
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
@@ -222,7 +223,8 @@ def make_inputs(wl: Workload | str, T: int | None = None, seed: int | None = Non
     if wl.name == "tiny_mrope":
         pos = rng.integers(0, 32, size=(3, T)).astype(np.int32)
     else:
-        pos = workload_positions(wl)[:, :T]
+        pos = workload_positions(wl)[:, pos_offset:pos_offset + T]
+        assert pos.shape[1] == T, "pos_offset + T exceeds the workload"
     out = dict(q=_store(q, wl.dtype), k=_store(k, wl.dtype),
                wq=None if wq is None else _store(wq, wl.dtype),
                wk=None if wk is None else _store(wk, wl.dtype),
