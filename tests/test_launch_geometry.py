@@ -26,27 +26,37 @@ def pick_vec(es, D, rd, aligned_bytes=16, strides=()):
     return 0
 
 
-def plan(T, D, rd, es, cus=256, fused=True):
+WAVE_TOKENS = 1   # tokens per wavefront at most (MROPE_WAVE_TOKENS)
+OUT_OF_RANGE = 0x80000000
+
+
+def plan(T, D, rd, es, fused=True, wave_tokens=WAVE_TOKENS):
     v = pick_vec(es, D, rd)
     assert v, (D, rd, es)
     half = rd // 2
     lpr = D // (2 * v)
     rpw = WAVE // lpr
     lrot = half // v
-    target = cus * 16
-    nt = (T + target - 1) // target
-    nt_max = max(1, min(64, 1024 // half)) if half else 64
-    nt = max(1, min(nt, nt_max))
-    ntiles = (T + nt - 1) // nt
-    grid = min((ntiles + WPB - 1) // WPB, 1048576)
-    lds_floats_per_wave = 2 * nt * half if fused else 0
-    return dict(v=v, half=half, lpr=lpr, rpw=rpw, lrot=lrot, nt=nt, ntiles=ntiles, grid=grid,
-                lds_floats=lds_floats_per_wave)
+    nt_cap = max(1, min(16, 512 // half)) if half else 16
+    nt = max(1, min(nt_cap, wave_tokens))
+    waves = -(-T // nt)
+    return dict(v=v, half=half, lpr=lpr, rpw=rpw, lrot=lrot, nt=nt, nwaves=waves,
+                lds_doubles=2 * nt * half if fused else 0)
 
 
-def simulate(T, heads, D, rd, es, fused=True, U=4):
+def first_row_split(grp, H):
+    """The kernel's grp / H through a binary32 reciprocal, corrected once."""
+    tl = int(np.float32(np.float32(grp) * np.float32(np.float32(1.0) / np.float32(H))))
+    if tl * H > grp:
+        tl -= 1
+    if (tl + 1) * H <= grp:
+        tl += 1
+    return tl, grp - tl * H
+
+
+def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS):
     """Returns per-slot write counts of q/k outputs; asserts read bounds."""
-    p = plan(T, D, rd, es, fused=fused)
+    p = plan(T, D, rd, es, fused=fused, wave_tokens=wave_tokens)
     v, half, lpr, rpw, lrot, nt = p["v"], p["half"], p["lpr"], p["rpw"], p["lrot"], p["nt"]
     writes = [np.zeros((T, H, D), dtype=np.int32) for H in heads]
     lanes = np.arange(WAVE)
@@ -56,43 +66,63 @@ def simulate(T, heads, D, rd, es, fused=True, U=4):
     col_a = np.where(l < lrot, l * v, rd + (l - lrot) * v)
     col_b = np.where(l < lrot, half + l * v, rd + (lpr - lrot + (l - lrot)) * v)
     assert np.all(col_a + v <= D) and np.all(col_b + v <= D)
-    wstride = p["grid"] * WPB
-    for wave0 in range(min(wstride, p["ntiles"])):
-        for tile in range(wave0, p["ntiles"], wstride):
-            t0 = tile * nt
-            ntok = min(nt, T - t0)
-            if fused:
-                n = ntok * half
-                assert n <= p["lds_floats"] // 2
-            for s, H in enumerate(heads):
-                if H == 0:
-                    continue
-                nrows = ntok * H
-                tl = grp // H
-                h = grp - tl * H
-                dq, dr = rpw // H, rpw % H
-                for r0 in range(0, nrows, U * rpw):
-                    for u in range(U):
-                        r = r0 + u * rpw + grp
-                        ok = lane_on & (r < nrows)
-                        # the incremental (token, head) equals the division
-                        assert np.all(tl[ok] == r[ok] // H) and np.all(h[ok] == r[ok] % H)
-                        tok = t0 + tl
-                        assert np.all(tok[ok] < T) and np.all(h[ok] < H)
-                        tlr = np.where(ok, tl, 0)
-                        if fused:
-                            rot = l < lrot
-                            o = tlr * half + col_a
-                            assert np.all(o[rot] + v <= nt * half)
-                        for i in np.nonzero(ok)[0]:
-                            writes[s][tok[i], h[i], col_a[i]:col_a[i] + v] += 1
-                            writes[s][tok[i], h[i], col_b[i]:col_b[i] + v] += 1
-                        h = h + dr
-                        tl = tl + dq
-                        wrap = h >= H
-                        h = np.where(wrap, h - H, h)
-                        tl = np.where(wrap, tl + 1, tl)
+    xts = [H * D + 8 * v for H in heads]          # a token stride wider than the rows
+    for w in range(p["nwaves"]):
+        t0 = w * nt
+        assert t0 < T
+        ntok = min(nt, T - t0)
+        if fused:
+            assert ntok * half <= p["lds_doubles"] // 2
+        for s, H in enumerate(heads):
+            if H == 0:
+                continue
+            extent = ((ntok - 1) * xts[s] + H * D) * es   # tile buffer size in bytes
+            assert extent < OUT_OF_RANGE
+            nrows = ntok * H
+            split = [first_row_split(int(g), H) for g in grp]
+            tl = np.array([a for a, _ in split])
+            h = np.array([b for _, b in split])
+            assert np.all(tl == grp // H) and np.all(h == grp % H)
+            dq, dr = rpw // H, rpw % H
+            xo = (tl * xts[s] + h * D) * es
+            xinc = (dq * xts[s] + dr * D) * es
+            xwrap = (xts[s] - H * D) * es
+            steps = -(-nrows // rpw)
+            full = steps // U
+            batches = [U] * full + [1] * (steps - full * U)
+            r0 = 0
+            for uu in batches:
+                for u in range(uu):
+                    r = r0 + u * rpw + grp
+                    ok = lane_on & (r < nrows)
+                    assert np.all(tl[ok] == r[ok] // H) and np.all(h[ok] == r[ok] % H)
+                    off = np.where(ok, xo, OUT_OF_RANGE)
+                    # live rows stay inside the tile buffer, masked ones outside it
+                    assert np.all(off[ok] + col_b[ok] * es + v * es <= extent)
+                    assert np.all(off[~ok] >= extent)
+                    tlr = np.where(ok, tl, 0)
+                    if fused:
+                        o = tlr * half + col_a
+                        assert np.all(o[l < lrot] + v <= nt * half)
+                    for i in np.nonzero(ok)[0]:
+                        tok = t0 + tl[i]
+                        writes[s][tok, h[i], col_a[i]:col_a[i] + v] += 1
+                        writes[s][tok, h[i], col_b[i]:col_b[i] + v] += 1
+                    xo = xo + xinc
+                    h = h + dr
+                    tl = tl + dq
+                    wrap = h >= H
+                    h = np.where(wrap, h - H, h)
+                    tl = np.where(wrap, tl + 1, tl)
+                    xo = np.where(wrap, xo + xwrap, xo)
+                r0 += uu * rpw
     return writes, p
+
+
+def test_first_row_split_exact_for_all_head_counts():
+    for H in range(1, 4097):
+        for g in range(64):
+            assert first_row_split(g, H) == (g // H, g % H), (g, H)
 
 
 GEOMS = [
@@ -114,13 +144,14 @@ GEOMS = [
 ]
 
 
+@pytest.mark.parametrize("U,wave_tokens", [(1, 1), (2, 1), (4, 2), (2, 16)])
 @pytest.mark.parametrize("T,heads,D,rd,es", GEOMS)
-def test_every_output_written_once_and_reads_in_bounds(T, heads, D, rd, es):
-    writes, p = simulate(T, heads, D, rd, es)
+def test_every_output_written_once_and_reads_in_bounds(T, heads, D, rd, es, U, wave_tokens):
+    writes, p = simulate(T, heads, D, rd, es, U=U, wave_tokens=wave_tokens)
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))
-    assert p["lds_floats"] * WPB * 4 <= 32 * 1024
+    assert p["lds_doubles"] * WPB * 8 <= 32 * 1024
 
 
 def test_rms_norm_only_geometry():
@@ -133,5 +164,5 @@ def test_rms_norm_only_geometry():
 def test_full_size_plans():
     for name, wl in W.WORKLOADS.items():
         p = plan(wl.T, wl.D, wl.rotary_dim, wl.elem_bytes)
-        assert p["ntiles"] * p["nt"] >= wl.T > (p["ntiles"] - 1) * p["nt"]
-        assert p["lds_floats"] * WPB * 4 <= 32 * 1024
+        assert p["nwaves"] * p["nt"] >= wl.T > (p["nwaves"] - 1) * p["nt"]
+        assert p["lds_doubles"] * WPB * 8 <= 32 * 1024

@@ -52,7 +52,9 @@ def _heads_view(x, name):
     if x.dim() != 3:
         raise MropeError(_lib.MROPE_EINVAL, f"{name} must be [T, heads, D], got {tuple(x.shape)}")
     T, H, D = x.shape
-    if D > 0 and x.stride(2) != 1 and D > 1:
+    if x.numel() == 0:
+        return H * D
+    if D > 1 and x.stride(2) != 1:
         raise MropeError(_lib.MROPE_EINVAL, f"{name} last dim must be contiguous")
     if H > 1 and x.stride(1) != D:
         raise MropeError(_lib.MROPE_EINVAL, f"{name} heads must be contiguous (stride D)")

@@ -144,19 +144,6 @@ int build_table(int rotary_dim, double theta, const int* section, int n_sections
   return MROPE_OK;
 }
 
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  if (dev < 64) cached[dev] = cus;
-  return cus;
-}
-
 // Largest chunk (elements) that keeps every access aligned and the lane
 // mapping exact: rotary chunks tile [0, half), pass-through lanes own two
 // chunks of [rd, D).
@@ -290,23 +277,24 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   p.eps = eps;
   p.inv_d = 1.0 / (double)a.D;
 
-  // Tokens per tile: enough wavefronts to fill the chip (16 per CU), at most
-  // 1024 / half tokens so a wavefront's cos/sin slice stays within 8 KB.
-  const int64_t target_waves = (int64_t)device_cu_count() * 16;
-  int64_t nt = (a.T + target_waves - 1) / target_waves;
-  int64_t nt_max = p.half > 0 ? 1024 / p.half : 64;
-  if (nt_max < 1) nt_max = 1;
-  if (nt_max > 64) nt_max = 64;
-  if (nt > nt_max) nt = nt_max;
-  if (nt < 1) nt = 1;
-  p.nt = (int)nt;
-  p.ntiles = (a.T + nt - 1) / nt;
-  const int64_t blocks = (p.ntiles + mrope::kWavesPerBlock - 1) / mrope::kWavesPerBlock;
-  const int grid = (int)(blocks < 1048576 ? blocks : 1048576);
-  const int lds = cs_mode == mrope::kCsFromPositions
-                      ? mrope::kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(float)
-                      : 0;
-  const int hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, p, tab, grid, lds, stream);
+  // Tokens per tile: a wavefront's cos/sin slice (2 * nt * half doubles)
+  // stays within 8 KB.
+  int nt_cap = p.half > 0 ? 512 / p.half : 16;
+  if (nt_cap < 1) nt_cap = 1;
+  if (nt_cap > 16) nt_cap = 16;
+  // The kernels address a tile of each tensor through a buffer descriptor
+  // with 32-bit byte offsets: a tile's extent must stay below 2^31 bytes.
+  for (int s = 0; s < 2; ++s) {
+    if (a.heads[s] == 0) continue;
+    const int64_t row = (int64_t)a.heads[s] * a.D;
+    for (const int64_t ts : {a.x_ts[s], a.y_ts[s]}) {
+      while (nt_cap > 1 && ((int64_t)(nt_cap - 1) * ts + row) * es >= (int64_t(1) << 31)) --nt_cap;
+      if ((ts + row) * es >= (int64_t(1) << 31))
+        return fail(MROPE_EUNSUPPORTED, "a token stride of %lld elements is too large",
+                    (long long)ts);
+    }
+  }
+  const int hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, p, tab, nt_cap, stream);
   if (hrc != (int)hipSuccess)
     return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
   return ok();

@@ -44,8 +44,9 @@ struct QKParams {
   int lpr;               // lanes per head row: D / (2 * V)
   int rpw;               // rows per wavefront instruction: 64 / lpr
   int lrot;              // rotary lanes per row: half / V
-  int nt;                // tokens per tile (one tile per wavefront step)
-  int64_t ntiles;
+  int nt;                // tokens per wavefront (set by the launcher)
+  int dq[2], dr[2];      // rpw = dq * heads + dr, per tensor (launcher)
+  float inv_heads[2];    // 1 / heads, per tensor (launcher)
   const int32_t* pos;
   int64_t pos_stride;
   const float* cos;
@@ -67,8 +68,10 @@ struct CosSinParams {
 };
 
 // Launchers (mrope_kernels.hip).  Return a hipError_t value as int.
+// nt_cap bounds the tokens per wavefront (its cos/sin LDS slice holds
+// 2 * nt * half doubles, and a tile's byte extent must fit 31 bits).
 int launch_qk(int dtype, int vec, int cs_mode, bool norm, const QKParams& p,
-              const ColTable& tab, int grid, int lds_bytes, void* stream);
+              const ColTable& tab, int nt_cap, void* stream);
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
 
 }  // namespace mrope

@@ -30,6 +30,25 @@
 
 #include "mrope_internal.h"
 
+// Row-steps whose loads are issued together, per lane, by element type.
+#ifndef MROPE_ROWS_IN_FLIGHT_BF16
+#define MROPE_ROWS_IN_FLIGHT_BF16 2
+#endif
+#ifndef MROPE_ROWS_IN_FLIGHT_F32
+#define MROPE_ROWS_IN_FLIGHT_F32 4
+#endif
+// Non-temporal (streaming) hint on the row stores, by element type.
+#ifndef MROPE_NT_STORES_BF16
+#define MROPE_NT_STORES_BF16 1
+#endif
+#ifndef MROPE_NT_STORES_F32
+#define MROPE_NT_STORES_F32 0
+#endif
+// Tokens per wavefront (at most; fewer when a token's cos/sin is large).
+#ifndef MROPE_WAVE_TOKENS
+#define MROPE_WAVE_TOKENS 1
+#endif
+
 namespace mrope {
 namespace {
 
@@ -88,11 +107,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Round two binary32 values to bfloat16 in place (kept as binary32).
-__device__ __forceinline__ void round_bf16_pair(float& a, float& b) {
-  const uint32_t u = pack_bf16(a, b);
-  a = bf_lo(u);
-  b = bf_hi(u);
+// Round a binary32 value to bfloat16, kept as binary32: converting the pair
+// (0, x) puts bf16(x) in the high half over a zero low half, which is the
+// binary32 pattern of bf16(x) -- one v_cvt_pk_bf16_f32, no unpacking.
+__device__ __forceinline__ float round_bf16(float x) {
+  return __builtin_bit_cast(float, pack_bf16(0.0f, x));
 }
 
 template <bool BF16, int V>
@@ -131,14 +150,10 @@ __device__ __forceinline__ void pack(const float (&x)[V], Words<(BF16 ? 2 : 4) *
 // Round the 2V values of a lane (two chunks) to bfloat16, kept as binary32.
 template <int V>
 __device__ __forceinline__ void round_bf16_chunks(float (&a)[V], float (&b)[V]) {
-  if constexpr (V == 1) {
-    round_bf16_pair(a[0], b[0]);
-  } else {
 #pragma unroll
-    for (int i = 0; i < V; i += 2) {
-      round_bf16_pair(a[i], a[i + 1]);
-      round_bf16_pair(b[i], b[i + 1]);
-    }
+  for (int i = 0; i < V; ++i) {
+    a[i] = round_bf16(a[i]);
+    b[i] = round_bf16(b[i]);
   }
 }
 
@@ -151,8 +166,10 @@ __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
   int lo = (int)(uint32_t)u;
   int hi = (int)(uint32_t)(u >> 32);
-  lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
-  hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
+  // Every lane of these patterns reads an active lane, so no fill value is
+  // needed (bound_ctrl set).
+  lo = __builtin_amdgcn_mov_dpp(lo, CTRL, 0xF, 0xF, true);
+  hi = __builtin_amdgcn_mov_dpp(hi, CTRL, 0xF, 0xF, true);
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 
@@ -203,24 +220,214 @@ __device__ __forceinline__ void angle_cos_sin(int32_t pos, float inv, float& c, 
 // The q/k kernel.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int V, int CS, bool NORM>
+// Cross-lane float64 sum over the LPR lanes of a row (LPR a power of two
+// known at compile time), or over p.lpr lanes when LPR == 0.
+template <int LPR>
+__device__ __forceinline__ double row_sum(double v, int lpr) {
+  if constexpr (LPR == 0) {
+    return group_sum(v, lpr);
+  } else {
+    if constexpr (LPR >= 2) v += dpp_f64<0xB1>(v);
+    if constexpr (LPR >= 4) v += dpp_f64<0x4E>(v);
+    if constexpr (LPR >= 8) v += dpp_f64<0x141>(v);
+    if constexpr (LPR >= 16) v += dpp_f64<0x140>(v);
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
+    if constexpr (LPR >= 64) v += __shfl_xor(v, 32);
+    return v;
+  }
+}
+
+// Raw buffer access.  A descriptor covers one tile of one tensor; an offset
+// past its range makes a load return zeros and drops a store in hardware, so
+// masked rows issue the same instructions as live ones with no branch around
+// them (which also keeps the compiler's memory-counter waits exact).
+constexpr int kBufferWord3 = 0x00020000;    // gfx9 raw buffer, dword data
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
+}
+
+template <int CB>
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t rs, uint32_t off, Words<CB>& r) {
+  if constexpr (CB == 16) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (CB == 8) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else if constexpr (CB == 4) {
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+  } else {
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+  }
+}
+
+template <bool BF16, int CB>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                          const Words<CB>& r) {
+  // aux 2: non-temporal (streaming) store
+  constexpr int aux = (BF16 ? MROPE_NT_STORES_BF16 : MROPE_NT_STORES_F32) ? 2 : 0;
+  if constexpr (CB == 16) {
+    const u32x4_t v = {r.w[0], r.w[1], r.w[2], r.w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, aux);
+  } else if constexpr (CB == 8) {
+    const u32x2_t v = {r.w[0], r.w[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, aux);
+  } else if constexpr (CB == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, aux);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)r.w[0], rs, off, 0, aux);
+  }
+}
+
+// Per-tensor state of one tile while its rows are processed.
+template <int CB>
+struct SlotState {
+  __amdgpu_buffer_rsrc_t rx, ry;  // tile-local buffers of input and output
+  uint32_t xo, yo;                // byte offsets of this lane's next row
+  uint32_t xinc, yinc;            // advance by rpw rows ...
+  uint32_t xwrap, ywrap;          // ... plus this when the head index wraps
+  int tl, h;                      // token (in tile) and head of the next row
+  int dq, dr;                     // rpw = dq * H + dr
+  int H, nrows;
+};
+
+// Loads UU row-steps (two chunks per lane each), then finishes them in order:
+// RMSNorm, rotation, stores.  Rows past the tile read and write through the
+// out-of-range offset, so the memory operations per call are static.
+template <bool BF16, int V, int CS, bool NORM, int LPR, int UU, typename CsT>
+__device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st, int r0,
+                                              const QKParams& p, int grp, int rpw, int lpr,
+                                              bool lane_on, bool rot, uint32_t ca, uint32_t cb,
+                                              int col_a, const float (&wa)[V],
+                                              const float (&wb)[V], const CsT* lc,
+                                              const CsT* ls, int64_t t0) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int CB = ES * V;
+  Words<CB> ra[UU], rb[UU];
+  int tlu[UU];
+  bool ok[UU];
+  uint32_t you[UU];
+#pragma unroll
+  for (int u = 0; u < UU; ++u) {
+    const int r = r0 + u * rpw + grp;
+    ok[u] = lane_on && r < st.nrows;
+    tlu[u] = st.tl;
+    you[u] = ok[u] ? st.yo : kOutOfRange;
+    const uint32_t xoff = ok[u] ? st.xo : kOutOfRange;
+    buf_load<CB>(st.rx, xoff + ca, ra[u]);
+    buf_load<CB>(st.rx, xoff + cb, rb[u]);
+    st.xo += st.xinc;
+    st.yo += st.yinc;
+    st.h += st.dr;
+    st.tl += st.dq;
+    if (st.h >= st.H) {
+      st.h -= st.H;
+      ++st.tl;
+      st.xo += st.xwrap;
+      st.yo += st.ywrap;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UU; ++u) {
+    float a[V], b[V];
+    unpack<BF16, V>(ra[u], a);
+    unpack<BF16, V>(rb[u], b);
+
+    if constexpr (NORM) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        ss = __builtin_fma((double)a[i], (double)a[i], ss);
+        ss = __builtin_fma((double)b[i], (double)b[i], ss);
+      }
+      ss = row_sum<LPR>(ss, lpr);
+      const float rs = rsqrt_to_f32(ss * p.inv_d + (double)p.eps);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        a[i] = a[i] * rs;
+        b[i] = b[i] * rs;
+      }
+      if constexpr (BF16) round_bf16_chunks<V>(a, b);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        a[i] = a[i] * wa[i];
+        b[i] = b[i] * wb[i];
+      }
+      if constexpr (BF16) round_bf16_chunks<V>(a, b);
+    }
+
+    if constexpr (CS != kCsNone) {
+      if (rot) {
+        // Rows past the tile's end read the cos/sin of the tile's first
+        // token, so every read stays inside the LDS slice / caller tables.
+        const int tlr = ok[u] ? tlu[u] : 0;
+        double ca_[V], sa_[V], cb_[V], sb_[V];
+        if constexpr (CS == kCsFromPositions) {
+          const int o = tlr * p.half + col_a;
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            ca_[i] = (double)lc[o + i];
+            sa_[i] = (double)ls[o + i];
+            cb_[i] = ca_[i];
+            sb_[i] = sa_[i];
+          }
+        } else {
+          const int64_t o = (t0 + tlr) * p.cs_ts + col_a;
+          const int64_t ob = o - col_a + (int64_t)(cb / ES);
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            ca_[i] = (double)p.cos[o + i];
+            sa_[i] = (double)p.sin[o + i];
+            cb_[i] = (double)p.cos[ob + i];
+            sb_[i] = (double)p.sin[ob + i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const double y1 = a[i];
+          const double y2 = b[i];
+          const double o1 = __builtin_fma(y1, ca_[i], -(y2 * sa_[i]));
+          const double o2 = __builtin_fma(y2, cb_[i], y1 * sb_[i]);
+          a[i] = (float)o1;
+          b[i] = (float)o2;
+        }
+      }
+    }
+
+    Words<CB> wa_out, wb_out;
+    pack<BF16, V>(a, wa_out);
+    pack<BF16, V>(b, wb_out);
+    buf_store<BF16, CB>(st.ry, you[u] + ca, wa_out);
+    buf_store<BF16, CB>(st.ry, you[u] + cb, wb_out);
+  }
+}
+
+// Wavefront w owns the tile of tokens [w*nt, w*nt + nt): first the tile's
+// cos/sin (in its LDS slice), then the tile's q rows and k rows, U row-steps
+// per batch of loads.  Wavefronts are short-lived and many; the hardware
+// overlaps them, and the chip's active window of rows stays contiguous.
+template <bool BF16, int V, int CS, bool NORM, int LPR>
 __global__ void __launch_bounds__(kBlockThreads)
 qk_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int CB = ES * V;
-  constexpr int U = 4;  // rows in flight per lane
-  extern __shared__ float lds[];
+  constexpr int U = BF16 ? MROPE_ROWS_IN_FLIGHT_BF16 : MROPE_ROWS_IN_FLIGHT_F32;
+  typedef double cs_t;
+  extern __shared__ double lds[];
 
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wib = threadIdx.x / kWaveSize;
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int half = p.half;
-  float* lc = lds + wib * (2 * p.nt * half);
-  float* ls = lc + p.nt * half;
+  cs_t* lc = lds + wib * (2 * p.nt * half);
+  cs_t* ls = lc + p.nt * half;
 
-  const int lpr = p.lpr;
+  const int lpr = LPR > 0 ? LPR : p.lpr;
+  const int rpw = LPR > 0 ? kWaveSize / LPR : p.rpw;
   const int grp = lane / lpr;
   const int l = lane - grp * lpr;
-  const bool lane_on = grp < p.rpw;
+  const bool lane_on = grp < rpw;
   const bool rot = (CS != kCsNone) && (l < p.lrot);
   int col_a, col_b;
   if (l < p.lrot) {
@@ -232,20 +439,24 @@ qk_kernel(const QKParams p, const ColTable tab) {
     col_a = p.rd + m * V;
     col_b = p.rd + (npass + m) * V;
   }
+  const uint32_t ca = (uint32_t)(col_a * ES);
+  const uint32_t cb = (uint32_t)(col_b * ES);
 
-  const int64_t wstride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t tile = (int64_t)blockIdx.x * kWavesPerBlock + wib; tile < p.ntiles;
-       tile += wstride) {
-    const int64_t t0 = tile * p.nt;
-    const int ntok = (int)((p.T - t0) < p.nt ? (p.T - t0) : p.nt);
-
+  // This wavefront's tile: tokens [t0, t0 + ntok).
+  const int64_t t0 = ((int64_t)blockIdx.x * kWavesPerBlock + wib) * p.nt;
+  if (t0 >= p.T) return;
+  const int ntok = (int)((p.T - t0) < p.nt ? (p.T - t0) : p.nt);
+  {
     if constexpr (CS == kCsFromPositions) {
       const int n = ntok * half;
       for (int idx = lane; idx < n; idx += kWaveSize) {
         const int tl = idx / half;
         const int j = idx - tl * half;
         const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t0 + tl];
-        angle_cos_sin(pp, tab.inv[j], lc[idx], ls[idx]);
+        float c, s;
+        angle_cos_sin(pp, tab.inv[j], c, s);
+        lc[idx] = (cs_t)c;
+        ls[idx] = (cs_t)s;
       }
       // LDS traffic of one wavefront is processed in order; this only keeps
       // the compiler from moving the reads above the writes.
@@ -258,11 +469,29 @@ qk_kernel(const QKParams p, const ColTable tab) {
     for (int s = 0; s < 2; ++s) {
       const int H = p.heads[s];
       if (H == 0) continue;
-      const int nrows = ntok * H;
-      const char* xb = static_cast<const char*>(p.x[s]);
-      char* yb = static_cast<char*>(p.y[s]);
       const int64_t xts = p.x_ts[s];
       const int64_t yts = p.y_ts[s];
+      SlotState<CB> st;
+      // Tile-local buffers: byte offsets below stay within 32 bits.
+      st.rx = buffer_of(static_cast<const char*>(p.x[s]) + t0 * xts * ES,
+                        (uint32_t)(((int64_t)(ntok - 1) * xts + (int64_t)H * p.D) * ES));
+      st.ry = buffer_of(static_cast<const char*>(p.y[s]) + t0 * yts * ES,
+                        (uint32_t)(((int64_t)(ntok - 1) * yts + (int64_t)H * p.D) * ES));
+      st.H = H;
+      st.nrows = ntok * H;
+      st.dq = p.dq[s];
+      st.dr = p.dr[s];
+      // grp / H for grp < 64 through a binary32 reciprocal, corrected once.
+      st.tl = (int)((float)grp * p.inv_heads[s]);
+      if (st.tl * H > grp) --st.tl;
+      if ((st.tl + 1) * H <= grp) ++st.tl;
+      st.h = grp - st.tl * H;
+      st.xo = (uint32_t)(((int64_t)st.tl * xts + (int64_t)st.h * p.D) * ES);
+      st.yo = (uint32_t)(((int64_t)st.tl * yts + (int64_t)st.h * p.D) * ES);
+      st.xinc = (uint32_t)(((int64_t)st.dq * xts + (int64_t)st.dr * p.D) * ES);
+      st.yinc = (uint32_t)(((int64_t)st.dq * yts + (int64_t)st.dr * p.D) * ES);
+      st.xwrap = (uint32_t)((xts - (int64_t)H * p.D) * ES);
+      st.ywrap = (uint32_t)((yts - (int64_t)H * p.D) * ES);
 
       float wa[V], wb[V];
       if constexpr (NORM) {
@@ -273,117 +502,17 @@ qk_kernel(const QKParams p, const ColTable tab) {
         unpack<BF16, V>(r, wb);
       }
 
-      // (token, head) of this lane's row, advanced by rpw rows per step.
-      int tl = grp / H;
-      int h = grp - tl * H;
-      const int dq = p.rpw / H;
-      const int dr = p.rpw - dq * H;
-
-      for (int r0 = 0; r0 < nrows; r0 += U * p.rpw) {
-        Words<CB> ra[U], rb[U];
-        int tlu[U];
-        bool ok[U];
-        int64_t yoff[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int r = r0 + u * p.rpw + grp;
-          ok[u] = lane_on && r < nrows;
-          tlu[u] = tl;
-          const int64_t xoff = (t0 + tl) * xts + (int64_t)h * p.D;
-          yoff[u] = (t0 + tl) * yts + (int64_t)h * p.D;
-          if (ok[u]) {
-            load_words<CB>(xb + (xoff + col_a) * ES, ra[u]);
-            load_words<CB>(xb + (xoff + col_b) * ES, rb[u]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < Words<CB>::N; ++i) ra[u].w[i] = rb[u].w[i] = 0u;
-          }
-          h += dr;
-          tl += dq;
-          if (h >= H) {
-            h -= H;
-            ++tl;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float a[V], b[V];
-          unpack<BF16, V>(ra[u], a);
-          unpack<BF16, V>(rb[u], b);
-
-          if constexpr (NORM) {
-            double ss = 0.0;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-              ss = __builtin_fma((double)a[i], (double)a[i], ss);
-              ss = __builtin_fma((double)b[i], (double)b[i], ss);
-            }
-            ss = group_sum(ss, lpr);
-            const float rs = rsqrt_to_f32(ss * p.inv_d + (double)p.eps);
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-              a[i] = a[i] * rs;
-              b[i] = b[i] * rs;
-            }
-            if constexpr (BF16) round_bf16_chunks<V>(a, b);
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-              a[i] = a[i] * wa[i];
-              b[i] = b[i] * wb[i];
-            }
-            if constexpr (BF16) round_bf16_chunks<V>(a, b);
-          }
-
-          if constexpr (CS != kCsNone) {
-            if (rot) {
-              // Rows past the tile's end are computed but not stored; read
-              // their cos/sin from the tile's first token so every read stays
-              // inside this wavefront's LDS slice and the caller's tables.
-              const int tlr = ok[u] ? tlu[u] : 0;
-              float ca[V], sa[V], cb[V], sb[V];
-              if constexpr (CS == kCsFromPositions) {
-                const int o = tlr * half + col_a;
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                  ca[i] = lc[o + i];
-                  sa[i] = ls[o + i];
-                  cb[i] = ca[i];
-                  sb[i] = sa[i];
-                }
-              } else {
-                const int64_t o = (t0 + tlr) * p.cs_ts;
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                  ca[i] = p.cos[o + col_a + i];
-                  sa[i] = p.sin[o + col_a + i];
-                  cb[i] = p.cos[o + col_b + i];
-                  sb[i] = p.sin[o + col_b + i];
-                }
-              }
-#pragma unroll
-              for (int i = 0; i < V; ++i) {
-                const double ya = a[i];
-                const double yb = b[i];
-                const double oa = __builtin_fma(ya, (double)ca[i], -(yb * (double)sa[i]));
-                const double ob = __builtin_fma(yb, (double)cb[i], ya * (double)sb[i]);
-                a[i] = (float)oa;
-                b[i] = (float)ob;
-              }
-            }
-          }
-
-          if (ok[u]) {
-            Words<CB> wa_out, wb_out;
-            pack<BF16, V>(a, wa_out);
-            pack<BF16, V>(b, wb_out);
-            store_words<CB>(yb + (yoff[u] + col_a) * ES, wa_out);
-            store_words<CB>(yb + (yoff[u] + col_b) * ES, wb_out);
-          }
-        }
-      }
+      // Full batches of U row-steps, then single steps for the remainder.
+      const int steps = (st.nrows + rpw - 1) / rpw;
+      const int full = steps / U;
+      int r0 = 0;
+      for (int g = 0; g < full; ++g, r0 += U * rpw)
+        process_steps<BF16, V, CS, NORM, LPR, U>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
+                                                 col_a, wa, wb, lc, ls, t0);
+      for (; r0 < st.nrows; r0 += rpw)
+        process_steps<BF16, V, CS, NORM, LPR, 1>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
+                                                 col_a, wa, wb, lc, ls, t0);
     }
-    // The next tile rewrites this wavefront's LDS slice; keep the order.
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -404,43 +533,73 @@ __global__ void __launch_bounds__(256) cos_sin_kernel(const CosSinParams p, cons
   sr[j + p.half] = s;
 }
 
-template <bool BF16, int V, int CS, bool NORM>
-int launch_t(const QKParams& p, const ColTable& tab, int grid, int lds, hipStream_t st) {
-  hipLaunchKernelGGL((qk_kernel<BF16, V, CS, NORM>), dim3(grid), dim3(kBlockThreads), lds, st,
-                     p, tab);
+template <bool BF16, int V, int CS, bool NORM, int LPR>
+int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
+  const bool cs_lds = CS == kCsFromPositions;
+  p.nt = nt_cap < MROPE_WAVE_TOKENS ? nt_cap : MROPE_WAVE_TOKENS;
+  if (p.nt < 1) p.nt = 1;
+  for (int s = 0; s < 2; ++s) {
+    const int H = p.heads[s] > 0 ? p.heads[s] : 1;
+    p.dq[s] = p.rpw / H;
+    p.dr[s] = p.rpw - p.dq[s] * H;
+    p.inv_heads[s] = 1.0f / (float)H;
+  }
+  const int64_t waves = (p.T + p.nt - 1) / p.nt;
+  const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(double) : 0;
+  hipLaunchKernelGGL((qk_kernel<BF16, V, CS, NORM, LPR>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads), lds, st, p, tab);
   return (int)hipGetLastError();
 }
 
-template <bool BF16, int V>
-int launch_mode(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, int grid,
-                int lds, hipStream_t st) {
+template <bool BF16, int V, int LPR>
+int launch_mode(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, int nt_cap,
+                hipStream_t st) {
   if (cs_mode == kCsFromPositions)
-    return norm ? launch_t<BF16, V, kCsFromPositions, true>(p, tab, grid, lds, st)
-                : launch_t<BF16, V, kCsFromPositions, false>(p, tab, grid, lds, st);
+    return norm ? launch_t<BF16, V, kCsFromPositions, true, LPR>(p, tab, nt_cap, st)
+                : launch_t<BF16, V, kCsFromPositions, false, LPR>(p, tab, nt_cap, st);
   if (cs_mode == kCsFromTable && !norm)
-    return launch_t<BF16, V, kCsFromTable, false>(p, tab, grid, lds, st);
+    return launch_t<BF16, V, kCsFromTable, false, LPR>(p, tab, nt_cap, st);
   if (cs_mode == kCsNone && norm)
-    return launch_t<BF16, V, kCsNone, true>(p, tab, grid, lds, st);
+    return launch_t<BF16, V, kCsNone, true, LPR>(p, tab, nt_cap, st);
   return (int)hipErrorInvalidValue;
+}
+
+// 16-byte chunks with a power-of-two lane count per row get a kernel with the
+// lane count fixed at compile time; everything else takes the runtime form.
+template <bool BF16, int V>
+int launch_lpr(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, int nt_cap,
+               hipStream_t st) {
+  if constexpr (V * (BF16 ? 2 : 4) == 16) {
+    switch (p.lpr) {
+      case 2: return launch_mode<BF16, V, 2>(cs_mode, norm, p, tab, nt_cap, st);
+      case 4: return launch_mode<BF16, V, 4>(cs_mode, norm, p, tab, nt_cap, st);
+      case 8: return launch_mode<BF16, V, 8>(cs_mode, norm, p, tab, nt_cap, st);
+      case 16: return launch_mode<BF16, V, 16>(cs_mode, norm, p, tab, nt_cap, st);
+      case 32: return launch_mode<BF16, V, 32>(cs_mode, norm, p, tab, nt_cap, st);
+      default: break;
+    }
+  }
+  return launch_mode<BF16, V, 0>(cs_mode, norm, p, tab, nt_cap, st);
 }
 
 }  // namespace
 
 int launch_qk(int dtype, int vec, int cs_mode, bool norm, const QKParams& p,
-              const ColTable& tab, int grid, int lds_bytes, void* stream) {
+              const ColTable& tab, int nt_cap, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == MROPE_DTYPE_BF16) {
     switch (vec) {
-      case 8: return launch_mode<true, 8>(cs_mode, norm, p, tab, grid, lds_bytes, st);
-      case 4: return launch_mode<true, 4>(cs_mode, norm, p, tab, grid, lds_bytes, st);
-      case 2: return launch_mode<true, 2>(cs_mode, norm, p, tab, grid, lds_bytes, st);
-      case 1: return launch_mode<true, 1>(cs_mode, norm, p, tab, grid, lds_bytes, st);
+      case 8: return launch_lpr<true, 8>(cs_mode, norm, p, tab, nt_cap, st);
+      case 4: return launch_lpr<true, 4>(cs_mode, norm, p, tab, nt_cap, st);
+      case 2: return launch_lpr<true, 2>(cs_mode, norm, p, tab, nt_cap, st);
+      case 1: return launch_lpr<true, 1>(cs_mode, norm, p, tab, nt_cap, st);
     }
   } else {
     switch (vec) {
-      case 4: return launch_mode<false, 4>(cs_mode, norm, p, tab, grid, lds_bytes, st);
-      case 2: return launch_mode<false, 2>(cs_mode, norm, p, tab, grid, lds_bytes, st);
-      case 1: return launch_mode<false, 1>(cs_mode, norm, p, tab, grid, lds_bytes, st);
+      case 4: return launch_lpr<false, 4>(cs_mode, norm, p, tab, nt_cap, st);
+      case 2: return launch_lpr<false, 2>(cs_mode, norm, p, tab, nt_cap, st);
+      case 1: return launch_lpr<false, 1>(cs_mode, norm, p, tab, nt_cap, st);
     }
   }
   return (int)hipErrorInvalidValue;
