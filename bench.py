@@ -10,6 +10,11 @@ Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
 kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
 bounded sample of the same workload (cpu_baseline).
 
+Warmup is at least W steps and at least --min-warmup-s seconds: the first
+tens of milliseconds of sustained HBM traffic run at a different clock state,
+and the timed K steps are meant to see the steady state.  Each step is one
+kernel launch on torch's current stream, timed with HIP events on that stream.
+
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --copy-calib BYTES   # plain device copy, for counter scaling
 """
@@ -91,8 +96,9 @@ def copy_calib(nbytes: int, steps: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--min-warmup-s", type=float, default=0.5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0)
@@ -129,9 +135,13 @@ def main():
         M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
                            wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_warm < args.min_warmup_s:
+        for _ in range(50):
+            step()
+        done += 50
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -154,7 +164,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": done,
         "ms_per_step": ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True,
@@ -169,8 +179,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "kernel": "qk_kernel<bf16,8,positions,norm>" if wl.dtype == "bf16"
-                     else "qk_kernel<f32,4,positions>"},
+                     "kernel": "qk_kernel (rmsnorm_mrope_qk)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, wl)
