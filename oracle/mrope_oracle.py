@@ -358,3 +358,49 @@ def rmsnorm_mrope_qk(q, k, pos, *, rotary_dim: int, theta: float, section, layou
     qo = encode(apply_rotary_values(qv, cos, sin, rotary_dim), dtype)
     ko = encode(apply_rotary_values(kv, cos, sin, rotary_dim), dtype)
     return qo, ko
+
+
+# ---------------------------------------------------------------------------
+# Decode: positions from the cache length, rotated K appended to a KV cache
+# ---------------------------------------------------------------------------
+
+def decode_positions(cache_len, new_tokens: int, rope_delta=None) -> np.ndarray:
+    """Positions of the new tokens of a decode step, flattened [B * new_tokens].
+
+    RoPE post, "Qwen3.5: MRoPE call chain" (``compute_3d_position_ids``): once
+    ``rope_deltas`` are stored and the cache is non-empty, the positions are
+    recovered from the sequence index counted from the cache length, expanded
+    to all three axes, plus each sample's ``rope_deltas`` (the next rotary
+    position minus the valid sequence length, from ``get_rope_index``).
+    Token i of sample b gets ``cache_len[b] + i + rope_delta[b]``.
+    """
+    cache_len = np.asarray(cache_len, dtype=np.int64)
+    B = cache_len.shape[0]
+    delta = np.zeros(B, dtype=np.int64) if rope_delta is None else np.asarray(rope_delta, np.int64)
+    i = np.arange(new_tokens, dtype=np.int64)
+    return (cache_len[:, None] + i[None, :] + delta[:, None]).reshape(-1)
+
+
+def mrope_decode_qk(q, k, cache_len, new_tokens: int, rope_delta, k_cache, *, rotary_dim: int,
+                    theta: float, wq=None, wk=None, eps: float = 0.0, dtype: str = "bf16"):
+    """One decode step: RMSNorm + rotary on q and k of B * new_tokens tokens
+    whose positions follow ``decode_positions`` (text positions: the same on
+    every axis, so the rotation is 1-D RoPE whatever the section), then the
+    rotated k of token (b, i) is written to ``k_cache[b, cache_len[b] + i]``.
+
+    ``k_cache`` is [B, capacity, hk, D] in the stored representation; rows at
+    or past the capacity are not written.  Returns (q_out, new k_cache).
+    """
+    pos = decode_positions(cache_len, new_tokens, rope_delta)
+    half = rotary_dim // 2
+    qo, ko = rmsnorm_mrope_qk(q, k, pos.reshape(1, -1), rotary_dim=rotary_dim, theta=theta,
+                              section=(half,), layout=LAYOUT_CHUNKED, wq=wq, wk=wk, eps=eps,
+                              dtype=dtype)
+    cache = np.array(k_cache, copy=True)
+    cap = cache.shape[1]
+    for b in range(len(cache_len)):
+        for i in range(new_tokens):
+            slot = int(cache_len[b]) + i
+            if slot < cap:
+                cache[b, slot] = ko[b * new_tokens + i]
+    return qo, cache

@@ -563,3 +563,47 @@ def test_planted_mistake_is_caught(monkeypatch, name, mutant, check):
     monkeypatch.setattr(O, name, mutant)
     with pytest.raises(AssertionError):
         check()
+
+
+# ---------------------------------------------------------------------------
+# Decode positions
+# ---------------------------------------------------------------------------
+
+def test_decode_position_continues_the_prefill():
+    """rope_deltas is the next rotary position minus the valid length (RoPE
+    post, get_rope_index), so the first decode token after a prefill sits at
+    the prefill's largest position + 1 on every axis; text-only prompts have
+    delta 0 and decode continues at the cache length."""
+    g = _golden("position_table.json")
+    segs = [(k, tuple(v) if isinstance(v, list) else v) for k, v in g["segments"]]
+    pos, delta = W.rope_index(segs, merge=g["merge"])
+    L = pos.shape[1]
+    p = O.decode_positions([L], 3, [delta])
+    assert p.tolist() == [int(pos.max()) + 1 + i for i in range(3)]     # 7, 8, 9
+    text, d0 = W.rope_index([("text", 5)])
+    assert d0 == 0
+    assert O.decode_positions([5, 9], 2).tolist() == [5, 6, 9, 10]
+
+
+def test_decode_equals_prefill_on_the_same_positions():
+    """A decode step is the fused path on text positions plus a cache write."""
+    rng = np.random.default_rng(40)
+    B, n, hq, hk, D, cap = 3, 2, 4, 2, 32, 12
+    q, k = W.random_qk(rng, B * n, hq, hk, D, "bf16")
+    wq, wk = W.random_weight(rng, D, "bf16"), W.random_weight(rng, D, "bf16")
+    cache_len = np.array([0, 5, 11])
+    delta = np.array([0, -3, 2])
+    cache = W.random_qk(rng, B * cap, hk, 1, D, "bf16")[0].reshape(B, cap, hk, D)
+    qo, newc = O.mrope_decode_qk(q, k, cache_len, n, delta, cache, rotary_dim=D, theta=1e6,
+                                 wq=wq, wk=wk, eps=1e-6, dtype="bf16")
+    pos = O.decode_positions(cache_len, n, delta)
+    for layout, sec in [("interleaved", (6, 5, 5)), ("chunked", (6, 5, 5))]:
+        fq, fk = O.rmsnorm_mrope_qk(q, k, np.stack([pos, pos, pos]), rotary_dim=D, theta=1e6,
+                                    section=sec, layout=layout, wq=wq, wk=wk, eps=1e-6,
+                                    dtype="bf16")
+        assert np.array_equal(fq, qo)
+    assert np.array_equal(newc[0, 0:2], fk[0:2]) and np.array_equal(newc[1, 5:7], fk[2:4])
+    assert np.array_equal(newc[2, 11], fk[4])            # slot 12 is past the capacity
+    untouched = np.ones((B, cap), bool)
+    untouched[0, 0:2] = untouched[1, 5:7] = untouched[2, 11] = False
+    assert np.array_equal(newc[untouched], cache[untouched])
