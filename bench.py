@@ -117,8 +117,9 @@ def main():
     import workloads as W
     import vlm_multimodal_rotary_amd as M
 
-    wl = W.WORKLOADS[args.workload]
-    inp = W.make_inputs(wl)
+    decode = args.workload in W.DECODE_WORKLOADS
+    wl = W.DECODE_WORKLOADS[args.workload] if decode else W.WORKLOADS[args.workload]
+    inp = W.make_decode_inputs(wl) if decode else W.make_inputs(wl)
 
     def dev(a):
         if a is None:
@@ -127,13 +128,23 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    q, k, pos = dev(inp["q"]), dev(inp["k"]), dev(inp["pos"])
+    q, k = dev(inp["q"]), dev(inp["k"])
     wq, wk = dev(inp["wq"]), dev(inp["wk"])
-    q_out, k_out = torch.empty_like(q), torch.empty_like(k)
+    q_out = torch.empty_like(q)
+    if decode:
+        cache_len, rope_delta, k_cache = (dev(inp["cache_len"]), dev(inp["rope_delta"]),
+                                          dev(inp["k_cache"]))
 
-    def step():
-        M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
-                           wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out)
+        def step():
+            M.mrope_decode_qk(q, k, cache_len, rope_delta, wl.new_tokens, wl.rotary_dim,
+                              wl.theta, k_cache, wq=wq, wk=wk, eps=wl.eps, q_out=q_out)
+    else:
+        pos = dev(inp["pos"])
+        k_out = torch.empty_like(k)
+
+        def step():
+            M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
+                               wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out)
 
     t_warm = time.perf_counter()
     done = 0
@@ -158,8 +169,17 @@ def main():
     alg_bytes = wl.algorithmic_bytes()
     achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
+    if decode:
+        config = {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.new_tokens,
+                  "hq": wl.hq, "hk": wl.hk, "D": wl.D, "rotary_dim": wl.rotary_dim,
+                  "theta": wl.theta, "cache_rows": wl.capacity, "rmsnorm": wl.norm}
+    else:
+        config = {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
+                  "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
+                  "section": list(wl.section), "rmsnorm": wl.norm}
     line = {
-        "metric": "Q+K tokens/s, fused RMSNorm+MRoPE (rmsnorm_mrope_qk)",
+        "metric": ("decode tokens/s, mrope_decode_qk" if decode else
+                   "Q+K tokens/s, fused RMSNorm+MRoPE (rmsnorm_mrope_qk)"),
         "value": wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -172,16 +192,15 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded normal q/k, N(1,0.1) weights, workload position tables)",
-        "config": {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
-                   "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
-                   "section": list(wl.section), "rmsnorm": wl.norm},
+        "config": config,
         "hbm_gbps": achieved_gbps,
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "kernel": "qk_kernel (rmsnorm_mrope_qk)"},
+                     "kernel": "qk_kernel (mrope_decode_qk)" if decode
+                     else "qk_kernel (rmsnorm_mrope_qk)"},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not decode:
         line["cpu_baseline"] = cpu_baseline(inp, wl)
     print(json.dumps(line), flush=True)
 

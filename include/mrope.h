@@ -181,6 +181,38 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq,
                      void* stream);
 
 /*
+ * mrope_decode_qk — one decode step of the fused path ([RoPE] Qwen3.5 call
+ * chain, compute_3d_position_ids: with rope_deltas stored and a non-empty
+ * cache, positions are recovered from the sequence index counted from the
+ * cache length, the same on all three axes, plus each sample's rope_deltas).
+ * Token i of sequence b is row b*new_tokens + i of q and k; its position is
+ * p = cache_len[b] + i + rope_delta[b] (rope_delta NULL = 0) on every axis,
+ * so the rotation is 1-D RoPE with inv_freq = mrope_inv_freq(rotary_dim,
+ * theta) whatever the model's section.  Optional per-head RMSNorm as in
+ * rmsnorm_mrope_qk.  Rotated q goes to q_out; rotated k of token (b, i) is
+ * written into the KV cache row
+ *     k_cache + b*k_cache_seq_stride + (cache_len[b] + i)*k_cache_tok_stride
+ * (hk*D contiguous elements); a row at or past k_cache_capacity (or below 0)
+ * is not written.
+ *   q: device [batch*new_tokens][hq][D]; k likewise with hk heads.
+ *   cache_len, rope_delta: device int32 [batch] (rope_delta may be NULL).
+ *   k_cache: device, batch sequences of k_cache_capacity rows; strides in
+ *            elements (k_cache_tok_stride >= hk*D, k_cache_seq_stride >=
+ *            k_cache_capacity*k_cache_tok_stride when batch > 1).
+ * Positions must stay below 2^24 in magnitude.  EINVAL on bad shapes, null
+ * pointers, or a cache that overlaps q, k, q_out, the weights or cache_len /
+ * rope_delta.
+ */
+int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq,
+                    const void* k, int64_t k_tok_stride, int hk,
+                    int batch, int new_tokens, int D, int rotary_dim,
+                    const int32_t* cache_len, const int32_t* rope_delta, double theta,
+                    const void* wq, const void* wk, float eps, int dtype,
+                    void* q_out, int64_t q_out_tok_stride,
+                    void* k_cache, int64_t k_cache_seq_stride, int64_t k_cache_tok_stride,
+                    int k_cache_capacity, void* stream);
+
+/*
  * mrope_last_error — message for the last non-zero return on this thread
  * (empty string if none).  The pointer stays valid until the next call on
  * the same thread.

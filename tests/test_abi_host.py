@@ -209,3 +209,32 @@ def test_binding_builds_no_cpu_path():
     import inspect
     src = inspect.getsource(M)
     assert "oracle" not in src and "numpy.cos" not in src and "np.cos" not in src
+
+
+@fake_ptr_test
+def test_decode_rejects_bad_arguments():
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(q=FAKE, q_ts=32 * 128, hq=32, k=FAKE + 0x4000000, k_ts=4 * 128, hk=4, batch=8,
+                 n=1, D=128, rd=128, cl=FAKE + 0x8000000, rdel=FAKE + 0x8001000, theta=1e6,
+                 wq=FAKE + 0xC000000, wk=FAKE + 0xC001000, eps=1e-6, dtype=_lib.DTYPE_BF16,
+                 qo=FAKE + 0x20000000, qo_ts=32 * 128, kc=FAKE + 0x30000000,
+                 kc_seq=64 * 4 * 128, kc_tok=4 * 128, cap=64)
+        a.update(kw)
+        return lib.mrope_decode_qk(a["q"], a["q_ts"], a["hq"], a["k"], a["k_ts"], a["hk"],
+                                   a["batch"], a["n"], a["D"], a["rd"], a["cl"], a["rdel"],
+                                   a["theta"], a["wq"], a["wk"], a["eps"], a["dtype"], a["qo"],
+                                   a["qo_ts"], a["kc"], a["kc_seq"], a["kc_tok"], a["cap"], None)
+
+    assert call(batch=0) == _lib.MROPE_OK                      # nothing to do
+    assert call(batch=-1) == _lib.MROPE_EINVAL
+    assert call(cl=0) == _lib.MROPE_EINVAL                     # no cache lengths
+    assert call(cap=0) == _lib.MROPE_EINVAL
+    assert call(kc_tok=100) == _lib.MROPE_EINVAL               # row stride < hk*D
+    assert call(kc_seq=10 * 4 * 128) == _lib.MROPE_EINVAL      # sequences overlap
+    assert call(kc=FAKE + 64) == _lib.MROPE_EINVAL             # cache overlaps q
+    assert call(kc=FAKE + 0x8000000 - 4 * 128) == _lib.MROPE_EINVAL   # cache overlaps cache_len
+    assert call(wk=0) == _lib.MROPE_EINVAL
+    assert call(rd=129) == _lib.MROPE_EINVAL
+    assert call(theta=-1.0) == _lib.MROPE_EINVAL

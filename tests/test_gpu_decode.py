@@ -1,0 +1,94 @@
+"""GPU parity of the decode step (mrope_decode_qk) against the CPU oracle."""
+import numpy as np
+import pytest
+
+from oracle import mrope_oracle as O
+import workloads as W
+from tests._helpers import assert_bf16_close, assert_close, from_dev, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import vlm_multimodal_rotary_amd as lib
+    lib.load()
+    return lib
+
+
+def _run(M, inp, wl, use_delta=True, in_place=False):
+    import torch
+    dt = wl.dtype
+    q, k = to_dev(inp["q"], dt), to_dev(inp["k"], dt)
+    cache = to_dev(inp["k_cache"], dt)
+    cl = to_dev(inp["cache_len"], "i32")
+    rd = to_dev(inp["rope_delta"], "i32") if use_delta else None
+    wq = to_dev(inp["wq"], dt) if wl.norm else None
+    wk = to_dev(inp["wk"], dt) if wl.norm else None
+    qo = M.mrope_decode_qk(q, k, cl, rd, inp["new_tokens"], wl.rotary_dim, wl.theta, cache,
+                           wq=wq, wk=wk, eps=wl.eps, q_out=q if in_place else None)
+    torch.cuda.synchronize()
+    return from_dev(qo), from_dev(cache)
+
+
+def _oracle(inp, wl, use_delta=True):
+    return O.mrope_decode_qk(inp["q"], inp["k"], inp["cache_len"], inp["new_tokens"],
+                             inp["rope_delta"] if use_delta else None, inp["k_cache"],
+                             rotary_dim=wl.rotary_dim, theta=wl.theta,
+                             wq=inp["wq"] if wl.norm else None,
+                             wk=inp["wk"] if wl.norm else None, eps=wl.eps, dtype=wl.dtype)
+
+
+@pytest.mark.parametrize("batch,new_tokens,capacity,use_delta", [
+    (7, 1, 64, True), (5, 3, 40, True), (9, 2, 300, False), (1, 1, 1, True)])
+def test_decode_matches_oracle(M, batch, new_tokens, capacity, use_delta):
+    wl = W.DECODE_WORKLOADS["omni_decode"]
+    inp = W.make_decode_inputs(wl, batch=batch, new_tokens=new_tokens, capacity=capacity)
+    note(f"decode B={batch} n={new_tokens} cap={capacity} delta={use_delta}")
+    gq, gc = _run(M, inp, wl, use_delta)
+    oq, oc = _oracle(inp, wl, use_delta)
+    assert_bf16_close(gq, oq, 1, "decode q")
+    assert_bf16_close(gc, oc, 1, "decode k cache")
+    # rows other than the appended ones are untouched, bit for bit
+    touched = np.zeros((batch, capacity), bool)
+    for b in range(batch):
+        for i in range(new_tokens):
+            if inp["cache_len"][b] + i < capacity:
+                touched[b, inp["cache_len"][b] + i] = True
+    assert np.array_equal(gc[~touched], inp["k_cache"][~touched])
+
+
+def test_decode_rows_past_capacity_are_not_written(M):
+    wl = W.DECODE_WORKLOADS["omni_decode"]
+    inp = W.make_decode_inputs(wl, batch=4, new_tokens=4, capacity=10)
+    inp["cache_len"] = np.array([0, 7, 9, 12], dtype=np.int32)   # 7..10, 9..12, 12..15 overflow
+    note("decode capacity overflow")
+    gq, gc = _run(M, inp, wl)
+    oq, oc = _oracle(inp, wl)
+    assert_bf16_close(gq, oq, 1, "decode q")
+    assert_bf16_close(gc, oc, 1, "decode cache")
+    assert np.array_equal(gc[3], inp["k_cache"][3])
+
+
+def test_decode_in_place_q_and_full_size(M):
+    wl = W.DECODE_WORKLOADS["omni_decode"]
+    inp = W.make_decode_inputs(wl, batch=64, capacity=256)
+    note("decode in place")
+    gq, gc = _run(M, inp, wl, in_place=True)
+    oq, oc = _oracle(inp, wl)
+    assert_bf16_close(gq, oq, 1, "decode q in place")
+    assert_bf16_close(gc, oc, 1, "decode cache")
+    # the benchmark's configuration, checked on a sample of sequences
+    inp = W.make_decode_inputs(wl)
+    note(f"decode full B={inp['batch']} cap={inp['capacity']}")
+    gq, gc = _run(M, inp, wl)
+    rows = np.random.default_rng(7).choice(inp["batch"], 24, replace=False)
+    sub = dict(inp)
+    sub["q"], sub["k"] = inp["q"][rows], inp["k"][rows]
+    sub["cache_len"], sub["rope_delta"] = inp["cache_len"][rows], inp["rope_delta"][rows]
+    sub["k_cache"] = inp["k_cache"][rows]
+    oq, oc = _oracle(sub, wl)
+    assert_bf16_close(gq[rows], oq, 1, "decode q sampled")
+    assert_bf16_close(gc[rows], oc, 1, "decode cache sampled")

@@ -17,7 +17,7 @@ from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, MropeError, check, float_arra
                    int_array, load)
 
 __all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "rms_norm",
-           "apply_rotary_qk", "rmsnorm_mrope_qk", "MropeError", "load"]
+           "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "MropeError", "load"]
 
 
 def _torch():
@@ -152,3 +152,30 @@ def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
         _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out), _heads_view(k_out, "k_out"),
         _stream(q)))
     return q_out, k_out
+
+
+def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: int, theta: float,
+                    k_cache, wq=None, wk=None, eps: float = 1e-6, q_out=None):
+    """One decode step: q, k [batch*new_tokens, heads, D]; cache_len and
+    rope_delta (or None) int32 [batch] on the device; k_cache [batch,
+    capacity, hk, D] receives the rotated k at rows cache_len[b] + i.
+    Returns q_out (k_cache is updated in place)."""
+    torch = _torch()
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    T, hq, D = q.shape
+    hk = k.shape[1]
+    batch = cache_len.shape[0]
+    if cache_len.dtype != torch.int32 or (rope_delta is not None and rope_delta.dtype != torch.int32):
+        raise MropeError(_lib.MROPE_EINVAL, "cache_len and rope_delta must be int32")
+    if batch * new_tokens != T:
+        raise MropeError(_lib.MROPE_EINVAL, "q rows must equal batch * new_tokens")
+    if k_cache.dim() != 4 or k_cache.shape[2] != hk or k_cache.shape[3] != D:
+        raise MropeError(_lib.MROPE_EINVAL, "k_cache must be [batch, capacity, hk, D]")
+    if k_cache.stride(3) != 1 or (hk > 1 and k_cache.stride(2) != D):
+        raise MropeError(_lib.MROPE_EINVAL, "k_cache rows must be contiguous")
+    check(load().mrope_decode_qk(
+        _ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"), hk, batch,
+        int(new_tokens), D, int(rotary_dim), _ptr(cache_len), _ptr(rope_delta), float(theta),
+        _ptr(wq), _ptr(wk), float(eps), _dtype_code(q), _ptr(q_out), _heads_view(q_out, "q_out"),
+        _ptr(k_cache), k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _stream(q)))
+    return q_out

@@ -48,6 +48,9 @@ SIGNATURES = {
     "rmsnorm_mrope_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_i64, _c_int,
                                   _c_int, _vp, _c_i64, _c_int, _ip, _c_int, _c_int, _c_double,
                                   _vp, _vp, _c_float, _c_int, _vp, _c_i64, _vp, _c_i64, _vp]),
+    "mrope_decode_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _vp, _vp, _c_double, _vp, _vp, _c_float, _c_int,
+                                 _vp, _c_i64, _vp, _c_i64, _c_i64, _c_int, _vp]),
     "mrope_last_error": (ctypes.c_char_p, []),
 }
 

@@ -233,13 +233,23 @@ int check_qk_tensors(const QKArgs& a, bool need_rd) {
 }
 
 // Launch geometry and the remaining per-launch fields.
+struct DecodeArgs {
+  const int32_t* cache_len = nullptr;
+  const int32_t* rope_delta = nullptr;
+  int new_tokens = 0;
+  int64_t kc_seq = 0, kc_tok = 0;
+  int kc_cap = 0;
+};
+
 int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
            const int32_t* pos, int64_t pos_stride, const float* cos, const float* sin,
-           int64_t cs_ts, float eps, void* stream, const Extent* extra, int n_extra) {
+           int64_t cs_ts, float eps, void* stream, const Extent* extra, int n_extra,
+           const DecodeArgs* dec = nullptr) {
   const int es = elem_bytes_of(a.dtype);
   const void* ptrs[6] = {a.x[0], a.x[1], a.y[0], a.y[1], a.w[0], a.w[1]};
-  int64_t strides[4] = {a.x_ts[0], a.x_ts[1], a.y_ts[0], a.y_ts[1]};
-  const int v = pick_vec(a.dtype, a.D, a.rd, ptrs, 6, strides, 4);
+  int64_t strides[6] = {a.x_ts[0], a.x_ts[1], a.y_ts[0], a.y_ts[1],
+                        dec ? dec->kc_seq : 0, dec ? dec->kc_tok : 0};
+  const int v = pick_vec(a.dtype, a.D, a.rd, ptrs, 6, strides, 6);
   if (v == 0)
     return fail(MROPE_EUNSUPPORTED,
                 "no vector width fits D = %d, rotary_dim = %d and the buffer alignment "
@@ -276,6 +286,14 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   p.cs_ts = cs_ts;
   p.eps = eps;
   p.inv_d = 1.0 / (double)a.D;
+  if (dec != nullptr) {
+    p.cache_len = dec->cache_len;
+    p.rope_delta = dec->rope_delta;
+    p.new_tokens = dec->new_tokens;
+    p.kc_seq = dec->kc_seq;
+    p.kc_tok = dec->kc_tok;
+    p.kc_cap = dec->kc_cap;
+  }
 
   // Tokens per tile: a wavefront's cos/sin slice (2 * nt * half doubles)
   // stays within 8 KB.
@@ -469,6 +487,88 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
   Extent extra[1] = {extent_of(pos, n_axes, pos_axis_stride, T, 4)};
   return run_qk(a, mrope::kCsFromPositions, norm, tab, pos, pos_axis_stride, nullptr, nullptr, 0,
                 eps, stream, extra, 1);
+}
+
+int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
+                    int64_t k_tok_stride, int hk, int batch, int new_tokens, int D,
+                    int rotary_dim, const int32_t* cache_len, const int32_t* rope_delta,
+                    double theta, const void* wq, const void* wk, float eps, int dtype,
+                    void* q_out, int64_t q_out_tok_stride, void* k_cache,
+                    int64_t k_cache_seq_stride, int64_t k_cache_tok_stride, int k_cache_capacity,
+                    void* stream) {
+  if (batch < 0 || new_tokens < 0)
+    return fail(MROPE_EINVAL, "batch = %d and new_tokens = %d must be >= 0", batch, new_tokens);
+  const int64_t T = (int64_t)batch * new_tokens;
+  QKArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x[0] = q;
+  a.x[1] = k;
+  a.x_ts[0] = q_tok_stride;
+  a.x_ts[1] = k_tok_stride;
+  a.heads[0] = hq;
+  a.heads[1] = hk;
+  a.y[0] = q_out;
+  a.y[1] = k_cache;
+  a.y_ts[0] = q_out_tok_stride;
+  a.y_ts[1] = (int64_t)hk * D;  // one row at a time; the cache layout is checked below
+  a.w[0] = wq;
+  a.w[1] = wk;
+  a.T = T;
+  a.D = D;
+  a.rd = rotary_dim;
+  a.dtype = dtype;
+  int rc = check_qk_tensors(a, true);
+  if (rc) return rc;
+  if ((wq == nullptr) != (wk == nullptr))
+    return fail(MROPE_EINVAL, "wq and wk must both be given or both be NULL");
+  const bool norm = wq != nullptr;
+  if (norm && (!std::isfinite(eps) || eps < 0.0f))
+    return fail(MROPE_EINVAL, "eps must be finite and >= 0");
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(MROPE_EINVAL, "theta must be positive and finite");
+  if (T > 0 && cache_len == nullptr) return fail(MROPE_EINVAL, "cache_len is NULL");
+  const int es = elem_bytes_of(dtype);
+  Extent cache_ext;
+  if (T > 0 && hk > 0) {
+    if (k_cache_capacity < 1) return fail(MROPE_EINVAL, "k_cache_capacity must be >= 1");
+    if (k_cache_tok_stride < (int64_t)hk * D)
+      return fail(MROPE_EINVAL, "k_cache_tok_stride %lld < hk*D", (long long)k_cache_tok_stride);
+    if (batch > 1 && k_cache_seq_stride < (int64_t)k_cache_capacity * k_cache_tok_stride)
+      return fail(MROPE_EINVAL, "k_cache_seq_stride is smaller than capacity * tok_stride");
+    cache_ext = extent_of(k_cache, 1,
+                          0, ((int64_t)(batch - 1) * k_cache_seq_stride +
+                              (int64_t)(k_cache_capacity - 1) * k_cache_tok_stride +
+                              (int64_t)hk * D), es);
+    const Extent qin = extent_of(q, T, q_tok_stride, (int64_t)hq * D, es);
+    const Extent kin = extent_of(k, T, k_tok_stride, (int64_t)hk * D, es);
+    const Extent qout = extent_of(q_out, T, q_out_tok_stride, (int64_t)hq * D, es);
+    if (overlaps(cache_ext, qin) || overlaps(cache_ext, kin) || overlaps(cache_ext, qout))
+      return fail(MROPE_EINVAL, "k_cache overlaps q, k or q_out");
+    if (norm && (overlaps(cache_ext, extent_of(wq, 1, D, D, es)) ||
+                 overlaps(cache_ext, extent_of(wk, 1, D, D, es))))
+      return fail(MROPE_EINVAL, "k_cache overlaps a weight vector");
+  }
+  mrope::ColTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  // Text positions: every column reads the same position, so one chunked
+  // section covering all columns is the 1-D RoPE table.
+  const int half = rotary_dim / 2;
+  rc = build_table(rotary_dim, theta, &half, 1, MROPE_LAYOUT_CHUNKED, nullptr, tab);
+  if (rc) return rc;
+  Extent extra[2] = {extent_of(cache_len, 1, 0, batch, 4),
+                     extent_of(rope_delta, 1, 0, batch, 4)};
+  DecodeArgs dec;
+  dec.cache_len = cache_len;
+  dec.rope_delta = rope_delta;
+  dec.new_tokens = new_tokens;
+  dec.kc_seq = k_cache_seq_stride;
+  dec.kc_tok = k_cache_tok_stride;
+  dec.kc_cap = k_cache_capacity;
+  if (hk > 0 && T > 0)
+    for (const Extent& e : extra)
+      if (overlaps(cache_ext, e)) return fail(MROPE_EINVAL, "k_cache overlaps cache_len/rope_delta");
+  return run_qk(a, mrope::kCsDecode, norm, tab, nullptr, 0, nullptr, nullptr, 0, eps, stream,
+                extra, 2, &dec);
 }
 
 const char* mrope_last_error(void) { return g_err.c_str(); }

@@ -26,6 +26,8 @@ enum CsMode : int {
   kCsFromPositions = 0,  // computed per tile from positions (fused path)
   kCsFromTable = 1,      // read from caller cos/sin tables [T][rotary_dim]
   kCsNone = 2,           // no rotation (RMSNorm only)
+  kCsDecode = 3,         // decode: text positions from cache length + rope_delta,
+                         // k written to a KV cache (one token per wavefront)
 };
 
 // One launch processes up to two tensors (slot 0 = q, slot 1 = k) that share
@@ -54,6 +56,13 @@ struct QKParams {
   int64_t cs_ts;
   float eps;
   double inv_d;          // 1.0 / D
+  // decode mode
+  const int32_t* cache_len;   // [batch]
+  const int32_t* rope_delta;  // [batch] or null
+  int new_tokens;             // tokens per sequence; token t = b * new_tokens + i
+  int64_t kc_seq;             // k-cache stride between sequences (elements)
+  int64_t kc_tok;             // k-cache stride between positions (elements)
+  int kc_cap;                 // k-cache positions per sequence
 };
 
 struct CosSinParams {

@@ -364,7 +364,7 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
         // token, so every read stays inside the LDS slice / caller tables.
         const int tlr = ok[u] ? tlu[u] : 0;
         double ca_[V], sa_[V], cb_[V], sb_[V];
-        if constexpr (CS == kCsFromPositions) {
+        if constexpr (CS == kCsFromPositions || CS == kCsDecode) {
           const int o = tlr * p.half + col_a;
 #pragma unroll
           for (int i = 0; i < V; ++i) {
@@ -447,6 +447,25 @@ qk_kernel(const QKParams p, const ColTable tab) {
   if (t0 >= p.T) return;
   const int ntok = (int)((p.T - t0) < p.nt ? (p.T - t0) : p.nt);
   {
+    // Decode: token t0 is token i of sequence b; its text position (the same
+    // on every axis) continues the sequence's cache.
+    [[maybe_unused]] int32_t dec_slot = 0;
+    [[maybe_unused]] int64_t dec_seq = 0;
+    if constexpr (CS == kCsDecode) {
+      dec_seq = t0 / p.new_tokens;
+      const int i = (int)(t0 - dec_seq * p.new_tokens);
+      dec_slot = p.cache_len[dec_seq] + i;
+      const int32_t pp = dec_slot + (p.rope_delta != nullptr ? p.rope_delta[dec_seq] : 0);
+      for (int j = lane; j < half; j += kWaveSize) {
+        float c, s;
+        angle_cos_sin(pp, tab.inv[j], c, s);
+        lc[j] = (cs_t)c;
+        ls[j] = (cs_t)s;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     if constexpr (CS == kCsFromPositions) {
       const int n = ntok * half;
       for (int idx = lane; idx < n; idx += kWaveSize) {
@@ -477,6 +496,16 @@ qk_kernel(const QKParams p, const ColTable tab) {
                         (uint32_t)(((int64_t)(ntok - 1) * xts + (int64_t)H * p.D) * ES));
       st.ry = buffer_of(static_cast<const char*>(p.y[s]) + t0 * yts * ES,
                         (uint32_t)(((int64_t)(ntok - 1) * yts + (int64_t)H * p.D) * ES));
+      if constexpr (CS == kCsDecode) {
+        if (s == 1) {
+          // Rotated k goes to its cache row; a row outside [0, capacity) gets
+          // an empty buffer, so its stores are dropped.
+          const bool in_cache = dec_slot >= 0 && dec_slot < p.kc_cap;
+          st.ry = buffer_of(static_cast<const char*>(p.y[1]) +
+                                (dec_seq * p.kc_seq + (int64_t)(in_cache ? dec_slot : 0) * p.kc_tok) * ES,
+                            in_cache ? (uint32_t)((int64_t)H * p.D * ES) : 0u);
+        }
+      }
       st.H = H;
       st.nrows = ntok * H;
       st.dq = p.dq[s];
@@ -535,9 +564,9 @@ __global__ void __launch_bounds__(256) cos_sin_kernel(const CosSinParams p, cons
 
 template <bool BF16, int V, int CS, bool NORM, int LPR>
 int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
-  const bool cs_lds = CS == kCsFromPositions;
+  const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
   p.nt = nt_cap < MROPE_WAVE_TOKENS ? nt_cap : MROPE_WAVE_TOKENS;
-  if (p.nt < 1) p.nt = 1;
+  if (p.nt < 1 || CS == kCsDecode) p.nt = 1;
   for (int s = 0; s < 2; ++s) {
     const int H = p.heads[s] > 0 ? p.heads[s] : 1;
     p.dq[s] = p.rpw / H;
@@ -558,6 +587,9 @@ int launch_mode(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, 
   if (cs_mode == kCsFromPositions)
     return norm ? launch_t<BF16, V, kCsFromPositions, true, LPR>(p, tab, nt_cap, st)
                 : launch_t<BF16, V, kCsFromPositions, false, LPR>(p, tab, nt_cap, st);
+  if (cs_mode == kCsDecode)
+    return norm ? launch_t<BF16, V, kCsDecode, true, LPR>(p, tab, nt_cap, st)
+                : launch_t<BF16, V, kCsDecode, false, LPR>(p, tab, nt_cap, st);
   if (cs_mode == kCsFromTable && !norm)
     return launch_t<BF16, V, kCsFromTable, false, LPR>(p, tab, nt_cap, st);
   if (cs_mode == kCsNone && norm)

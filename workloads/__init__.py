@@ -242,3 +242,79 @@ def random_qk(rng: np.random.Generator, T: int, hq: int, hk: int, D: int, dtype:
 
 def random_weight(rng: np.random.Generator, D: int, dtype: str):
     return _store((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32), dtype)
+
+
+# ---------------------------------------------------------------------------
+# Decode steps
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    index: int
+    dtype: str
+    batch: int            # sequences
+    new_tokens: int       # tokens appended per sequence
+    hq: int
+    hk: int
+    D: int
+    rotary_dim: int
+    theta: float
+    capacity: int         # KV-cache rows per sequence
+    norm: bool
+    eps: float = 1e-6
+    description: str = ""
+
+    @property
+    def T(self) -> int:
+        return self.batch * self.new_tokens
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self) -> int:
+        """Read q and k, write q_out and the k-cache rows, read cache_len and
+        rope_delta, read the two weight vectors."""
+        qk = self.T * (2 * self.hq + 2 * self.hk) * self.D * self.elem_bytes
+        meta = 2 * 4 * self.batch
+        w = 2 * self.D * self.elem_bytes if self.norm else 0
+        return qk + meta + w
+
+
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload("omni_decode", 6, "bf16", 512, 1, 32, 4, 128, 128, 1e6, 1024, True,
+                       description="Omni-like decode: 512 sequences x 1 new token, "
+                                   "k appended to a 1024-row cache"),
+    ]
+}
+
+
+def make_decode_inputs(wl: DecodeWorkload | str, batch: int | None = None,
+                       new_tokens: int | None = None, capacity: int | None = None,
+                       seed: int | None = None) -> dict:
+    """Seeded decode-step inputs: q, k [batch*new_tokens, heads, D], weights,
+    cache_len uniform in [0, capacity - new_tokens], rope_delta uniform in
+    [-300, 0] (a prompt with visual segments advances its positions by less
+    than its token count), and a random k_cache [batch, capacity, hk, D]."""
+    if isinstance(wl, str):
+        wl = DECODE_WORKLOADS[wl]
+    B = wl.batch if batch is None else batch
+    n = wl.new_tokens if new_tokens is None else new_tokens
+    cap = wl.capacity if capacity is None else capacity
+    rng = np.random.default_rng(wl.index if seed is None else seed)
+    q = rng.standard_normal((B * n, wl.hq, wl.D), dtype=np.float32)
+    k = rng.standard_normal((B * n, wl.hk, wl.D), dtype=np.float32)
+    wq = wk = None
+    if wl.norm:
+        wq = (1.0 + 0.1 * rng.standard_normal(wl.D)).astype(np.float32)
+        wk = (1.0 + 0.1 * rng.standard_normal(wl.D)).astype(np.float32)
+    cache_len = rng.integers(0, max(1, cap - n + 1), size=B).astype(np.int32)
+    rope_delta = rng.integers(-300, 1, size=B).astype(np.int32)
+    cache = rng.standard_normal((B, cap, wl.hk, wl.D), dtype=np.float32)
+    return dict(q=_store(q, wl.dtype), k=_store(k, wl.dtype),
+                wq=None if wq is None else _store(wq, wl.dtype),
+                wk=None if wk is None else _store(wk, wl.dtype),
+                cache_len=cache_len, rope_delta=rope_delta, k_cache=_store(cache, wl.dtype),
+                workload=wl, batch=B, new_tokens=n, capacity=cap)
