@@ -92,3 +92,54 @@ def test_decode_in_place_q_and_full_size(M):
     oq, oc = _oracle(sub, wl)
     assert_bf16_close(gq[rows], oq, 1, "decode q sampled")
     assert_bf16_close(gc[rows], oc, 1, "decode cache sampled")
+
+
+def test_decode_and_prefill_replay_in_a_hip_graph(M):
+    """Captured launches replay correctly: several replays with eager work and
+    synchronisations between them, each checked against the eager result."""
+    import torch
+    wl = W.DECODE_WORKLOADS["omni_decode"]
+    inp = W.make_decode_inputs(wl, batch=32, capacity=128)
+    dt = wl.dtype
+    q, k = to_dev(inp["q"], dt), to_dev(inp["k"], dt)
+    cl, rd = to_dev(inp["cache_len"], "i32"), to_dev(inp["rope_delta"], "i32")
+    wq, wk = to_dev(inp["wq"], dt), to_dev(inp["wk"], dt)
+    cache_eager = to_dev(inp["k_cache"], dt)
+    q_eager = M.mrope_decode_qk(q, k, cl, rd, 1, wl.rotary_dim, wl.theta, cache_eager,
+                                wq=wq, wk=wk, eps=wl.eps)
+    pw = W.WORKLOADS["omni_text_prefill"]
+    pinp = W.make_inputs(pw, T=100)
+    pq, pk, pos = to_dev(pinp["q"], "bf16"), to_dev(pinp["k"], "bf16"), to_dev(pinp["pos"], "i32")
+    pwq, pwk = to_dev(pinp["wq"], "bf16"), to_dev(pinp["wk"], "bf16")
+    pq_eager, pk_eager = M.rmsnorm_mrope_qk(pq, pk, pos, 128, pw.theta, pw.section, pw.layout,
+                                            wq=pwq, wk=pwk, eps=pw.eps)
+    torch.cuda.synchronize()
+
+    cache_g = to_dev(inp["k_cache"], dt)
+    q_g = torch.empty_like(q)
+    pq_g, pk_g = torch.empty_like(pq), torch.empty_like(pk)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.mrope_decode_qk(q, k, cl, rd, 1, wl.rotary_dim, wl.theta, cache_g, wq=wq, wk=wk,
+                          eps=wl.eps, q_out=q_g)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.mrope_decode_qk(q, k, cl, rd, 1, wl.rotary_dim, wl.theta, cache_g, wq=wq, wk=wk,
+                          eps=wl.eps, q_out=q_g)
+        M.rmsnorm_mrope_qk(pq, pk, pos, 128, pw.theta, pw.section, pw.layout, wq=pwq, wk=pwk,
+                           eps=pw.eps, q_out=pq_g, k_out=pk_g)
+    for rep in range(4):
+        q_g.zero_()
+        pq_g.zero_()
+        pk_g.zero_()
+        cache_g.copy_(to_dev(inp["k_cache"], dt))
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q_g.view(torch.int16), q_eager.view(torch.int16)), rep
+        assert torch.equal(cache_g.view(torch.int16), cache_eager.view(torch.int16)), rep
+        assert torch.equal(pq_g.view(torch.int16), pq_eager.view(torch.int16)), rep
+        assert torch.equal(pk_g.view(torch.int16), pk_eager.view(torch.int16)), rep

@@ -30,7 +30,10 @@ WAVE_TOKENS = 1   # tokens per wavefront at most (MROPE_WAVE_TOKENS)
 OUT_OF_RANGE = 0x80000000
 
 
-def plan(T, D, rd, es, fused=True, wave_tokens=WAVE_TOKENS):
+MIN_WAVES = 2048  # wavefronts a launch aims for before splitting tiles (MROPE_MIN_WAVES)
+
+
+def plan(T, D, rd, es, fused=True, wave_tokens=WAVE_TOKENS, heads=(1, 1), min_waves=MIN_WAVES):
     v = pick_vec(es, D, rd)
     assert v, (D, rd, es)
     half = rd // 2
@@ -39,25 +42,29 @@ def plan(T, D, rd, es, fused=True, wave_tokens=WAVE_TOKENS):
     lrot = half // v
     nt_cap = max(1, min(16, 512 // half)) if half else 16
     nt = max(1, min(nt_cap, wave_tokens))
-    waves = -(-T // nt)
-    return dict(v=v, half=half, lpr=lpr, rpw=rpw, lrot=lrot, nt=nt, nwaves=waves,
-                lds_doubles=2 * nt * half if fused else 0)
+    tiles = -(-T // nt)
+    tile_steps = -(-nt * heads[0] // rpw) + -(-nt * heads[1] // rpw)
+    parts = max(1, min(tile_steps, -(-min_waves // tiles)))
+    return dict(v=v, half=half, lpr=lpr, rpw=rpw, lrot=lrot, nt=nt, nwaves=tiles * parts,
+                parts=parts, lds_doubles=2 * nt * half if fused else 0)
 
 
-def first_row_split(grp, H):
-    """The kernel's grp / H through a binary32 reciprocal, corrected once."""
-    tl = int(np.float32(np.float32(grp) * np.float32(np.float32(1.0) / np.float32(H))))
-    if tl * H > grp:
+def first_row_split(r, H):
+    """The kernel's r / H through a binary32 reciprocal, corrected once."""
+    tl = int(np.float32(np.float32(r) * np.float32(np.float32(1.0) / np.float32(H))))
+    if tl * H > r:
         tl -= 1
-    if (tl + 1) * H <= grp:
+    if (tl + 1) * H <= r:
         tl += 1
-    return tl, grp - tl * H
+    return tl, r - tl * H
 
 
-def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS):
+def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_waves=MIN_WAVES):
     """Returns per-slot write counts of q/k outputs; asserts read bounds."""
-    p = plan(T, D, rd, es, fused=fused, wave_tokens=wave_tokens)
+    p = plan(T, D, rd, es, fused=fused, wave_tokens=wave_tokens, heads=heads,
+             min_waves=min_waves)
     v, half, lpr, rpw, lrot, nt = p["v"], p["half"], p["lpr"], p["rpw"], p["lrot"], p["nt"]
+    parts = p["parts"]
     writes = [np.zeros((T, H, D), dtype=np.int32) for H in heads]
     lanes = np.arange(WAVE)
     grp = lanes // lpr
@@ -68,29 +75,35 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS):
     assert np.all(col_a + v <= D) and np.all(col_b + v <= D)
     xts = [H * D + 8 * v for H in heads]          # a token stride wider than the rows
     for w in range(p["nwaves"]):
-        t0 = w * nt
+        tile, part = divmod(w, parts)
+        t0 = tile * nt
         assert t0 < T
         ntok = min(nt, T - t0)
         if fused:
             assert ntok * half <= p["lds_doubles"] // 2
+        steps_q = -(-ntok * heads[0] // rpw)
+        steps_all = steps_q + -(-ntok * heads[1] // rpw)
+        sb, se = steps_all * part // parts, steps_all * (part + 1) // parts
         for s, H in enumerate(heads):
             if H == 0:
+                continue
+            lo = sb if s == 0 else max(sb, steps_q) - steps_q
+            hi = min(se, steps_q) if s == 0 else se - steps_q
+            if lo >= hi:
                 continue
             extent = ((ntok - 1) * xts[s] + H * D) * es   # tile buffer size in bytes
             assert extent < OUT_OF_RANGE
             nrows = ntok * H
-            split = [first_row_split(int(g), H) for g in grp]
+            split = [first_row_split(int(lo * rpw + g), H) for g in grp]
             tl = np.array([a for a, _ in split])
             h = np.array([b for _, b in split])
-            assert np.all(tl == grp // H) and np.all(h == grp % H)
             dq, dr = rpw // H, rpw % H
             xo = (tl * xts[s] + h * D) * es
             xinc = (dq * xts[s] + dr * D) * es
             xwrap = (xts[s] - H * D) * es
-            steps = -(-nrows // rpw)
-            full = steps // U
-            batches = [U] * full + [1] * (steps - full * U)
-            r0 = 0
+            full = (hi - lo) // U
+            batches = [U] * full + [1] * ((hi - lo) - full * U)
+            r0 = lo * rpw
             for uu in batches:
                 for u in range(uu):
                     r = r0 + u * rpw + grp
@@ -119,10 +132,15 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS):
     return writes, p
 
 
-def test_first_row_split_exact_for_all_head_counts():
+def test_first_row_split_exact():
     for H in range(1, 4097):
         for g in range(64):
             assert first_row_split(g, H) == (g // H, g % H), (g, H)
+    rng = np.random.default_rng(0)
+    for _ in range(20000):
+        H = int(rng.integers(1, 100000))
+        r = int(rng.integers(0, 2 ** 23))
+        assert first_row_split(r, H) == (r // H, r % H), (r, H)
 
 
 GEOMS = [
@@ -144,10 +162,12 @@ GEOMS = [
 ]
 
 
-@pytest.mark.parametrize("U,wave_tokens", [(1, 1), (2, 1), (4, 2), (2, 16)])
+@pytest.mark.parametrize("U,wave_tokens,min_waves", [(1, 1, 1), (2, 1, 2048), (4, 2, 2048),
+                                                      (2, 16, 64), (2, 1, 1 << 20)])
 @pytest.mark.parametrize("T,heads,D,rd,es", GEOMS)
-def test_every_output_written_once_and_reads_in_bounds(T, heads, D, rd, es, U, wave_tokens):
-    writes, p = simulate(T, heads, D, rd, es, U=U, wave_tokens=wave_tokens)
+def test_every_output_written_once_and_reads_in_bounds(T, heads, D, rd, es, U, wave_tokens,
+                                                         min_waves):
+    writes, p = simulate(T, heads, D, rd, es, U=U, wave_tokens=wave_tokens, min_waves=min_waves)
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))
@@ -161,8 +181,18 @@ def test_rms_norm_only_geometry():
     assert np.all(writes[0] == 1)
 
 
+def test_decode_sized_launch_splits_tiles():
+    p = plan(512, 128, 128, 2, heads=(32, 4))
+    assert p["parts"] == 4 and p["nwaves"] == 2048
+    writes, p = simulate(512, (32, 4), 128, 128, 2)
+    assert np.all(writes[0] == 1) and np.all(writes[1] == 1)
+
+
 def test_full_size_plans():
     for name, wl in W.WORKLOADS.items():
-        p = plan(wl.T, wl.D, wl.rotary_dim, wl.elem_bytes)
-        assert p["nwaves"] * p["nt"] >= wl.T > (p["nwaves"] - 1) * p["nt"]
+        p = plan(wl.T, wl.D, wl.rotary_dim, wl.elem_bytes, heads=(wl.hq, wl.hk))
+        tiles = p["nwaves"] // p["parts"]
+        assert tiles * p["nt"] >= wl.T > (tiles - 1) * p["nt"]
         assert p["lds_doubles"] * WPB * 8 <= 32 * 1024
+        if wl.T >= MIN_WAVES:
+            assert p["parts"] == 1

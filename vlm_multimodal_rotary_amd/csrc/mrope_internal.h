@@ -46,7 +46,8 @@ struct QKParams {
   int lpr;               // lanes per head row: D / (2 * V)
   int rpw;               // rows per wavefront instruction: 64 / lpr
   int lrot;              // rotary lanes per row: half / V
-  int nt;                // tokens per wavefront (set by the launcher)
+  int nt;                // tokens per tile (set by the launcher)
+  int parts;             // wavefronts per tile (set by the launcher)
   int dq[2], dr[2];      // rpw = dq * heads + dr, per tensor (launcher)
   float inv_heads[2];    // 1 / heads, per tensor (launcher)
   const int32_t* pos;

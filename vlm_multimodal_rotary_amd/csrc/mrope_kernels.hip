@@ -44,6 +44,10 @@
 #ifndef MROPE_NT_STORES_F32
 #define MROPE_NT_STORES_F32 0
 #endif
+// Wavefronts a launch aims to have in flight before it splits tiles.
+#ifndef MROPE_MIN_WAVES
+#define MROPE_MIN_WAVES 2048
+#endif
 // Tokens per wavefront (at most; fewer when a token's cos/sin is large).
 #ifndef MROPE_WAVE_TOKENS
 #define MROPE_WAVE_TOKENS 1
@@ -51,6 +55,8 @@
 
 namespace mrope {
 namespace {
+
+constexpr int64_t kMinWaves = MROPE_MIN_WAVES;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -442,10 +448,18 @@ qk_kernel(const QKParams p, const ColTable tab) {
   const uint32_t ca = (uint32_t)(col_a * ES);
   const uint32_t cb = (uint32_t)(col_b * ES);
 
-  // This wavefront's tile: tokens [t0, t0 + ntok).
-  const int64_t t0 = ((int64_t)blockIdx.x * kWavesPerBlock + wib) * p.nt;
+  // This wavefront's tile (tokens [t0, t0 + ntok)) and its part of the
+  // tile's row-steps (q steps first, then k steps), p.parts parts per tile.
+  const uint32_t wave = blockIdx.x * (uint32_t)kWavesPerBlock + (uint32_t)wib;
+  const uint32_t tile = wave / (uint32_t)p.parts;
+  const int part = (int)(wave - tile * (uint32_t)p.parts);
+  const int64_t t0 = (int64_t)tile * p.nt;
   if (t0 >= p.T) return;
   const int ntok = (int)((p.T - t0) < p.nt ? (p.T - t0) : p.nt);
+  const int steps_q = (ntok * p.heads[0] + rpw - 1) / rpw;
+  const int steps_all = steps_q + (ntok * p.heads[1] + rpw - 1) / rpw;
+  const int step_begin = steps_all * part / p.parts;
+  const int step_end = steps_all * (part + 1) / p.parts;
   {
     // Decode: token t0 is token i of sequence b; its text position (the same
     // on every axis) continues the sequence's cache.
@@ -488,6 +502,10 @@ qk_kernel(const QKParams p, const ColTable tab) {
     for (int s = 0; s < 2; ++s) {
       const int H = p.heads[s];
       if (H == 0) continue;
+      // This part's steps of tensor s.
+      const int lo = s == 0 ? step_begin : (step_begin > steps_q ? step_begin : steps_q) - steps_q;
+      const int hi = s == 0 ? (step_end < steps_q ? step_end : steps_q) : step_end - steps_q;
+      if (lo >= hi) continue;
       const int64_t xts = p.x_ts[s];
       const int64_t yts = p.y_ts[s];
       SlotState<CB> st;
@@ -510,11 +528,13 @@ qk_kernel(const QKParams p, const ColTable tab) {
       st.nrows = ntok * H;
       st.dq = p.dq[s];
       st.dr = p.dr[s];
-      // grp / H for grp < 64 through a binary32 reciprocal, corrected once.
-      st.tl = (int)((float)grp * p.inv_heads[s]);
-      if (st.tl * H > grp) --st.tl;
-      if ((st.tl + 1) * H <= grp) ++st.tl;
-      st.h = grp - st.tl * H;
+      // First row of this lane: r = lo * rpw + grp; r / H through a binary32
+      // reciprocal (r < 2^23, so the estimate is off by at most one), corrected.
+      const int r_first = lo * rpw + grp;
+      st.tl = (int)((float)r_first * p.inv_heads[s]);
+      if (st.tl * H > r_first) --st.tl;
+      if ((st.tl + 1) * H <= r_first) ++st.tl;
+      st.h = r_first - st.tl * H;
       st.xo = (uint32_t)(((int64_t)st.tl * xts + (int64_t)st.h * p.D) * ES);
       st.yo = (uint32_t)(((int64_t)st.tl * yts + (int64_t)st.h * p.D) * ES);
       st.xinc = (uint32_t)(((int64_t)st.dq * xts + (int64_t)st.dr * p.D) * ES);
@@ -532,13 +552,12 @@ qk_kernel(const QKParams p, const ColTable tab) {
       }
 
       // Full batches of U row-steps, then single steps for the remainder.
-      const int steps = (st.nrows + rpw - 1) / rpw;
-      const int full = steps / U;
-      int r0 = 0;
+      const int full = (hi - lo) / U;
+      int r0 = lo * rpw;
       for (int g = 0; g < full; ++g, r0 += U * rpw)
         process_steps<BF16, V, CS, NORM, LPR, U>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
                                                  col_a, wa, wb, lc, ls, t0);
-      for (; r0 < st.nrows; r0 += rpw)
+      for (; r0 < hi * rpw; r0 += rpw)
         process_steps<BF16, V, CS, NORM, LPR, 1>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
                                                  col_a, wa, wb, lc, ls, t0);
     }
@@ -573,7 +592,16 @@ int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
     p.dr[s] = p.rpw - p.dq[s] * H;
     p.inv_heads[s] = 1.0f / (float)H;
   }
-  const int64_t waves = (p.T + p.nt - 1) / p.nt;
+  // Small launches split each tile's row-steps over several wavefronts so
+  // that about kMinWaves are in flight; large ones keep one per tile.
+  const int64_t tiles = (p.T + p.nt - 1) / p.nt;
+  const int tile_steps = (p.nt * p.heads[0] + p.rpw - 1) / p.rpw +
+                         (p.nt * p.heads[1] + p.rpw - 1) / p.rpw;
+  int64_t parts = (kMinWaves + tiles - 1) / tiles;
+  if (parts > tile_steps) parts = tile_steps;
+  if (parts < 1) parts = 1;
+  p.parts = (int)parts;
+  const int64_t waves = tiles * parts;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   const int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(double) : 0;
   hipLaunchKernelGGL((qk_kernel<BF16, V, CS, NORM, LPR>), dim3((unsigned)blocks),
