@@ -46,6 +46,16 @@ Readings where the pages leave a step open:
 6. An interleaved section whose rule would give an axis fewer columns than its
    section entry is rejected (assertion), as is a section that does not sum to
    rotary_dim/2.
+7. Rotation precision "dtype" (M01 drill shape trace, the apply_rotary row,
+   and its broadcast note: for bf16 input cos/sin are cast to x.dtype before
+   the multiplies, as HF does): every tensor operation of
+   ``x*cos + rotate_half(x)*sin`` rounds to x.dtype, and a bf16 operation
+   computes in binary32 before it rounds (the tensor arithmetic of PyTorch).
+   So ``bf(fl32(bf(x*c_b) + bf(-x2*s_b)))`` with ``c_b = bf(cos)``.
+8. Rotation precision "fp32" (Qwen3-VL ``apply_rotary_pos_emb_vision``):
+   q/k and cos/sin are upcast to binary32, each product and the sum rounds
+   to binary32, and the result is cast to x.dtype once at the end.  For
+   binary32 input "dtype" and "fp32" are the same arithmetic.
 """
 from __future__ import annotations
 
@@ -320,6 +330,51 @@ def apply_rotary_values(y, cos, sin, rotary_dim: int):
     return out
 
 
+PRECISIONS = ("exact", "dtype", "fp32")
+
+
+def apply_rotary_tensor_ops(y, cos, sin, rotary_dim: int, dtype: str, precision: str):
+    """The rotation as a sequence of tensor operations, each rounded.
+
+    precision "dtype": cos/sin cast to x.dtype first, then the two products
+    and their sum each rounded to x.dtype (M01 drill, apply_rotary row of the
+    shape trace).  precision "fp32": cos/sin and y in binary32, the products
+    and the sum each rounded to binary32 (Qwen3-VL vision rotary); the cast
+    to x.dtype happens when the result is encoded.
+
+    ``y`` holds exact float64 values of the stored input; products of two
+    values of at most 24 significant bits are exact in float64, and the sum
+    of two binary32 values rounded in float64 and then to binary32 equals the
+    sum rounded once (53 >= 2*24 + 2), so ``fl32`` after the float64
+    operation is the binary32 operation.
+    """
+    if precision == "dtype":
+        rnd = bf if dtype == "bf16" else fl32
+    elif precision == "fp32":
+        rnd = fl32
+    else:
+        raise ValueError(precision)
+    y = np.asarray(y, dtype=np.float64)
+    c = np.asarray(cos, dtype=np.float32).astype(np.float64)[:, None, :]
+    s = np.asarray(sin, dtype=np.float32).astype(np.float64)[:, None, :]
+    if precision == "dtype":
+        c = np.asarray(rnd(c), dtype=np.float64)
+        s = np.asarray(rnd(s), dtype=np.float64)
+    rot = y[..., :rotary_dim]
+    p1 = np.asarray(rnd(rot * c), dtype=np.float64)
+    p2 = np.asarray(rnd(rotate_half(rot) * s), dtype=np.float64)
+    out = y.copy()
+    out[..., :rotary_dim] = rnd(p1 + p2)
+    return out
+
+
+def rotary_values(y, cos, sin, rotary_dim: int, dtype: str, precision: str = "exact"):
+    """The rotation in the requested precision (float64 values; encode rounds)."""
+    if precision == "exact":
+        return apply_rotary_values(y, cos, sin, rotary_dim)
+    return apply_rotary_tensor_ops(y, cos, sin, rotary_dim, dtype, precision)
+
+
 # ---------------------------------------------------------------------------
 # Entry points mirroring the library's operations (stored representations)
 # ---------------------------------------------------------------------------
@@ -330,15 +385,16 @@ def rms_norm(x, w, eps: float, dtype: str):
     return encode(y, dtype)
 
 
-def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, dtype: str):
+def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, dtype: str, precision: str = "exact"):
     """Rotate q[T, hq, D] and k[T, hk, D] with the same per-token cos/sin."""
-    qo = encode(apply_rotary_values(decode(q, dtype), cos, sin, rotary_dim), dtype)
-    ko = encode(apply_rotary_values(decode(k, dtype), cos, sin, rotary_dim), dtype)
+    qo = encode(rotary_values(decode(q, dtype), cos, sin, rotary_dim, dtype, precision), dtype)
+    ko = encode(rotary_values(decode(k, dtype), cos, sin, rotary_dim, dtype, precision), dtype)
     return qo, ko
 
 
 def rmsnorm_mrope_qk(q, k, pos, *, rotary_dim: int, theta: float, section, layout,
-                     wq=None, wk=None, eps: float = 0.0, dtype: str = "bf16"):
+                     wq=None, wk=None, eps: float = 0.0, dtype: str = "bf16",
+                     precision: str = "exact"):
     """The fused hot path: optional per-head RMSNorm, then MRoPE, on q and k.
 
     The RMSNorm output is on the dtype grid (cast back) before the rotation,
@@ -355,8 +411,8 @@ def rmsnorm_mrope_qk(q, k, pos, *, rotary_dim: int, theta: float, section, layou
     if wq is not None:
         qv = rms_norm_values(qv, decode(wq, dtype), eps, dtype)
         kv = rms_norm_values(kv, decode(wk, dtype), eps, dtype)
-    qo = encode(apply_rotary_values(qv, cos, sin, rotary_dim), dtype)
-    ko = encode(apply_rotary_values(kv, cos, sin, rotary_dim), dtype)
+    qo = encode(rotary_values(qv, cos, sin, rotary_dim, dtype, precision), dtype)
+    ko = encode(rotary_values(kv, cos, sin, rotary_dim, dtype, precision), dtype)
     return qo, ko
 
 
@@ -382,7 +438,8 @@ def decode_positions(cache_len, new_tokens: int, rope_delta=None) -> np.ndarray:
 
 
 def mrope_decode_qk(q, k, cache_len, new_tokens: int, rope_delta, k_cache, *, rotary_dim: int,
-                    theta: float, wq=None, wk=None, eps: float = 0.0, dtype: str = "bf16"):
+                    theta: float, wq=None, wk=None, eps: float = 0.0, dtype: str = "bf16",
+                    precision: str = "exact"):
     """One decode step: RMSNorm + rotary on q and k of B * new_tokens tokens
     whose positions follow ``decode_positions`` (text positions: the same on
     every axis, so the rotation is 1-D RoPE whatever the section), then the
@@ -395,7 +452,7 @@ def mrope_decode_qk(q, k, cache_len, new_tokens: int, rope_delta, k_cache, *, ro
     half = rotary_dim // 2
     qo, ko = rmsnorm_mrope_qk(q, k, pos.reshape(1, -1), rotary_dim=rotary_dim, theta=theta,
                               section=(half,), layout=LAYOUT_CHUNKED, wq=wq, wk=wk, eps=eps,
-                              dtype=dtype)
+                              dtype=dtype, precision=precision)
     cache = np.array(k_cache, copy=True)
     cap = cache.shape[1]
     for b in range(len(cache_len)):

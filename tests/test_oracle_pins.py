@@ -462,6 +462,95 @@ def test_fused_equals_composition_of_the_parts():
 
 
 # ---------------------------------------------------------------------------
+# Rotation precisions written as tensor operations
+# ---------------------------------------------------------------------------
+
+def _torch_tensor_rotation(x_stored, cos, sin, rd, dtype, precision):
+    """``x*cos + rotate_half(x)*sin`` evaluated by PyTorch CPU tensor ops, one
+    op at a time, in the dtypes the two readings name: cos/sin cast to the
+    tensor's dtype ("dtype", M01 drill), or everything upcast to float32 and
+    one cast at the end ("fp32", Qwen3-VL vision rotary).  PyTorch's own
+    kernels do the rounding, so this is an implementation independent of the
+    oracle's float64-plus-explicit-rounding arithmetic."""
+    import torch
+    if dtype == "bf16":
+        x = torch.from_numpy(np.ascontiguousarray(x_stored).view(np.int16)).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(np.ascontiguousarray(x_stored))
+    c = torch.from_numpy(np.ascontiguousarray(cos))[:, None, :]
+    s = torch.from_numpy(np.ascontiguousarray(sin))[:, None, :]
+    xr = x[..., :rd]
+    if precision == "dtype":
+        c, s = c.to(x.dtype), s.to(x.dtype)
+    else:
+        xr = xr.float()
+    h = rd // 2
+    rh = torch.cat((-xr[..., h:], xr[..., :h]), dim=-1)
+    out = (xr * c + rh * s).to(x.dtype)
+    out = torch.cat((out, x[..., rd:]), dim=-1)
+    if dtype == "bf16":
+        return out.view(torch.int16).numpy().view(np.uint16)
+    return out.numpy()
+
+
+def check_tensor_op_precisions():
+    rng = np.random.default_rng(41)
+    for dtype in ("bf16", "f32"):
+        # 2^20 elements: binary32 arithmetic then one bf16 cast differs from
+        # the single rounding on about one element in 40000
+        for T, H, D, rd in ((2048, 8, 64, 64), (96, 3, 48, 16)):
+            v = rng.standard_normal((T, H, D)) * 2.0 ** rng.integers(-12, 12, (T, H, 1))
+            x = O.encode(v, dtype)
+            pos = rng.integers(0, 200000, (3, T)).astype(np.int32)
+            cos, sin = O.mrope_cos_sin(pos, O.inv_freq(rd, 1e6), (rd // 4, rd // 8, rd // 8),
+                                       "interleaved", rd)
+            exact = O.apply_rotary_qk(x, x, cos, sin, rd, dtype)[0]
+            for precision in ("dtype", "fp32"):
+                got = O.apply_rotary_qk(x, x, cos, sin, rd, dtype, precision)[0]
+                want = _torch_tensor_rotation(x, cos, sin, rd, dtype, precision)
+                assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (dtype, precision)
+                # the rounding points matter: each reading differs from one rounding
+                if rd == D:
+                    assert np.count_nonzero(got != exact) > 0, (dtype, precision)
+
+
+def test_tensor_op_precisions_match_pytorch_tensor_arithmetic():
+    check_tensor_op_precisions()
+
+
+def test_tensor_op_precisions_differ_where_the_readings_differ():
+    """For bf16 the two readings give different results on some elements
+    (cos/sin rounded to 8 bits and three roundings, against binary32
+    arithmetic and one cast); for binary32 they are the same arithmetic."""
+    rng = np.random.default_rng(42)
+    T, H, D = 64, 4, 32
+    pos = rng.integers(0, 100000, (3, T)).astype(np.int32)
+    cos, sin = O.mrope_cos_sin(pos, O.inv_freq(D, 1e6), (8, 4, 4), "interleaved", D)
+    xb = O.encode(rng.standard_normal((T, H, D)), "bf16")
+    a = O.apply_rotary_qk(xb, xb, cos, sin, D, "bf16", "dtype")[0]
+    b = O.apply_rotary_qk(xb, xb, cos, sin, D, "bf16", "fp32")[0]
+    assert np.count_nonzero(a != b) > 0
+    xf = O.encode(rng.standard_normal((T, H, D)), "f32")
+    a = O.apply_rotary_qk(xf, xf, cos, sin, D, "f32", "dtype")[0]
+    b = O.apply_rotary_qk(xf, xf, cos, sin, D, "f32", "fp32")[0]
+    assert np.array_equal(a, b)
+
+
+def test_every_precision_is_the_identity_at_position_zero():
+    rng = np.random.default_rng(43)
+    T, H, D = 5, 2, 16
+    pos = np.zeros((3, T), dtype=np.int32)
+    for dtype in ("bf16", "f32"):
+        x = O.encode(rng.standard_normal((T, H, D)), dtype)
+        for precision in O.PRECISIONS:
+            out, _ = O.rmsnorm_mrope_qk(x, x, pos, rotary_dim=D, theta=1e6, section=(4, 2, 2),
+                                        layout="interleaved", dtype=dtype, precision=precision)
+            assert np.array_equal(np.abs(out.astype(np.float64) if dtype == "f32" else
+                                         O.decode(out, dtype)),
+                                  np.abs(O.decode(x, dtype))), (dtype, precision)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -540,8 +629,19 @@ def _mut_cos_sin_swapped(pos, axis, invc):
     return s, c
 
 
+def _mut_tensor_ops_cos_not_cast(y, cos, sin, rotary_dim, dtype, precision):
+    # the cast of cos/sin to the tensor dtype forgotten: binary32 arithmetic
+    return _ORIG_TENSOR_OPS(y, cos, sin, rotary_dim, dtype, "fp32")
+
+
+def _mut_tensor_ops_products_unrounded(y, cos, sin, rotary_dim, dtype, precision):
+    # the products kept exact: only the cast at the end rounds
+    return O.apply_rotary_values(y, cos, sin, rotary_dim)
+
+
 _ORIG_AXIS = O.axis_table
 _ORIG_CS = O.cos_sin_half
+_ORIG_TENSOR_OPS = O.apply_rotary_tensor_ops
 
 MUTATIONS = [
     ("rotate_half", _mut_rotate_half_wrong_sign, check_rotary_printed),
@@ -553,6 +653,8 @@ MUTATIONS = [
     ("rms_norm_values", _mut_norm_values_multiply_first, check_rmsnorm_bf16_order),
     ("apply_rotary_values", _mut_gptj_pairs, check_rotation_bruteforce),
     ("cos_sin_half", _mut_cos_sin_swapped, check_cos_sin_printed),
+    ("apply_rotary_tensor_ops", _mut_tensor_ops_cos_not_cast, check_tensor_op_precisions),
+    ("apply_rotary_tensor_ops", _mut_tensor_ops_products_unrounded, check_tensor_op_precisions),
 ]
 
 

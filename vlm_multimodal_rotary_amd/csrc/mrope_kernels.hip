@@ -451,15 +451,17 @@ qk_kernel(const QKParams p, const ColTable tab) {
   // This wavefront's tile (tokens [t0, t0 + ntok)) and its part of the
   // tile's row-steps (q steps first, then k steps), p.parts parts per tile.
   const uint32_t wave = blockIdx.x * (uint32_t)kWavesPerBlock + (uint32_t)wib;
-  const uint32_t tile = wave / (uint32_t)p.parts;
-  const int part = (int)(wave - tile * (uint32_t)p.parts);
+  // Large launches have one part per tile; the divisions are skipped there.
+  const bool split = p.parts > 1;
+  const uint32_t tile = split ? wave / (uint32_t)p.parts : wave;
+  const int part = split ? (int)(wave - tile * (uint32_t)p.parts) : 0;
   const int64_t t0 = (int64_t)tile * p.nt;
   if (t0 >= p.T) return;
   const int ntok = (int)((p.T - t0) < p.nt ? (p.T - t0) : p.nt);
   const int steps_q = (ntok * p.heads[0] + rpw - 1) / rpw;
   const int steps_all = steps_q + (ntok * p.heads[1] + rpw - 1) / rpw;
-  const int step_begin = steps_all * part / p.parts;
-  const int step_end = steps_all * (part + 1) / p.parts;
+  const int step_begin = split ? steps_all * part / p.parts : 0;
+  const int step_end = split ? steps_all * (part + 1) / p.parts : steps_all;
   {
     // Decode: token t0 is token i of sequence b; its text position (the same
     // on every axis) continues the sequence's cache.
