@@ -58,7 +58,7 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, wl, budget_s: float = 12.0):
+def cpu_baseline(inp, wl, budget_s: float = 12.0, precision: str = "exact"):
     """The oracle as it stands, on consecutive 64-token windows of the same
     workload, until about budget_s of CPU time; single thread."""
     from oracle import mrope_oracle as O
@@ -72,7 +72,8 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0):
         O.rmsnorm_mrope_qk(inp["q"][sl], inp["k"][sl], inp["pos"][:, sl],
                            rotary_dim=wl.rotary_dim, theta=wl.theta, section=wl.section,
                            layout=wl.layout, wq=inp["wq"] if wl.norm else None,
-                           wk=inp["wk"] if wl.norm else None, eps=wl.eps, dtype=wl.dtype)
+                           wk=inp["wk"] if wl.norm else None, eps=wl.eps, dtype=wl.dtype,
+                           precision=precision)
         done += chunk
         t0 = (t0 + chunk) % (T - chunk + 1)
         elapsed = time.perf_counter() - start
@@ -101,6 +102,9 @@ def main():
     ap.add_argument("--min-warmup-s", type=float, default=0.5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--precision", default="exact", choices=["exact", "dtype", "fp32"],
+                    help="rotation rounding: exact (default), dtype (cos/sin cast to the "
+                         "tensor dtype, bf16 tensor ops) or fp32 (fp32 tensor ops)")
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps in one HIP graph and time graph replays "
@@ -140,14 +144,16 @@ def main():
 
         def step():
             M.mrope_decode_qk(q, k, cache_len, rope_delta, wl.new_tokens, wl.rotary_dim,
-                              wl.theta, k_cache, wq=wq, wk=wk, eps=wl.eps, q_out=q_out)
+                              wl.theta, k_cache, wq=wq, wk=wk, eps=wl.eps, q_out=q_out,
+                              precision=args.precision)
     else:
         pos = dev(inp["pos"])
         k_out = torch.empty_like(k)
 
         def step():
             M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
-                               wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out)
+                               wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out,
+                               precision=args.precision)
 
     t_warm = time.perf_counter()
     done = 0
@@ -191,15 +197,17 @@ def main():
 
     alg_bytes = wl.algorithmic_bytes()
     achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name) if args.precision == "exact" else None
     if decode:
         config = {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.new_tokens,
                   "hq": wl.hq, "hk": wl.hk, "D": wl.D, "rotary_dim": wl.rotary_dim,
-                  "theta": wl.theta, "cache_rows": wl.capacity, "rmsnorm": wl.norm}
+                  "theta": wl.theta, "cache_rows": wl.capacity, "rmsnorm": wl.norm,
+                  "precision": args.precision}
     else:
         config = {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
                   "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
-                  "section": list(wl.section), "rmsnorm": wl.norm}
+                  "section": list(wl.section), "rmsnorm": wl.norm,
+                  "precision": args.precision}
     line = {
         "metric": ("decode tokens/s, mrope_decode_qk" if decode else
                    "Q+K tokens/s, fused RMSNorm+MRoPE (rmsnorm_mrope_qk)"),
@@ -225,7 +233,7 @@ def main():
                      else "qk_kernel (rmsnorm_mrope_qk)"},
     }
     if not args.no_cpu_baseline and not decode:
-        line["cpu_baseline"] = cpu_baseline(inp, wl)
+        line["cpu_baseline"] = cpu_baseline(inp, wl, precision=args.precision)
     print(json.dumps(line), flush=True)
 
 

@@ -61,6 +61,26 @@ extern "C" {
 #define MROPE_DTYPE_F32  0
 #define MROPE_DTYPE_BF16 1
 
+/* Rotation precision (argument `precision` of the rotating entry points).
+ *  EXACT: the products of the stored value and the binary32 cos/sin and
+ *         their sum are evaluated in double (the products are exact), rounded
+ *         to binary32 and then (bf16) to bfloat16: the binary32 result of
+ *         the rotation, rounded to the tensor's dtype.
+ *  DTYPE: the rotation as tensor operations in the tensor's dtype ([M01]
+ *         shape trace, apply_rotary row, and its broadcast note: cos/sin are
+ *         cast to x.dtype before the multiplies, as HF's text rotary does):
+ *         c = dt(cos), s = dt(sin); out = dt(dt(x*c) + dt(rotate_half(x)*s)),
+ *         where dt() rounds to the dtype and each bf16 operation is computed
+ *         in binary32 before it rounds.
+ *  FP32:  the rotation as binary32 tensor operations with one cast at the
+ *         end ([QVL] apply_rotary_pos_emb_vision): out = dt(f(f(x*cos) +
+ *         f(rotate_half(x)*sin))) with f() rounding to binary32.
+ * For MROPE_DTYPE_F32, DTYPE and FP32 are the same arithmetic.  No mode fuses
+ * a product into the sum. */
+#define MROPE_PRECISION_EXACT 0
+#define MROPE_PRECISION_DTYPE 1
+#define MROPE_PRECISION_FP32  2
+
 /* Largest rotary_dim the kernels accept (the per-column table travels as a
  * kernel argument). */
 #define MROPE_MAX_ROTARY_DIM 512
@@ -137,19 +157,21 @@ int rms_norm(const void* x, int64_t x_tok_stride, int64_t T, int heads, int D,
  *   out[j]      = x[j]*cos[j]      - x[j+h]*sin[j]        (j < h = rotary_dim/2)
  *   out[j+h]    = x[j+h]*cos[j+h]  + x[j]*sin[j+h]
  *   out[j]      = x[j]                                    (rotary_dim <= j < D)
- * computed in double from the stored inputs and the binary32 tables, rounded
- * once to binary32 and then (bf16) to bfloat16.
+ * evaluated with the rounding points `precision` names (MROPE_PRECISION_*;
+ * EXACT: in double from the stored inputs and the binary32 tables, rounded
+ * once to binary32 and then (bf16) to bfloat16).
  *   q: device [T][hq][D], token stride q_tok_stride; k likewise with hk heads
  *      (k may be NULL when hk == 0).
  *   cos, sin: device binary32 [T][rotary_dim], token stride cs_tok_stride.
  *   q_out, k_out: device, same shapes, own token strides (may equal q / k).
- * EINVAL on bad shapes (rotary_dim odd, <= 0 or > D), null pointers, overlap.
+ * EINVAL on bad shapes (rotary_dim odd, <= 0 or > D), null pointers, overlap,
+ * or an unknown precision.
  */
 int apply_rotary_qk(const void* q, int64_t q_tok_stride, int hq,
                     const void* k, int64_t k_tok_stride, int hk,
                     int64_t T, int D, int rotary_dim,
                     const float* cos, const float* sin, int64_t cs_tok_stride,
-                    int dtype,
+                    int dtype, int precision,
                     void* q_out, int64_t q_out_tok_stride,
                     void* k_out, int64_t k_out_tok_stride,
                     void* stream);
@@ -165,8 +187,10 @@ int apply_rotary_qk(const void* q, int64_t q_tok_stride, int hq,
  * apply_rotary_pos_emb; [M01] "Where it sits"; [QVL] the vision rotary).
  * cos/sin are formed once per (token, column) and shared by all hq + hk heads.
  * The result is bit-identical to rms_norm followed by mrope_cos_sin and
- * apply_rotary_qk.
+ * apply_rotary_qk with the same precision.
  *   wq, wk: device [D] weights of the dtype; both NULL = no normalisation.
+ *   precision: MROPE_PRECISION_* (rotation only; the RMSNorm is the same in
+ *              every mode).
  *   Other arguments as in the functions above.
  * EINVAL as above, or if exactly one of wq / wk is NULL.
  */
@@ -175,7 +199,7 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq,
                      int64_t T, int D, int rotary_dim,
                      const int32_t* pos, int64_t pos_axis_stride, int n_axes,
                      const int* section, int n_sections, int layout, double theta,
-                     const void* wq, const void* wk, float eps, int dtype,
+                     const void* wq, const void* wk, float eps, int dtype, int precision,
                      void* q_out, int64_t q_out_tok_stride,
                      void* k_out, int64_t k_out_tok_stride,
                      void* stream);
@@ -188,8 +212,9 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq,
  * Token i of sequence b is row b*new_tokens + i of q and k; its position is
  * p = cache_len[b] + i + rope_delta[b] (rope_delta NULL = 0) on every axis,
  * so the rotation is 1-D RoPE with inv_freq = mrope_inv_freq(rotary_dim,
- * theta) whatever the model's section.  Optional per-head RMSNorm as in
- * rmsnorm_mrope_qk.  Rotated q goes to q_out; rotated k of token (b, i) is
+ * theta) whatever the model's section.  Optional per-head RMSNorm and the
+ * rotation precision as in rmsnorm_mrope_qk.  Rotated q goes to q_out;
+ * rotated k of token (b, i) is
  * written into the KV cache row
  *     k_cache + b*k_cache_seq_stride + (cache_len[b] + i)*k_cache_tok_stride
  * (hk*D contiguous elements); a row at or past k_cache_capacity (or below 0)
@@ -207,7 +232,7 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq,
                     const void* k, int64_t k_tok_stride, int hk,
                     int batch, int new_tokens, int D, int rotary_dim,
                     const int32_t* cache_len, const int32_t* rope_delta, double theta,
-                    const void* wq, const void* wk, float eps, int dtype,
+                    const void* wq, const void* wk, float eps, int dtype, int precision,
                     void* q_out, int64_t q_out_tok_stride,
                     void* k_cache, int64_t k_cache_seq_stride, int64_t k_cache_tok_stride,
                     int k_cache_capacity, void* stream);

@@ -111,20 +111,23 @@ def _fused(**kw):
                 D=128, rd=128, pos=FAKE + 0x8000000, pos_stride=16, n_axes=3,
                 section=(24, 20, 20), layout=_lib.LAYOUT_INTERLEAVED, theta=1e6,
                 wq=FAKE + 0xC000000, wk=FAKE + 0xC001000, eps=1e-6, dtype=_lib.DTYPE_BF16,
-                qo=FAKE + 0x20000000, qo_ts=32 * 128, ko=FAKE + 0x24000000, ko_ts=4 * 128)
+                prec=_lib.PRECISION_EXACT, qo=FAKE + 0x20000000, qo_ts=32 * 128,
+                ko=FAKE + 0x24000000, ko_ts=4 * 128)
     args.update(kw)
     a = args
     sec = list(a["section"]) if a["section"] is not None else []
     return _lib.load().rmsnorm_mrope_qk(
         a["q"], a["q_ts"], a["hq"], a["k"], a["k_ts"], a["hk"], a["T"], a["D"], a["rd"],
         a["pos"], a["pos_stride"], a["n_axes"], _lib.int_array(sec), len(sec), a["layout"],
-        a["theta"], a["wq"], a["wk"], a["eps"], a["dtype"], a["qo"], a["qo_ts"], a["ko"],
-        a["ko_ts"], None)
+        a["theta"], a["wq"], a["wk"], a["eps"], a["dtype"], a["prec"], a["qo"], a["qo_ts"],
+        a["ko"], a["ko_ts"], None)
 
 
 @fake_ptr_test
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), _lib.MROPE_EUNSUPPORTED),
+    (dict(prec=3), _lib.MROPE_EINVAL),
+    (dict(prec=-1), _lib.MROPE_EINVAL),
     (dict(rd=127), _lib.MROPE_EINVAL),
     (dict(rd=256), _lib.MROPE_EINVAL),               # > D
     (dict(D=127, rd=126), _lib.MROPE_EINVAL),        # odd D
@@ -178,12 +181,16 @@ def test_rms_norm_and_apply_rotary_reject_bad_arguments():
                       FAKE + 0x100000, 127, None)
     assert rc == _lib.MROPE_EINVAL                     # odd D
     rc = lib.apply_rotary_qk(FAKE, 128, 1, None, 0, 0, 4, 128, 128, None, None, 128,
-                             _lib.DTYPE_F32, FAKE + 0x100000, 128, None, 0, None)
+                             _lib.DTYPE_F32, 0, FAKE + 0x100000, 128, None, 0, None)
     assert rc == _lib.MROPE_EINVAL                     # no cos/sin
     rc = lib.apply_rotary_qk(FAKE, 128, 1, None, 0, 0, 4, 128, 128, FAKE + 0x300000,
-                             FAKE + 0x100000, 128, _lib.DTYPE_F32, FAKE + 0x100000, 128, None,
+                             FAKE + 0x100000, 128, _lib.DTYPE_F32, 0, FAKE + 0x100000, 128, None,
                              0, None)
     assert rc == _lib.MROPE_EINVAL                     # q_out overlaps sin
+    rc = lib.apply_rotary_qk(FAKE, 128, 1, None, 0, 0, 4, 128, 128, FAKE + 0x300000,
+                             FAKE + 0x400000, 128, _lib.DTYPE_F32, 5, FAKE + 0x100000, 128, None,
+                             0, None)
+    assert rc == _lib.MROPE_EINVAL                     # unknown precision
 
 
 @fake_ptr_test
@@ -219,13 +226,15 @@ def test_decode_rejects_bad_arguments():
         a = dict(q=FAKE, q_ts=32 * 128, hq=32, k=FAKE + 0x4000000, k_ts=4 * 128, hk=4, batch=8,
                  n=1, D=128, rd=128, cl=FAKE + 0x8000000, rdel=FAKE + 0x8001000, theta=1e6,
                  wq=FAKE + 0xC000000, wk=FAKE + 0xC001000, eps=1e-6, dtype=_lib.DTYPE_BF16,
-                 qo=FAKE + 0x20000000, qo_ts=32 * 128, kc=FAKE + 0x30000000,
+                 prec=_lib.PRECISION_EXACT, qo=FAKE + 0x20000000, qo_ts=32 * 128,
+                 kc=FAKE + 0x30000000,
                  kc_seq=64 * 4 * 128, kc_tok=4 * 128, cap=64)
         a.update(kw)
         return lib.mrope_decode_qk(a["q"], a["q_ts"], a["hq"], a["k"], a["k_ts"], a["hk"],
                                    a["batch"], a["n"], a["D"], a["rd"], a["cl"], a["rdel"],
-                                   a["theta"], a["wq"], a["wk"], a["eps"], a["dtype"], a["qo"],
-                                   a["qo_ts"], a["kc"], a["kc_seq"], a["kc_tok"], a["cap"], None)
+                                   a["theta"], a["wq"], a["wk"], a["eps"], a["dtype"],
+                                   a["prec"], a["qo"], a["qo_ts"], a["kc"], a["kc_seq"],
+                                   a["kc_tok"], a["cap"], None)
 
     assert call(batch=0) == _lib.MROPE_OK                      # nothing to do
     assert call(batch=-1) == _lib.MROPE_EINVAL
@@ -238,3 +247,4 @@ def test_decode_rejects_bad_arguments():
     assert call(wk=0) == _lib.MROPE_EINVAL
     assert call(rd=129) == _lib.MROPE_EINVAL
     assert call(theta=-1.0) == _lib.MROPE_EINVAL
+    assert call(prec=9) == _lib.MROPE_EINVAL

@@ -277,7 +277,8 @@ def test_packed_qkv_views_and_strided_positions(M):
     note("broadcast positions stride 0")
     rc = lib.rmsnorm_mrope_qk(qd.data_ptr(), H * D, H, kd.data_ptr(), H * D, H, T, D, rd,
                               p1d.data_ptr(), 0, 3, sec, 3, _lib.LAYOUT_INTERLEAVED, 1e6, None,
-                              None, 1e-6, _lib.DTYPE_BF16, qo1.data_ptr(), H * D, ko1.data_ptr(),
+                              None, 1e-6, _lib.DTYPE_BF16, _lib.PRECISION_EXACT, qo1.data_ptr(),
+                              H * D, ko1.data_ptr(),
                               H * D, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _lib.check(rc)
     qo3, _ = M.rmsnorm_mrope_qk(qd, kd, to_dev(np.stack([p1, p1, p1]), "i32"), rd, 1e6,

@@ -13,8 +13,8 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, MropeError, check, float_array,  # noqa: F401
-                   int_array, load)
+from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, PRECISIONS, MropeError, check,  # noqa: F401
+                   float_array, int_array, load)
 
 __all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "rms_norm",
            "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "MropeError", "load"]
@@ -36,6 +36,14 @@ def _dtype_code(t) -> int:
 
 def _layout_code(layout) -> int:
     return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def _precision_code(precision) -> int:
+    if isinstance(precision, str):
+        if precision not in PRECISIONS:
+            raise MropeError(_lib.MROPE_EINVAL, f"precision must be one of {list(PRECISIONS)}")
+        return PRECISIONS[precision]
+    return int(precision)
 
 
 def _ptr(t):
@@ -111,8 +119,14 @@ def rms_norm(x, w, eps: float, out=None):
     return out
 
 
-def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, q_out=None, k_out=None):
-    """Split-half rotation of q [T, hq, D] and k [T, hk, D] with cos/sin [T, rotary_dim]."""
+def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, q_out=None, k_out=None,
+                    precision="exact"):
+    """Split-half rotation of q [T, hq, D] and k [T, hk, D] with cos/sin [T, rotary_dim].
+
+    precision: "exact" (one rounding of the binary32 result), "dtype" (cos/sin
+    cast to the tensor dtype, every tensor operation rounded to it) or "fp32"
+    (binary32 tensor operations, one cast at the end).
+    """
     torch = _torch()
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
@@ -121,17 +135,18 @@ def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, q_out=None, k_out=None):
     check(load().apply_rotary_qk(_ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"),
                                  hk, T, D, int(rotary_dim), _ptr(cos), _ptr(sin),
                                  cos.stride(0) if T > 0 else rotary_dim, _dtype_code(q),
-                                 _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out),
+                                 _precision_code(precision), _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out),
                                  _heads_view(k_out, "k_out"), _stream(q)))
     return q_out, k_out
 
 
 def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
-                     wq=None, wk=None, eps: float = 1e-6, q_out=None, k_out=None):
+                     wq=None, wk=None, eps: float = 1e-6, q_out=None, k_out=None,
+                     precision="exact"):
     """Fused per-head RMSNorm (if weights are given) + MRoPE on q and k.
 
     pos: int32 [n_axes, T] on the device (3 axes for interleaved, 2 for
-    vision_2d, len(section) for chunked).
+    vision_2d, len(section) for chunked).  precision as in apply_rotary_qk.
     """
     torch = _torch()
     q_out = torch.empty_like(q) if q_out is None else q_out
@@ -149,17 +164,19 @@ def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
         _ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"), hk, T, D,
         int(rotary_dim), _ptr(pos), pos_stride, n_axes, int_array(sec), len(sec),
         _layout_code(layout), float(theta), _ptr(wq), _ptr(wk), float(eps), _dtype_code(q),
-        _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out), _heads_view(k_out, "k_out"),
+        _precision_code(precision), _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out), _heads_view(k_out, "k_out"),
         _stream(q)))
     return q_out, k_out
 
 
 def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: int, theta: float,
-                    k_cache, wq=None, wk=None, eps: float = 1e-6, q_out=None):
+                    k_cache, wq=None, wk=None, eps: float = 1e-6, q_out=None,
+                    precision="exact"):
     """One decode step: q, k [batch*new_tokens, heads, D]; cache_len and
     rope_delta (or None) int32 [batch] on the device; k_cache [batch,
     capacity, hk, D] receives the rotated k at rows cache_len[b] + i.
-    Returns q_out (k_cache is updated in place)."""
+    precision as in apply_rotary_qk.  Returns q_out (k_cache is updated in
+    place)."""
     torch = _torch()
     q_out = torch.empty_like(q) if q_out is None else q_out
     T, hq, D = q.shape
@@ -176,6 +193,7 @@ def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: in
     check(load().mrope_decode_qk(
         _ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"), hk, batch,
         int(new_tokens), D, int(rotary_dim), _ptr(cache_len), _ptr(rope_delta), float(theta),
-        _ptr(wq), _ptr(wk), float(eps), _dtype_code(q), _ptr(q_out), _heads_view(q_out, "q_out"),
+        _ptr(wq), _ptr(wk), float(eps), _dtype_code(q), _precision_code(precision), _ptr(q_out),
+        _heads_view(q_out, "q_out"),
         _ptr(k_cache), k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _stream(q)))
     return q_out

@@ -26,6 +26,11 @@ LAYOUTS = {"chunked": LAYOUT_CHUNKED, "interleaved": LAYOUT_INTERLEAVED,
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
+PRECISION_EXACT = 0
+PRECISION_DTYPE = 1
+PRECISION_FP32 = 2
+PRECISIONS = {"exact": PRECISION_EXACT, "dtype": PRECISION_DTYPE, "fp32": PRECISION_FP32}
+
 MAX_ROTARY_DIM = 512
 
 _c_int, _c_i64, _c_double, _c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
@@ -43,14 +48,15 @@ SIGNATURES = {
     "rms_norm": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _c_int, _vp, _c_float, _c_int, _vp,
                           _c_i64, _vp]),
     "apply_rotary_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_i64, _c_int,
-                                 _c_int, _vp, _vp, _c_i64, _c_int, _vp, _c_i64, _vp, _c_i64,
-                                 _vp]),
+                                 _c_int, _vp, _vp, _c_i64, _c_int, _c_int, _vp, _c_i64, _vp,
+                                 _c_i64, _vp]),
     "rmsnorm_mrope_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_i64, _c_int,
                                   _c_int, _vp, _c_i64, _c_int, _ip, _c_int, _c_int, _c_double,
-                                  _vp, _vp, _c_float, _c_int, _vp, _c_i64, _vp, _c_i64, _vp]),
+                                  _vp, _vp, _c_float, _c_int, _c_int, _vp, _c_i64, _vp, _c_i64,
+                                  _vp]),
     "mrope_decode_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _vp, _vp, _c_double, _vp, _vp, _c_float, _c_int,
-                                 _vp, _c_i64, _vp, _c_i64, _c_i64, _c_int, _vp]),
+                                 _c_int, _vp, _c_i64, _vp, _c_i64, _c_i64, _c_int, _vp]),
     "mrope_last_error": (ctypes.c_char_p, []),
 }
 

@@ -177,11 +177,16 @@ struct QKArgs {
   const void* w[2];
   int64_t T;
   int D, rd, dtype;
+  int precision;  // MROPE_PRECISION_*; EXACT for RMSNorm only
 };
 
 int check_qk_tensors(const QKArgs& a, bool need_rd) {
   int rc = check_dtype(a.dtype);
   if (rc) return rc;
+  if (a.precision != MROPE_PRECISION_EXACT && a.precision != MROPE_PRECISION_DTYPE &&
+      a.precision != MROPE_PRECISION_FP32)
+    return fail(MROPE_EINVAL, "precision %d is not one of MROPE_PRECISION_EXACT (0), "
+                "_DTYPE (1) or _FP32 (2)", a.precision);
   if (a.T < 0) return fail(MROPE_EINVAL, "T = %lld is negative", (long long)a.T);
   if (a.D <= 0 || a.D % 2 != 0) return fail(MROPE_EINVAL, "D = %d must be positive and even", a.D);
   if (need_rd) {
@@ -312,7 +317,10 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
                     (long long)ts);
     }
   }
-  const int hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, p, tab, nt_cap, stream);
+  // For binary32 tensors the cast of cos/sin to the dtype is the identity.
+  const int prec = (a.dtype == MROPE_DTYPE_F32 && a.precision == MROPE_PRECISION_FP32)
+                       ? MROPE_PRECISION_DTYPE : a.precision;
+  const int hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, prec, p, tab, nt_cap, stream);
   if (hrc != (int)hipSuccess)
     return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
   return ok();
@@ -408,7 +416,7 @@ int rms_norm(const void* x, int64_t x_tok_stride, int64_t T, int heads, int D, c
 int apply_rotary_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
                     int64_t k_tok_stride, int hk, int64_t T, int D, int rotary_dim,
                     const float* cos, const float* sin, int64_t cs_tok_stride, int dtype,
-                    void* q_out, int64_t q_out_tok_stride, void* k_out,
+                    int precision, void* q_out, int64_t q_out_tok_stride, void* k_out,
                     int64_t k_out_tok_stride, void* stream) {
   QKArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -426,6 +434,7 @@ int apply_rotary_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
   a.D = D;
   a.rd = rotary_dim;
   a.dtype = dtype;
+  a.precision = precision;
   int rc = check_qk_tensors(a, true);
   if (rc) return rc;
   if (cs_tok_stride < rotary_dim)
@@ -445,9 +454,9 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
                      int64_t k_tok_stride, int hk, int64_t T, int D, int rotary_dim,
                      const int32_t* pos, int64_t pos_axis_stride, int n_axes,
                      const int* section, int n_sections, int layout, double theta,
-                     const void* wq, const void* wk, float eps, int dtype, void* q_out,
-                     int64_t q_out_tok_stride, void* k_out, int64_t k_out_tok_stride,
-                     void* stream) {
+                     const void* wq, const void* wk, float eps, int dtype, int precision,
+                     void* q_out, int64_t q_out_tok_stride, void* k_out,
+                     int64_t k_out_tok_stride, void* stream) {
   QKArgs a;
   std::memset(&a, 0, sizeof(a));
   a.x[0] = q;
@@ -466,6 +475,7 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
   a.D = D;
   a.rd = rotary_dim;
   a.dtype = dtype;
+  a.precision = precision;
   int rc = check_qk_tensors(a, true);
   if (rc) return rc;
   if ((wq == nullptr) != (wk == nullptr))
@@ -493,7 +503,7 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
                     int64_t k_tok_stride, int hk, int batch, int new_tokens, int D,
                     int rotary_dim, const int32_t* cache_len, const int32_t* rope_delta,
                     double theta, const void* wq, const void* wk, float eps, int dtype,
-                    void* q_out, int64_t q_out_tok_stride, void* k_cache,
+                    int precision, void* q_out, int64_t q_out_tok_stride, void* k_cache,
                     int64_t k_cache_seq_stride, int64_t k_cache_tok_stride, int k_cache_capacity,
                     void* stream) {
   if (batch < 0 || new_tokens < 0)
@@ -517,6 +527,7 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
   a.D = D;
   a.rd = rotary_dim;
   a.dtype = dtype;
+  a.precision = precision;
   int rc = check_qk_tensors(a, true);
   if (rc) return rc;
   if ((wq == nullptr) != (wk == nullptr))

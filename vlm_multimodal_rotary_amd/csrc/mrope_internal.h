@@ -80,7 +80,9 @@ struct CosSinParams {
 // Launchers (mrope_kernels.hip).  Return a hipError_t value as int.
 // nt_cap bounds the tokens per wavefront (its cos/sin LDS slice holds
 // 2 * nt * half doubles, and a tile's byte extent must fit 31 bits).
-int launch_qk(int dtype, int vec, int cs_mode, bool norm, const QKParams& p,
+// prec: MROPE_PRECISION_EXACT or _DTYPE, or _FP32 for bf16 (the host maps
+// binary32 FP32 to DTYPE, the same arithmetic).
+int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKParams& p,
               const ColTable& tab, int nt_cap, void* stream);
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
 

@@ -163,6 +163,42 @@ __device__ __forceinline__ void round_bf16_chunks(float (&a)[V], float (&b)[V]) 
   }
 }
 
+// The rotation as tensor operations on one lane's pairs (x1 = a[i],
+// x2 = b[i]): out1 = x1*c - x2*s, out2 = x2*c + x1*s with every product and
+// sum rounded to binary32 and no product fused into a sum.  CAST rounds
+// cos/sin and both products to bfloat16 as well (bf16 tensor arithmetic
+// with cos/sin cast to the tensor's dtype); the last rounding to the stored
+// dtype happens when the chunk is packed.
+template <bool CAST, int V>
+__device__ __forceinline__ void rotate_tensor_ops(float (&a)[V], float (&b)[V],
+                                                  const double (&ca)[V], const double (&sa)[V],
+                                                  const double (&cb)[V], const double (&sb)[V]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    float c1 = (float)ca[i], s1 = (float)sa[i];
+    float c2 = (float)cb[i], s2 = (float)sb[i];
+    if constexpr (CAST) {
+      c1 = round_bf16(c1);
+      s1 = round_bf16(s1);
+      c2 = round_bf16(c2);
+      s2 = round_bf16(s2);
+    }
+    float p1 = a[i] * c1;
+    float p2 = b[i] * s1;
+    float p3 = b[i] * c2;
+    float p4 = a[i] * s2;
+    if constexpr (CAST) {
+      p1 = round_bf16(p1);
+      p2 = round_bf16(p2);
+      p3 = round_bf16(p3);
+      p4 = round_bf16(p4);
+    }
+    a[i] = p1 - p2;
+    b[i] = p3 + p4;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane sum of a float64 over the lpr lanes of a row.
 // ---------------------------------------------------------------------------
@@ -302,7 +338,7 @@ struct SlotState {
 // Loads UU row-steps (two chunks per lane each), then finishes them in order:
 // RMSNorm, rotation, stores.  Rows past the tile read and write through the
 // out-of-range offset, so the memory operations per call are static.
-template <bool BF16, int V, int CS, bool NORM, int LPR, int UU, typename CsT>
+template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC, int UU, typename CsT>
 __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st, int r0,
                                               const QKParams& p, int grp, int rpw, int lpr,
                                               bool lane_on, bool rot, uint32_t ca, uint32_t cb,
@@ -390,14 +426,18 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
             sb_[i] = (double)p.sin[ob + i];
           }
         }
+        if constexpr (PREC == MROPE_PRECISION_EXACT) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          const double y1 = a[i];
-          const double y2 = b[i];
-          const double o1 = __builtin_fma(y1, ca_[i], -(y2 * sa_[i]));
-          const double o2 = __builtin_fma(y2, cb_[i], y1 * sb_[i]);
-          a[i] = (float)o1;
-          b[i] = (float)o2;
+          for (int i = 0; i < V; ++i) {
+            const double y1 = a[i];
+            const double y2 = b[i];
+            const double o1 = __builtin_fma(y1, ca_[i], -(y2 * sa_[i]));
+            const double o2 = __builtin_fma(y2, cb_[i], y1 * sb_[i]);
+            a[i] = (float)o1;
+            b[i] = (float)o2;
+          }
+        } else {
+          rotate_tensor_ops<BF16 && PREC == MROPE_PRECISION_DTYPE, V>(a, b, ca_, sa_, cb_, sb_);
         }
       }
     }
@@ -414,7 +454,7 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
 // cos/sin (in its LDS slice), then the tile's q rows and k rows, U row-steps
 // per batch of loads.  Wavefronts are short-lived and many; the hardware
 // overlaps them, and the chip's active window of rows stays contiguous.
-template <bool BF16, int V, int CS, bool NORM, int LPR>
+template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 __global__ void __launch_bounds__(kBlockThreads)
 qk_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -557,10 +597,10 @@ qk_kernel(const QKParams p, const ColTable tab) {
       const int full = (hi - lo) / U;
       int r0 = lo * rpw;
       for (int g = 0; g < full; ++g, r0 += U * rpw)
-        process_steps<BF16, V, CS, NORM, LPR, U>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
+        process_steps<BF16, V, CS, NORM, LPR, PREC, U>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
                                                  col_a, wa, wb, lc, ls, t0);
       for (; r0 < hi * rpw; r0 += rpw)
-        process_steps<BF16, V, CS, NORM, LPR, 1>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
+        process_steps<BF16, V, CS, NORM, LPR, PREC, 1>(st, r0, p, grp, rpw, lpr, lane_on, rot, ca, cb,
                                                  col_a, wa, wb, lc, ls, t0);
     }
   }
@@ -583,7 +623,7 @@ __global__ void __launch_bounds__(256) cos_sin_kernel(const CosSinParams p, cons
   sr[j + p.half] = s;
 }
 
-template <bool BF16, int V, int CS, bool NORM, int LPR>
+template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
   p.nt = nt_cap < MROPE_WAVE_TOKENS ? nt_cap : MROPE_WAVE_TOKENS;
@@ -606,62 +646,81 @@ int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const int64_t waves = tiles * parts;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   const int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(double) : 0;
-  hipLaunchKernelGGL((qk_kernel<BF16, V, CS, NORM, LPR>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((qk_kernel<BF16, V, CS, NORM, LPR, PREC>), dim3((unsigned)blocks),
                      dim3(kBlockThreads), lds, st, p, tab);
   return (int)hipGetLastError();
 }
 
-template <bool BF16, int V, int LPR>
-int launch_mode(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, int nt_cap,
-                hipStream_t st) {
+template <bool BF16, int V, int LPR, int PREC>
+int launch_rotating(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, int nt_cap,
+                    hipStream_t st) {
   if (cs_mode == kCsFromPositions)
-    return norm ? launch_t<BF16, V, kCsFromPositions, true, LPR>(p, tab, nt_cap, st)
-                : launch_t<BF16, V, kCsFromPositions, false, LPR>(p, tab, nt_cap, st);
+    return norm ? launch_t<BF16, V, kCsFromPositions, true, LPR, PREC>(p, tab, nt_cap, st)
+                : launch_t<BF16, V, kCsFromPositions, false, LPR, PREC>(p, tab, nt_cap, st);
   if (cs_mode == kCsDecode)
-    return norm ? launch_t<BF16, V, kCsDecode, true, LPR>(p, tab, nt_cap, st)
-                : launch_t<BF16, V, kCsDecode, false, LPR>(p, tab, nt_cap, st);
+    return norm ? launch_t<BF16, V, kCsDecode, true, LPR, PREC>(p, tab, nt_cap, st)
+                : launch_t<BF16, V, kCsDecode, false, LPR, PREC>(p, tab, nt_cap, st);
   if (cs_mode == kCsFromTable && !norm)
-    return launch_t<BF16, V, kCsFromTable, false, LPR>(p, tab, nt_cap, st);
-  if (cs_mode == kCsNone && norm)
-    return launch_t<BF16, V, kCsNone, true, LPR>(p, tab, nt_cap, st);
+    return launch_t<BF16, V, kCsFromTable, false, LPR, PREC>(p, tab, nt_cap, st);
+  return (int)hipErrorInvalidValue;
+}
+
+template <bool BF16, int V, int LPR>
+int launch_mode(int cs_mode, bool norm, int prec, const QKParams& p, const ColTable& tab,
+                int nt_cap, hipStream_t st) {
+  if (cs_mode == kCsNone)
+    return norm ? launch_t<BF16, V, kCsNone, true, LPR, MROPE_PRECISION_EXACT>(p, tab, nt_cap, st)
+                : (int)hipErrorInvalidValue;
+  switch (prec) {
+    case MROPE_PRECISION_EXACT:
+      return launch_rotating<BF16, V, LPR, MROPE_PRECISION_EXACT>(cs_mode, norm, p, tab, nt_cap, st);
+    case MROPE_PRECISION_DTYPE:
+      return launch_rotating<BF16, V, LPR, MROPE_PRECISION_DTYPE>(cs_mode, norm, p, tab, nt_cap, st);
+    case MROPE_PRECISION_FP32:
+      // binary32 tensors arrive as DTYPE (the same arithmetic)
+      if constexpr (BF16)
+        return launch_rotating<BF16, V, LPR, MROPE_PRECISION_FP32>(cs_mode, norm, p, tab, nt_cap,
+                                                                   st);
+      break;
+  }
   return (int)hipErrorInvalidValue;
 }
 
 // 16-byte chunks with a power-of-two lane count per row get a kernel with the
 // lane count fixed at compile time; everything else takes the runtime form.
 template <bool BF16, int V>
-int launch_lpr(int cs_mode, bool norm, const QKParams& p, const ColTable& tab, int nt_cap,
-               hipStream_t st) {
+int launch_lpr(int cs_mode, bool norm, int prec, const QKParams& p, const ColTable& tab,
+               int nt_cap, hipStream_t st) {
   if constexpr (V * (BF16 ? 2 : 4) == 16) {
     switch (p.lpr) {
-      case 2: return launch_mode<BF16, V, 2>(cs_mode, norm, p, tab, nt_cap, st);
-      case 4: return launch_mode<BF16, V, 4>(cs_mode, norm, p, tab, nt_cap, st);
-      case 8: return launch_mode<BF16, V, 8>(cs_mode, norm, p, tab, nt_cap, st);
-      case 16: return launch_mode<BF16, V, 16>(cs_mode, norm, p, tab, nt_cap, st);
-      case 32: return launch_mode<BF16, V, 32>(cs_mode, norm, p, tab, nt_cap, st);
+      case 2: return launch_mode<BF16, V, 2>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 4: return launch_mode<BF16, V, 4>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 8: return launch_mode<BF16, V, 8>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 16: return launch_mode<BF16, V, 16>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 32: return launch_mode<BF16, V, 32>(cs_mode, norm, prec, p, tab, nt_cap, st);
       default: break;
     }
   }
-  return launch_mode<BF16, V, 0>(cs_mode, norm, p, tab, nt_cap, st);
+  return launch_mode<BF16, V, 0>(cs_mode, norm, prec, p, tab, nt_cap, st);
 }
 
 }  // namespace
 
-int launch_qk(int dtype, int vec, int cs_mode, bool norm, const QKParams& p,
+int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKParams& p,
               const ColTable& tab, int nt_cap, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == MROPE_DTYPE_BF16) {
     switch (vec) {
-      case 8: return launch_lpr<true, 8>(cs_mode, norm, p, tab, nt_cap, st);
-      case 4: return launch_lpr<true, 4>(cs_mode, norm, p, tab, nt_cap, st);
-      case 2: return launch_lpr<true, 2>(cs_mode, norm, p, tab, nt_cap, st);
-      case 1: return launch_lpr<true, 1>(cs_mode, norm, p, tab, nt_cap, st);
+      case 8: return launch_lpr<true, 8>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 4: return launch_lpr<true, 4>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 2: return launch_lpr<true, 2>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 1: return launch_lpr<true, 1>(cs_mode, norm, prec, p, tab, nt_cap, st);
     }
   } else {
     switch (vec) {
-      case 4: return launch_lpr<false, 4>(cs_mode, norm, p, tab, nt_cap, st);
-      case 2: return launch_lpr<false, 2>(cs_mode, norm, p, tab, nt_cap, st);
-      case 1: return launch_lpr<false, 1>(cs_mode, norm, p, tab, nt_cap, st);
+      case 4: return launch_lpr<false, 4>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 2: return launch_lpr<false, 2>(cs_mode, norm, prec, p, tab, nt_cap, st);
+      case 1: return launch_lpr<false, 1>(cs_mode, norm, prec, p, tab, nt_cap, st);
     }
   }
   return (int)hipErrorInvalidValue;
