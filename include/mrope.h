@@ -41,6 +41,7 @@
 #ifndef MROPE_H_
 #define MROPE_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -236,6 +237,76 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq,
                     void* q_out, int64_t q_out_tok_stride,
                     void* k_cache, int64_t k_cache_seq_stride, int64_t k_cache_tok_stride,
                     int k_cache_capacity, void* stream);
+
+/* Status bits written by the position builders into their device `status`
+ * word (0 = the inputs describe a sequence the walkthrough can build). */
+#define MROPE_POS_BAD_TYPE      1   /* a valid token's type is not 0, 1 or 2 (taken as text) */
+#define MROPE_POS_NO_GRID       2   /* a visual segment has no (usable) grid left: text positions */
+#define MROPE_POS_LENGTH        4   /* a visual segment's token count differs from its grid */
+#define MROPE_POS_NOT_DIVISIBLE 8   /* a vision grid's h or w is not a multiple of the merge size */
+#define MROPE_POS_COUNT        16   /* the grids' patch total differs from n_tokens */
+
+/*
+ * mrope_rope_index_workspace_size — bytes of device workspace
+ * mrope_rope_index needs for these sizes (0 on invalid sizes).
+ */
+size_t mrope_rope_index_workspace_size(int batch, int64_t seq_len, int n_images, int n_videos);
+
+/*
+ * mrope_rope_index — the 3-axis position table and rope_deltas of a batch of
+ * mixed text / image / video token sequences ([RoPE] get_rope_index
+ * walkthrough and its single-batch L = 10 table):
+ *  - padding (attention_mask 0) is removed first; it keeps position 0;
+ *  - the remaining tokens of a sample are split into runs of equal type
+ *    (0 text, 1 image, 2 video);
+ *  - a text run of n tokens takes p, p+1, ..., p+n-1 on all three axes and
+ *    advances p by n;
+ *  - an image run takes the next image grid (t, h, w) of the batch (one
+ *    iterator shared by all samples, in sample order); a video run takes the
+ *    next single-slice grid (1, h, w), each video of t slices giving t of
+ *    them; its slots (t, h/merge, w/merge), flattened width fastest, get
+ *    (p + ti, p + row, p + col); p then advances by max(h, w) / merge;
+ *  - rope_delta[b] = max position + 1 - valid token count (0 when none).
+ *   mm_token_type:   device int32 [batch][seq_len] (contiguous).
+ *   attention_mask:  device int32 [batch][seq_len], nonzero = valid; NULL =
+ *                    all valid.
+ *   image_grid_thw:  device int32 [n_images][3]; video_grid_thw likewise
+ *                    (NULL when the count is 0).
+ *   pos:             device int32 [3][batch*seq_len], axis stride
+ *                    pos_axis_stride (>= batch*seq_len): the layout the
+ *                    rotating entry points read (token b*seq_len + l).
+ *   rope_delta:      device int32 [batch].
+ *   status:          device int32, set to the OR of MROPE_POS_* conditions.
+ *   workspace:       device scratch of mrope_rope_index_workspace_size bytes,
+ *                    owned by the caller; its contents on entry do not matter.
+ * Three kernels on `stream`; the host does not wait.  Positions are computed
+ * in 64-bit integers and stored as int32.  EINVAL on negative sizes, a merge
+ * size outside [1, 1024], null pointers, a short or misaligned (8-byte)
+ * workspace, or overlapping outputs.
+ */
+int mrope_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask, int batch,
+                     int64_t seq_len, const int32_t* image_grid_thw, int n_images,
+                     const int32_t* video_grid_thw, int n_videos, int spatial_merge,
+                     int32_t* pos, int64_t pos_axis_stride, int32_t* rope_delta,
+                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mrope_vision_pos_ids — the (row, col) position of every vision patch
+ * ([QVL] rot_pos_emb): images in order; within an image, patches in
+ * merge x merge block order (block row, block col, row in block, col in
+ * block), row = block_row*merge + row_in_block, col likewise; the t frames of
+ * an image repeat its coordinates.
+ *   grid_thw: device int32 [n_images][3] (t, h, w), n_images <= 4096.
+ *   pos:      device int32 [2][n_tokens], axis stride pos_axis_stride: the
+ *             layout of the vision-2D rotating entry points.
+ *   status:   device int32: MROPE_POS_NOT_DIVISIBLE, MROPE_POS_COUNT (patches
+ *             past the grids' total are written as (0, 0)).
+ * EINVAL on bad sizes, a merge size outside [1, 1024], null pointers or
+ * overlapping buffers.
+ */
+int mrope_vision_pos_ids(const int32_t* grid_thw, int n_images, int spatial_merge,
+                         int64_t n_tokens, int32_t* pos, int64_t pos_axis_stride,
+                         int32_t* status, void* stream);
 
 /*
  * mrope_last_error — message for the last non-zero return on this thread

@@ -19,7 +19,8 @@ HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "mrope.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -248,3 +249,52 @@ def test_decode_rejects_bad_arguments():
     assert call(rd=129) == _lib.MROPE_EINVAL
     assert call(theta=-1.0) == _lib.MROPE_EINVAL
     assert call(prec=9) == _lib.MROPE_EINVAL
+
+
+def test_rope_index_workspace_size():
+    lib = _lib.load()
+    a = lib.mrope_rope_index_workspace_size(1, 32768, 0, 0)
+    b = lib.mrope_rope_index_workspace_size(4, 32768, 10, 3)
+    assert 0 < a < b
+    assert lib.mrope_rope_index_workspace_size(-1, 10, 0, 0) == 0
+    assert lib.mrope_rope_index_workspace_size(1, 0, 0, 0) > 0     # grid tables only
+
+
+@fake_ptr_test
+def test_position_builders_reject_bad_arguments():
+    lib = _lib.load()
+    ws_bytes = lib.mrope_rope_index_workspace_size(2, 100, 1, 1)
+
+    def call(**kw):
+        a = dict(types=FAKE, mask=0, B=2, L=100, img=FAKE + 0x1000, ni=1, vid=FAKE + 0x2000, nv=1,
+                 merge=2, pos=FAKE + 0x10000, ps=200, delta=FAKE + 0x20000, status=FAKE + 0x20100,
+                 ws=FAKE + 0x100000, wsb=ws_bytes)
+        a.update(kw)
+        return lib.mrope_rope_index(a["types"], a["mask"], a["B"], a["L"], a["img"], a["ni"],
+                                    a["vid"], a["nv"], a["merge"], a["pos"], a["ps"], a["delta"],
+                                    a["status"], a["ws"], a["wsb"], None)
+
+    assert call(B=-1) == _lib.MROPE_EINVAL
+    assert call(merge=0) == _lib.MROPE_EINVAL
+    assert call(types=0) == _lib.MROPE_EINVAL
+    assert call(status=0) == _lib.MROPE_EINVAL
+    assert call(img=0) == _lib.MROPE_EINVAL
+    assert call(ps=199) == _lib.MROPE_EINVAL                  # axis stride < B*L
+    assert call(wsb=ws_bytes - 1) == _lib.MROPE_EINVAL        # short workspace
+    assert call(ws=FAKE + 0x100004) == _lib.MROPE_EINVAL      # misaligned workspace
+    assert call(pos=FAKE + 0x800) == _lib.MROPE_EINVAL        # pos overlaps the types
+    assert call(delta=FAKE + 0x10000 + 4 * 150) == _lib.MROPE_EINVAL   # delta inside pos
+    assert call(ws=FAKE + 0x10000) == _lib.MROPE_EINVAL       # workspace overlaps pos
+
+    def vcall(**kw):
+        a = dict(grid=FAKE, n=2, merge=2, N=64, pos=FAKE + 0x1000, ps=64, status=FAKE + 0x2000)
+        a.update(kw)
+        return lib.mrope_vision_pos_ids(a["grid"], a["n"], a["merge"], a["N"], a["pos"], a["ps"],
+                                        a["status"], None)
+
+    assert vcall(n=-1) == _lib.MROPE_EINVAL
+    assert vcall(n=_lib.MAX_VISION_IMAGES + 1) == _lib.MROPE_EINVAL
+    assert vcall(merge=0) == _lib.MROPE_EINVAL
+    assert vcall(ps=63) == _lib.MROPE_EINVAL
+    assert vcall(status=0) == _lib.MROPE_EINVAL
+    assert vcall(pos=FAKE + 8) == _lib.MROPE_EINVAL           # pos overlaps the grids

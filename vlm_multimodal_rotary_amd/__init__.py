@@ -17,7 +17,8 @@ from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, PRECISIONS, MropeError, check
                    float_array, int_array, load)
 
 __all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "rms_norm",
-           "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "MropeError", "load"]
+           "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "rope_index",
+           "vision_pos_ids", "MropeError", "load"]
 
 
 def _torch():
@@ -197,3 +198,66 @@ def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: in
         _heads_view(q_out, "q_out"),
         _ptr(k_cache), k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _stream(q)))
     return q_out
+
+
+def _int32_device(t, name, shape_len):
+    torch = _torch()
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != shape_len:
+        raise MropeError(_lib.MROPE_EINVAL, f"{name} must be a contiguous int32 tensor "
+                                            f"with {shape_len} dims")
+    return t
+
+
+def _raise_on_status(status):
+    s = int(status.item())
+    if s:
+        bits = [msg for bit, msg in _lib.POS_FLAGS.items() if s & bit]
+        raise MropeError(_lib.MROPE_EINVAL, "position builder: " + "; ".join(bits))
+
+
+def rope_index(mm_token_type, image_grid_thw=None, video_grid_thw=None, attention_mask=None,
+               merge: int = 2, check: bool = True):
+    """3-axis positions and rope_deltas of a batch (get_rope_index) on the GPU.
+
+    mm_token_type, attention_mask: int32 [B, L] on the device (0 text, 1
+    image, 2 video; mask nonzero = valid).  Grids: int32 [n, 3] (t, h, w)
+    before merging.  Returns (pos int32 [3, B*L], rope_delta int32 [B],
+    status int32 [1]); with check=True the call waits for the status word and
+    raises on a nonzero one.
+    """
+    torch = _torch()
+    _int32_device(mm_token_type, "mm_token_type", 2)
+    B, L = mm_token_type.shape
+    dev = mm_token_type.device
+    if attention_mask is not None:
+        _int32_device(attention_mask, "attention_mask", 2)
+    ni = 0 if image_grid_thw is None else _int32_device(image_grid_thw, "image_grid_thw", 2).shape[0]
+    nv = 0 if video_grid_thw is None else _int32_device(video_grid_thw, "video_grid_thw", 2).shape[0]
+    lib = load()
+    ws_bytes = lib.mrope_rope_index_workspace_size(B, L, ni, nv)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    pos = torch.empty((3, B * L), dtype=torch.int32, device=dev)
+    delta = torch.empty(B, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    check_rc = lib.mrope_rope_index(_ptr(mm_token_type), _ptr(attention_mask), B, L,
+                                    _ptr(image_grid_thw), ni, _ptr(video_grid_thw), nv, int(merge),
+                                    _ptr(pos), B * L, _ptr(delta), _ptr(status), _ptr(workspace),
+                                    ws_bytes, _stream(mm_token_type))
+    _lib.check(check_rc)
+    if check:
+        _raise_on_status(status)
+    return pos, delta, status
+
+
+def vision_pos_ids(grid_thw, n_tokens: int, merge: int = 2, check: bool = True):
+    """(row, col) of every vision patch (rot_pos_emb order): int32 [2, n_tokens]."""
+    torch = _torch()
+    _int32_device(grid_thw, "grid_thw", 2)
+    pos = torch.empty((2, n_tokens), dtype=torch.int32, device=grid_thw.device)
+    status = torch.empty(1, dtype=torch.int32, device=grid_thw.device)
+    _lib.check(load().mrope_vision_pos_ids(_ptr(grid_thw), grid_thw.shape[0], int(merge),
+                                           int(n_tokens), _ptr(pos), max(int(n_tokens), 1),
+                                           _ptr(status), _stream(grid_thw)))
+    if check:
+        _raise_on_status(status)
+    return pos, status

@@ -33,6 +33,17 @@ PRECISIONS = {"exact": PRECISION_EXACT, "dtype": PRECISION_DTYPE, "fp32": PRECIS
 
 MAX_ROTARY_DIM = 512
 
+POS_BAD_TYPE = 1
+POS_NO_GRID = 2
+POS_LENGTH = 4
+POS_NOT_DIVISIBLE = 8
+POS_COUNT = 16
+POS_FLAGS = {POS_BAD_TYPE: "token type not 0/1/2", POS_NO_GRID: "visual run without a grid",
+             POS_LENGTH: "visual run length differs from its grid",
+             POS_NOT_DIVISIBLE: "grid not divisible by the merge size",
+             POS_COUNT: "patch total differs from n_tokens"}
+MAX_VISION_IMAGES = 4096
+
 _c_int, _c_i64, _c_double, _c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
 _vp = ctypes.c_void_p
 _ip = ctypes.POINTER(ctypes.c_int)
@@ -57,6 +68,10 @@ SIGNATURES = {
     "mrope_decode_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _vp, _vp, _c_double, _vp, _vp, _c_float, _c_int,
                                  _c_int, _vp, _c_i64, _vp, _c_i64, _c_i64, _c_int, _vp]),
+    "mrope_rope_index_workspace_size": (ctypes.c_size_t, [_c_int, _c_i64, _c_int, _c_int]),
+    "mrope_rope_index": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
+                                  _vp, _c_i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "mrope_vision_pos_ids": (_c_int, [_vp, _c_int, _c_int, _c_i64, _vp, _c_i64, _vp, _vp]),
     "mrope_last_error": (ctypes.c_char_p, []),
 }
 

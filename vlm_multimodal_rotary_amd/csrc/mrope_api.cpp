@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -326,9 +327,158 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   return ok();
 }
 
+// Byte offsets of the regions of the position builder's workspace.
+struct RopeWs {
+  size_t sum = 0, carry = 0, valid = 0, adv_i = 0, adv_v = 0, cum_t = 0, total = 0;
+  int64_t chunks_per_sample = 0;
+};
+
+bool rope_ws_layout(int B, int64_t L, int n_img, int n_vid, RopeWs& w) {
+  if (B < 0 || L < 0 || n_img < 0 || n_vid < 0) return false;
+  w.chunks_per_sample = (L + mrope::kPosChunk - 1) / mrope::kPosChunk;
+  const int64_t chunks = (int64_t)B * w.chunks_per_sample;
+  if (w.chunks_per_sample > INT32_MAX || chunks > INT32_MAX) return false;
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  size_t off = 0;
+  w.sum = off;
+  off = al(off + (size_t)chunks * mrope::kPosSumInts * 4);
+  w.carry = off;
+  off = al(off + (size_t)chunks * mrope::kPosCarryInts * 4);
+  w.valid = off;
+  off = al(off + (size_t)B * 4);
+  w.adv_i = off;
+  off = al(off + ((size_t)n_img + 1) * 8);
+  w.adv_v = off;
+  off = al(off + ((size_t)n_vid + 1) * 8);
+  w.cum_t = off;
+  off = al(off + ((size_t)n_vid + 1) * 4);
+  w.total = off;
+  return true;
+}
+
+Extent bytes_at(const void* base, int64_t n, int elem_bytes) {
+  return extent_of(base, 1, 0, n, elem_bytes);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mrope_rope_index_workspace_size(int batch, int64_t seq_len, int n_images, int n_videos) {
+  RopeWs w;
+  if (!rope_ws_layout(batch, seq_len, n_images, n_videos, w)) return 0;
+  return w.total;
+}
+
+int mrope_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask, int batch,
+                     int64_t seq_len, const int32_t* image_grid_thw, int n_images,
+                     const int32_t* video_grid_thw, int n_videos, int spatial_merge,
+                     int32_t* pos, int64_t pos_axis_stride, int32_t* rope_delta,
+                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || seq_len < 0 || n_images < 0 || n_videos < 0)
+    return fail(MROPE_EINVAL, "batch, seq_len, n_images and n_videos must be >= 0");
+  if (spatial_merge < 1 || spatial_merge > 1024)
+    return fail(MROPE_EINVAL, "spatial_merge = %d must be in [1, 1024]", spatial_merge);
+  RopeWs w;
+  if (!rope_ws_layout(batch, seq_len, n_images, n_videos, w))
+    return fail(MROPE_EUNSUPPORTED, "batch * seq_len is too large");
+  const int64_t T = (int64_t)batch * seq_len;
+  if (T > 0 && (mm_token_type == nullptr || pos == nullptr))
+    return fail(MROPE_EINVAL, "mm_token_type and pos must be non-NULL");
+  if (batch > 0 && rope_delta == nullptr) return fail(MROPE_EINVAL, "rope_delta is NULL");
+  if (status == nullptr) return fail(MROPE_EINVAL, "status is NULL");
+  if (n_images > 0 && image_grid_thw == nullptr) return fail(MROPE_EINVAL, "image_grid_thw is NULL");
+  if (n_videos > 0 && video_grid_thw == nullptr) return fail(MROPE_EINVAL, "video_grid_thw is NULL");
+  if (T > 0 && pos_axis_stride < T)
+    return fail(MROPE_EINVAL, "pos_axis_stride %lld < batch*seq_len %lld",
+                (long long)pos_axis_stride, (long long)T);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(MROPE_EINVAL, "workspace of %zu bytes needed (got %zu)", w.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+    return fail(MROPE_EINVAL, "workspace must be 8-byte aligned");
+  for (const void* ptr : {(const void*)mm_token_type, (const void*)attention_mask,
+                          (const void*)image_grid_thw, (const void*)video_grid_thw,
+                          (const void*)pos, (const void*)rope_delta, (const void*)status})
+    if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0)
+      return fail(MROPE_EINVAL, "int32 buffers must be 4-byte aligned");
+  const Extent outs[4] = {extent_of(pos, 3, pos_axis_stride, T, 4), bytes_at(rope_delta, batch, 4),
+                          bytes_at(status, 1, 4), bytes_at(workspace, (int64_t)w.total, 1)};
+  const Extent ins[4] = {bytes_at(mm_token_type, T, 4), bytes_at(attention_mask, T, 4),
+                         bytes_at(image_grid_thw, 3 * (int64_t)n_images, 4),
+                         bytes_at(video_grid_thw, 3 * (int64_t)n_videos, 4)};
+  for (int i = 0; i < 4; ++i) {
+    for (int k = 0; k < 4; ++k)
+      if (overlaps(outs[i], ins[k])) return fail(MROPE_EINVAL, "an output overlaps an input");
+    for (int k = i + 1; k < 4; ++k)
+      if (overlaps(outs[i], outs[k]))
+        return fail(MROPE_EINVAL, "pos, rope_delta, status and workspace must not overlap");
+  }
+  mrope::RopeIndexParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.types = mm_token_type;
+  p.mask = attention_mask;
+  p.B = batch;
+  p.L = seq_len;
+  p.C = (int)w.chunks_per_sample;
+  p.image_grid = image_grid_thw;
+  p.n_images = n_images;
+  p.video_grid = video_grid_thw;
+  p.n_videos = n_videos;
+  p.merge = spatial_merge;
+  p.pos = pos;
+  p.pos_stride = pos_axis_stride;
+  p.rope_delta = rope_delta;
+  p.status = status;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_sum = reinterpret_cast<int32_t*>(ws + w.sum);
+  p.ws_carry = reinterpret_cast<int32_t*>(ws + w.carry);
+  p.ws_valid = reinterpret_cast<int32_t*>(ws + w.valid);
+  p.ws_adv_i = reinterpret_cast<int64_t*>(ws + w.adv_i);
+  p.ws_adv_v = reinterpret_cast<int64_t*>(ws + w.adv_v);
+  p.ws_cum_t = reinterpret_cast<int32_t*>(ws + w.cum_t);
+  const int hrc = mrope::launch_rope_index(p, stream);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
+}
+
+int mrope_vision_pos_ids(const int32_t* grid_thw, int n_images, int spatial_merge,
+                         int64_t n_tokens, int32_t* pos, int64_t pos_axis_stride,
+                         int32_t* status, void* stream) {
+  if (n_images < 0 || n_images > mrope::kMaxVisionImages)
+    return fail(MROPE_EINVAL, "n_images = %d must be in [0, %d]", n_images,
+                mrope::kMaxVisionImages);
+  if (spatial_merge < 1 || spatial_merge > 1024)
+    return fail(MROPE_EINVAL, "spatial_merge = %d must be in [1, 1024]", spatial_merge);
+  if (n_tokens < 0) return fail(MROPE_EINVAL, "n_tokens is negative");
+  if (n_images > 0 && grid_thw == nullptr) return fail(MROPE_EINVAL, "grid_thw is NULL");
+  if (n_tokens > 0 && pos == nullptr) return fail(MROPE_EINVAL, "pos is NULL");
+  if (status == nullptr) return fail(MROPE_EINVAL, "status is NULL");
+  if (n_tokens > 0 && pos_axis_stride < n_tokens)
+    return fail(MROPE_EINVAL, "pos_axis_stride < n_tokens");
+  for (const void* ptr : {(const void*)grid_thw, (const void*)pos, (const void*)status})
+    if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0)
+      return fail(MROPE_EINVAL, "int32 buffers must be 4-byte aligned");
+  const Extent pe = extent_of(pos, 2, pos_axis_stride, n_tokens, 4);
+  const Extent ge = bytes_at(grid_thw, 3 * (int64_t)n_images, 4);
+  const Extent se = bytes_at(status, 1, 4);
+  if (overlaps(pe, ge) || overlaps(pe, se) || overlaps(se, ge))
+    return fail(MROPE_EINVAL, "pos, status and grid_thw must not overlap");
+  mrope::VisionPosParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.grid = grid_thw;
+  p.n_images = n_images;
+  p.merge = spatial_merge;
+  p.N = n_tokens;
+  p.pos = pos;
+  p.pos_stride = pos_axis_stride;
+  p.status = status;
+  const int hrc = mrope::launch_vision_pos_ids(p, stream);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
+}
 
 int mrope_inv_freq(int dim, double theta, float* out) {
   if (out == nullptr) return fail(MROPE_EINVAL, "out is NULL");

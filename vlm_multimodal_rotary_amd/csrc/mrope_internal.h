@@ -77,6 +77,52 @@ struct CosSinParams {
   int64_t cs_ts;
 };
 
+// Position builders (mrope_positions.hip).
+constexpr int kPosThreads = 256;
+constexpr int kPosPerThread = 16;
+constexpr int kPosChunk = kPosThreads * kPosPerThread;   // tokens per block
+constexpr int kPosSumInts = 9;      // chunk summary: nv, nt, ni, nvd, ft, lt, lsF, lsT, flags
+constexpr int kPosCarryInts = 9;    // chunk carry: F, A, prevT, img, vid, img0, vid0, S, segT
+constexpr int kPosCarryTile = 512;  // summaries per LDS tile of the carry pass
+constexpr int kMaxVisionImages = 4096;   // patch-count prefix in LDS: 32 KB
+
+struct RopeIndexParams {
+  const int32_t* types;       // [B][L]
+  const int32_t* mask;        // [B][L] or null
+  int B;
+  int64_t L;
+  int C;                      // chunks per sample
+  const int32_t* image_grid;  // [n_images][3]
+  int n_images;
+  const int32_t* video_grid;  // [n_videos][3]
+  int n_videos;
+  int merge;
+  int32_t* pos;               // [3][B*L], axis stride pos_stride
+  int64_t pos_stride;
+  int32_t* rope_delta;        // [B]
+  int32_t* status;
+  // workspace regions
+  int32_t* ws_sum;            // [B*C][kPosSumInts]
+  int32_t* ws_carry;          // [B*C][kPosCarryInts]
+  int32_t* ws_valid;          // [B]
+  int64_t* ws_adv_i;          // [n_images + 1]
+  int64_t* ws_adv_v;          // [n_videos + 1]
+  int32_t* ws_cum_t;          // [n_videos + 1]
+};
+
+struct VisionPosParams {
+  const int32_t* grid;        // [n_images][3]
+  int n_images;
+  int merge;
+  int64_t N;                  // patches the output holds
+  int32_t* pos;               // [2][N], axis stride pos_stride
+  int64_t pos_stride;
+  int32_t* status;
+};
+
+int launch_rope_index(const RopeIndexParams& p, void* stream);
+int launch_vision_pos_ids(const VisionPosParams& p, void* stream);
+
 // Launchers (mrope_kernels.hip).  Return a hipError_t value as int.
 // nt_cap bounds the tokens per wavefront (its cos/sin LDS slice holds
 // 2 * nt * half doubles, and a tile's byte extent must fit 31 bits).

@@ -318,3 +318,58 @@ def make_decode_inputs(wl: DecodeWorkload | str, batch: int | None = None,
                 wk=None if wk is None else _store(wk, wl.dtype),
                 cache_len=cache_len, rope_delta=rope_delta, k_cache=_store(cache, wl.dtype),
                 workload=wl, batch=B, new_tokens=n, capacity=cap)
+
+
+def random_mm_batch(rng, B: int, L: int, pad: bool = True, merge: int = 2):
+    """Random mixed-modality batch for the position builders: token types
+    [B, L] (0 text, 1 image, 2 video), attention mask [B, L], and the image /
+    video grids (t, h, w) the batch consumes in order.  Each sample is a
+    sequence of whole units -- a text run; an image followed by a text token;
+    a video whose single-slice runs are separated by timestamp text -- padded
+    on the left or with a hole near the start.  Grids are small (h, w even,
+    at most 6) so that many runs fit."""
+    types = np.zeros((B, L), dtype=np.int64)
+    mask = np.zeros((B, L), dtype=np.int64)
+    images, videos = [], []
+    for b in range(B):
+        budget = L - (int(rng.integers(0, L // 4 + 1)) if pad else 0)
+        flat = []
+        for _ in range(max(200, L // 2)):
+            if len(flat) >= budget:
+                break
+            r = rng.random()
+            if r < 0.45:
+                unit, img, vid = [0] * int(rng.integers(1, 12)), None, None
+            elif r < 0.75:
+                t, h, w = 1, 2 * int(rng.integers(1, 4)), 2 * int(rng.integers(1, 4))
+                unit = [1] * ((h // merge) * (w // merge)) + [0]
+                img, vid = (t, h, w), None
+            else:
+                t, h, w = int(rng.integers(1, 4)), 2 * int(rng.integers(1, 3)), 2 * int(rng.integers(1, 3))
+                unit = []
+                for _ in range(t):
+                    unit += [0] * int(rng.integers(1, 3)) + [2] * ((h // merge) * (w // merge))
+                unit += [0]
+                img, vid = None, (t, h, w)
+            if len(flat) + len(unit) > budget:
+                continue
+            flat += unit
+            if img:
+                images.append(img)
+            if vid:
+                videos.append(vid)
+        valid = len(flat)
+        hole = L - valid
+        if rng.random() < 0.5 or hole == 0:
+            types[b, hole:] = flat
+            mask[b, hole:] = 1
+        else:
+            # a hole inside the first text stretch (or at the start)
+            cut = 0
+            while cut < valid and flat[cut] == 0 and cut < 3:
+                cut += 1
+            types[b, :cut] = flat[:cut]
+            mask[b, :cut] = 1
+            types[b, cut + hole:] = flat[cut:]
+            mask[b, cut + hole:] = 1
+    return types, mask, images, videos
