@@ -84,6 +84,116 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0, precision: str = "exact"):
                       f"all {wl.hq}+{wl.hk} heads) of {wl.name}, {elapsed:.1f} s, one thread"}
 
 
+def time_steps(step, args, stream=None):
+    """Warm up (at least W steps and --min-warmup-s), optionally capture
+    --graph steps in one HIP graph, then time K steps with HIP events on the
+    launching stream.  Returns (ms per step, steps timed, warmup steps, wall
+    ms per step)."""
+    import torch
+    t_warm = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_warm < args.min_warmup_s:
+        for _ in range(50):
+            step()
+        done += 50
+        torch.cuda.synchronize()
+    runner = step
+    per_run = 1
+    if args.graph > 0:
+        # Capture G steps once; each replay launches them back to back without
+        # host overhead.  The captured launches are plain kernel launches.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.graph):
+                step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        runner = graph.replay
+        per_run = args.graph
+    runs = max(1, args.steps // per_run)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(runs):
+        runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    n = runs * per_run
+    return ev0.elapsed_time(ev1) / n, n, done, wall * 1e3 / n
+
+
+def bench_positions(args):
+    """One step = one mrope_rope_index call (three kernels) over the batch."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import vlm_multimodal_rotary_amd as M
+    from vlm_multimodal_rotary_amd import _lib
+    import ctypes
+
+    wl = W.POSITION_WORKLOADS[args.workload]
+    types, mask, images, videos = W.mm_prompt_batch(wl)
+    td, md = torch.from_numpy(types).cuda(), torch.from_numpy(mask).cuda()
+    gi, gv = torch.from_numpy(images).cuda(), torch.from_numpy(videos).cuda()
+    B, L = types.shape
+    lib = M.load()
+    ws_bytes = lib.mrope_rope_index_workspace_size(B, L, gi.shape[0], gv.shape[0])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    pos = torch.empty((3, B * L), dtype=torch.int32, device="cuda")
+    delta = torch.empty(B, dtype=torch.int32, device="cuda")
+    status = torch.empty(1, dtype=torch.int32, device="cuda")
+    P = ctypes.c_void_p
+
+    def step():
+        _lib.check(lib.mrope_rope_index(
+            P(td.data_ptr()), P(md.data_ptr()), B, L, P(gi.data_ptr()), gi.shape[0],
+            P(gv.data_ptr()), gv.shape[0], 2, P(pos.data_ptr()), B * L, P(delta.data_ptr()),
+            P(status.data_ptr()), P(ws.data_ptr()), ws_bytes,
+            P(torch.cuda.current_stream().cuda_stream)))
+
+    ms, n, warm, wall_ms = time_steps(step, args)
+    assert int(status.item()) == 0
+    alg = wl.algorithmic_bytes()
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "position-table tokens/s (mrope_rope_index)",
+        "value": wl.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "warmup": warm, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "graph_steps": args.graph, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic (seeded chat-style multimodal prompts)",
+        "config": {"workload": wl.name, "batch": B, "seq_len": L, "images": int(gi.shape[0]),
+                   "videos": int(gv.shape[0]), "merge": 2},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes": alg,
+                     "kernel": "rope_index_summarize + rope_index_carry + rope_index_apply "
+                               "(one step)"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import positions_oracle as PO
+        start = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - start < 10.0:
+            PO.get_rope_index(types, images, videos, mask)
+            reps += 1
+        el = time.perf_counter() - start
+        line["cpu_baseline"] = {"value": reps * wl.T / el, "unit": "tokens/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{reps} full batches of {wl.T} slots, {el:.1f} s, "
+                                          "one thread"}
+    print(json.dumps(line), flush=True)
+
+
 def copy_calib(nbytes: int, steps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -124,6 +234,9 @@ def main():
     import workloads as W
     import vlm_multimodal_rotary_amd as M
 
+    if args.workload in W.POSITION_WORKLOADS:
+        bench_positions(args)
+        return
     decode = args.workload in W.DECODE_WORKLOADS
     wl = W.DECODE_WORKLOADS[args.workload] if decode else W.WORKLOADS[args.workload]
     inp = W.make_decode_inputs(wl) if decode else W.make_inputs(wl)
@@ -155,45 +268,7 @@ def main():
                                wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out,
                                precision=args.precision)
 
-    t_warm = time.perf_counter()
-    done = 0
-    while done < args.warmup or time.perf_counter() - t_warm < args.min_warmup_s:
-        for _ in range(50):
-            step()
-        done += 50
-        torch.cuda.synchronize()
-    runner = step
-    per_run = 1
-    if args.graph > 0:
-        # Capture G steps once; each replay launches them back to back without
-        # host overhead.  The captured launches are plain kernel launches.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.graph):
-                step()
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-        runner = graph.replay
-        per_run = args.graph
-    runs = max(1, args.steps // per_run)
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(runs):
-        runner()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / (runs * per_run)    # one kernel launch per step
+    ms, n_timed, done, wall_ms = time_steps(step, args)   # one kernel launch per step
 
     alg_bytes = wl.algorithmic_bytes()
     achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
@@ -214,10 +289,10 @@ def main():
         "value": wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": runs * per_run,
+        "steps": n_timed,
         "warmup": done,
         "ms_per_step": ms,
-        "wall_ms_per_step": wall * 1e3 / (runs * per_run),
+        "wall_ms_per_step": wall_ms,
         "graph_steps": args.graph,
         "higher_is_better": True,
         "scaling": "weak",

@@ -122,7 +122,84 @@ class Tables:
         return int(self.adv_v[v] + (k - self.cum_t[v]) * (max(h, w) // self.merge))
 
 
-def model(types, mask, images, videos, merge, PT, PER):
+def carry_parallel(summaries, B, C, threads):
+    """The carry pass as the kernel runs it: contiguous chunk ranges per
+    thread, block scans between rounds, per-sample values as batch-wide
+    prefixes minus the sample's first chunk.  Returns the carries and the
+    per-sample (valid, end record)."""
+    n = B * C
+    per = -(-n // threads) if n else 0
+    rng = [(min(n, t * per), min(n, t * per + per)) for t in range(threads)]
+    S = [list(x) for x in summaries]
+    # round 1
+    t_nv = [sum(S[c][0] for c in range(a, b)) for a, b in rng]
+    t_nt = [sum(S[c][1] for c in range(a, b)) for a, b in rng]
+    t_lt = []
+    for a, b in rng:
+        v = -1
+        for c in range(a, b):
+            if S[c][5] >= 0:
+                v = c << 2 | S[c][5]
+        t_lt.append(v)
+    gF_ex, _ = _excl_sum(t_nv)
+    gA_ex, _ = _excl_sum(t_nt)
+    lt_ex, _ = _excl_max(t_lt, -1)
+    # round 2
+    t_ni, t_nvd, t_st = [], [], []
+    for t, (a, b) in enumerate(rng):
+        gF, gA, lt = gF_ex[t], gA_ex[t], lt_ex[t]
+        ni_s = nvd_s = 0
+        st = -1
+        for c in range(a, b):
+            first = (c // C) * C
+            nv, nt, ni, nvd, ft, lts, lsF, lsT, _ = S[c]
+            prevT = (lt & 3) if lt >= 0 and (lt >> 2) >= first else -1
+            fs = ft >= 0 and ft != prevT
+            ni_all, nvd_all = ni + (fs and ft == 1), nvd + (fs and ft == 2)
+            cand = ((gF + lsF) << 2 | lsT) if lsF >= 0 else ((gF << 2 | ft) if fs else -1)
+            S[c] = [gF, gA, prevT, ni_all, nvd_all, cand, None, None, nv]
+            ni_s += ni_all
+            nvd_s += nvd_all
+            st = max(st, cand)
+            gF += nv
+            gA += nt
+            if lts >= 0:
+                lt = c << 2 | lts
+        t_ni.append(ni_s)
+        t_nvd.append(nvd_s)
+        t_st.append(st)
+    img_ex, img_tot = _excl_sum(t_ni)
+    vid_ex, vid_tot = _excl_sum(t_nvd)
+    st_ex, _ = _excl_max(t_st, -1)
+    for t, (a, b) in enumerate(rng):
+        img, vid = img_ex[t], vid_ex[t]
+        for c in range(a, b):
+            S[c][6], S[c][7] = img, vid
+            img += S[c][3]
+            vid += S[c][4]
+    carries = [None] * n
+    valid, ends = [0] * B, [None] * B
+    for t, (a, b) in enumerate(rng):
+        st = st_ex[t]
+        for c in range(a, b):
+            bb, j = divmod(c, C)
+            s, s0 = S[c], S[bb * C]
+            F0 = s0[0]
+            S_in = (st >> 2) - F0 if st >= 0 and (st >> 2) >= F0 else -1
+            segT_in = (st & 3) if S_in >= 0 else -1
+            carries[c] = [s[0] - F0, s[1] - s0[1], s[2], s[6], s[7], s0[6], s0[7], S_in, segT_in]
+            st = max(st, s[5])
+            if j == C - 1:
+                v = s[0] + s[8] - F0
+                S_end = (st >> 2) - F0 if st >= 0 and (st >> 2) >= F0 else -1
+                segT_end = (st & 3) if S_end >= 0 else -1
+                valid[bb] = v
+                ends[bb] = (v - S_end, segT_end,
+                            (s[6] + s[3] - 1) if segT_end == 1 else (s[7] + s[4] - 1))
+    return carries, valid, ends, img_tot, vid_tot
+
+
+def model(types, mask, images, videos, merge, PT, PER, carry_threads=None):
     B, L = types.shape
     CH = PT * PER
     C = -(-L // CH)
@@ -159,6 +236,7 @@ def model(types, mask, images, videos, merge, PT, PER):
     status = 0
     img = vid = 0
     carries, valid = [], [0] * B
+    seq_ends = [None] * B
     delta = [0] * B
     F = A = 0
     prevT = S = segT = -1
@@ -185,12 +263,19 @@ def model(types, mask, images, videos, merge, PT, PER):
         if j == C - 1:
             valid[b] = F
             delta[b] = 0 if F == 0 else None
+            seq_ends[b] = (F - S, segT, (img if segT == 1 else vid) - 1)
             if segT in (1, 2):
                 g = tab.grid(segT, (img if segT == 1 else vid) - 1)
                 if g is not None and g["ok"] and F - S != g["slots"]:
                     status |= LENGTH
     if img > len(images) or vid > tab.cum_t[-1]:
         status |= NO_GRID
+    if carry_threads is not None:
+        # the kernel's parallel carry must reproduce the sequential walk
+        pc, pvalid, pends, pimg, pvid = carry_parallel(summaries, B, C, carry_threads)
+        assert pc == carries, (pc, carries)
+        assert pvalid == valid and (pimg, pvid) == (img, vid)
+        assert pends == seq_ends, (pends, seq_ends)
     # pass 3
     pos = np.zeros((3, B * L), dtype=np.int64)
     written = np.zeros(B * L, dtype=np.int64)
@@ -282,7 +367,8 @@ def test_model_matches_oracle(PT, PER, seed):
     types, mask, images, videos = W.random_mm_batch(rng, B, L)
     want, wd = P.get_rope_index(types, image_grid_thw=images or None,
                                 video_grid_thw=videos or None, attention_mask=mask)
-    got, gd, status = model(types, mask, images, videos, 2, PT, PER)
+    got, gd, status = model(types, mask, images, videos, 2, PT, PER,
+                            carry_threads=[1, 3, 256][seed % 3])
     assert status == 0
     assert np.array_equal(got, want)
     assert np.array_equal(gd, wd)

@@ -329,7 +329,7 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
 
 // Byte offsets of the regions of the position builder's workspace.
 struct RopeWs {
-  size_t sum = 0, carry = 0, valid = 0, adv_i = 0, adv_v = 0, cum_t = 0, total = 0;
+  size_t sum = 0, carry = 0, valid = 0, end = 0, adv_i = 0, adv_v = 0, cum_t = 0, total = 0;
   int64_t chunks_per_sample = 0;
 };
 
@@ -337,7 +337,9 @@ bool rope_ws_layout(int B, int64_t L, int n_img, int n_vid, RopeWs& w) {
   if (B < 0 || L < 0 || n_img < 0 || n_vid < 0) return false;
   w.chunks_per_sample = (L + mrope::kPosChunk - 1) / mrope::kPosChunk;
   const int64_t chunks = (int64_t)B * w.chunks_per_sample;
-  if (w.chunks_per_sample > INT32_MAX || chunks > INT32_MAX) return false;
+  // batch-wide filtered indices are packed as (index << 2 | type) in an int
+  if ((int64_t)B * L >= (int64_t(1) << 29)) return false;
+  (void)chunks;
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   size_t off = 0;
   w.sum = off;
@@ -346,6 +348,8 @@ bool rope_ws_layout(int B, int64_t L, int n_img, int n_vid, RopeWs& w) {
   off = al(off + (size_t)chunks * mrope::kPosCarryInts * 4);
   w.valid = off;
   off = al(off + (size_t)B * 4);
+  w.end = off;
+  off = al(off + (size_t)B * 12);
   w.adv_i = off;
   off = al(off + ((size_t)n_img + 1) * 8);
   w.adv_v = off;
@@ -434,6 +438,7 @@ int mrope_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask
   p.ws_sum = reinterpret_cast<int32_t*>(ws + w.sum);
   p.ws_carry = reinterpret_cast<int32_t*>(ws + w.carry);
   p.ws_valid = reinterpret_cast<int32_t*>(ws + w.valid);
+  p.ws_end = reinterpret_cast<int32_t*>(ws + w.end);
   p.ws_adv_i = reinterpret_cast<int64_t*>(ws + w.adv_i);
   p.ws_adv_v = reinterpret_cast<int64_t*>(ws + w.adv_v);
   p.ws_cum_t = reinterpret_cast<int32_t*>(ws + w.cum_t);

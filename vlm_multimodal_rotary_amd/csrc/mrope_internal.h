@@ -79,11 +79,12 @@ struct CosSinParams {
 
 // Position builders (mrope_positions.hip).
 constexpr int kPosThreads = 256;
-constexpr int kPosPerThread = 16;
+constexpr int kPosPerThread = 4;
 constexpr int kPosChunk = kPosThreads * kPosPerThread;   // tokens per block
 constexpr int kPosSumInts = 9;      // chunk summary: nv, nt, ni, nvd, ft, lt, lsF, lsT, flags
 constexpr int kPosCarryInts = 9;    // chunk carry: F, A, prevT, img, vid, img0, vid0, S, segT
-constexpr int kPosCarryTile = 512;  // summaries per LDS tile of the carry pass
+constexpr int kPosCarryLds = 1024;   // chunk records the carry pass keeps in LDS
+constexpr int kPosStageGrids = 256;  // grids per type the apply pass copies to LDS
 constexpr int kMaxVisionImages = 4096;   // patch-count prefix in LDS: 32 KB
 
 struct RopeIndexParams {
@@ -105,6 +106,7 @@ struct RopeIndexParams {
   int32_t* ws_sum;            // [B*C][kPosSumInts]
   int32_t* ws_carry;          // [B*C][kPosCarryInts]
   int32_t* ws_valid;          // [B]
+  int32_t* ws_end;            // [B][3] open segment at each sample's end
   int64_t* ws_adv_i;          // [n_images + 1]
   int64_t* ws_adv_v;          // [n_videos + 1]
   int32_t* ws_cum_t;          // [n_videos + 1]

@@ -140,18 +140,23 @@ __device__ __forceinline__ void read_run(const RopeIndexParams& p, int b, int64_
   r.ft = r.lt = r.lsF = r.lsT = -1;
   r.flags = 0;
   const int64_t row = (int64_t)b * p.L;
+  // Loads at clamped addresses, all issued before any is used; tokens past
+  // the row are discarded afterwards.
+  int tv[kPer], mv[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int64_t l = l0 + k;
+    const int64_t l = (l0 + k) < p.L ? (l0 + k) : (p.L - 1);
+    tv[k] = p.types[row + l];
+    mv[k] = p.mask != nullptr ? p.mask[row + l] : 1;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
     int ty = -1;
-    if (l < p.L) {
-      const bool v = p.mask == nullptr || p.mask[row + l] != 0;
-      if (v) {
-        ty = p.types[row + l];
-        if (ty < 0 || ty > 2) {
-          r.flags |= MROPE_POS_BAD_TYPE;
-          ty = 0;
-        }
+    if (l0 + k < p.L && mv[k] != 0) {
+      ty = tv[k];
+      if (ty < 0 || ty > 2) {
+        r.flags |= MROPE_POS_BAD_TYPE;
+        ty = 0;
       }
     }
     r.ty[k] = ty;
@@ -170,137 +175,167 @@ __device__ __forceinline__ void read_run(const RopeIndexParams& p, int b, int64_
   }
 }
 
-// The latest valid type of the threads before this one in the block, as an
-// encoded max: (thread << 2 | type), -1 for none.
-__device__ __forceinline__ int prev_type_in_block(const Run& r, int* sh) {
-  int tot;
-  const int enc = r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1;
-  const int m = block_excl_max(enc, -1, &tot, sh);
-  return m >= 0 ? (m & 3) : -1;
-}
-
 // ---------------------------------------------------------------------------
 // Pass 1: chunk summaries.
 // ---------------------------------------------------------------------------
 
+// Four per-run counts packed in 16-bit fields of one 64-bit word (a block
+// holds at most kPosChunk = 1024 tokens, so no field carries into the next).
+__device__ __forceinline__ unsigned long long pack4(int a, int b, int c, int d) {
+  return (unsigned long long)a | ((unsigned long long)b << 16) | ((unsigned long long)c << 32) |
+         ((unsigned long long)d << 48);
+}
+
+__device__ __forceinline__ int field(unsigned long long v, int i) {
+  return (int)((v >> (16 * i)) & 0xFFFFu);
+}
+
 __global__ void __launch_bounds__(kPT) rope_index_summarize(const RopeIndexParams p) {
   __shared__ int sh[kWaves];
-  __shared__ long long shl[kWaves];
+  __shared__ unsigned long long shu[kWaves];
   const int b = (int)(blockIdx.x / (unsigned)p.C);
   const int j = (int)(blockIdx.x - (unsigned)b * (unsigned)p.C);
   const int64_t l0 = (int64_t)j * kPosChunk + (int64_t)threadIdx.x * kPer;
   Run r;
   read_run(p, b, l0, r);
-  const int pt = prev_type_in_block(r, sh);
+  // latest valid type before this run in the chunk; the block total is the
+  // chunk's last valid type
+  int last_enc;
+  const int enc = r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1;
+  const int pe = block_excl_max(enc, -1, &last_enc, sh);
+  const int pt = pe >= 0 ? (pe & 3) : -1;
   // The run's first valid token starts a segment when a valid token earlier
   // in the chunk has another type; the chunk's first valid token is decided
   // by the carry pass.
   const bool fs = r.ft >= 0 && pt >= 0 && r.ft != pt;
   const int ni = r.ni + (fs && r.ft == 1);
   const int nvd = r.nvd + (fs && r.ft == 2);
-  int nv_tot, nt_tot, ni_tot, nvd_tot;
-  const int nv_ex = block_excl_sum(r.nv, &nv_tot, sh);
-  block_excl_sum(r.nt, &nt_tot, sh);
-  block_excl_sum(ni, &ni_tot, sh);
-  block_excl_sum(nvd, &nvd_tot, sh);
-  const int fl_tot = block_or(r.flags, sh);
+  unsigned long long tot;
+  const unsigned long long ex = block_excl_sum(pack4(r.nv, r.nt, ni, nvd), &tot, shu);
+  const int nv_ex = field(ex, 0);
   // last start of the chunk (chunk-local filtered index, type)
-  long long cand = -1;
-  if (r.lsF >= 0) cand = ((long long)(nv_ex + r.lsF) << 2) | r.lsT;
-  else if (fs) cand = ((long long)nv_ex << 2) | r.ft;
-  long long last_start;
-  block_excl_max(cand, -1LL, &last_start, shl);
-  // first and last valid type of the chunk
-  int first_enc, last_enc;
+  int cand = -1;
+  if (r.lsF >= 0) cand = ((nv_ex + r.lsF) << 2) | r.lsT;
+  else if (fs) cand = (nv_ex << 2) | r.ft;
+  int last_start;
+  block_excl_max(cand, -1, &last_start, sh);
+  // first valid type of the chunk (the smallest thread with a valid token)
+  int first_enc;
   block_excl_max(r.ft >= 0 ? (int)((kPT - 1 - threadIdx.x) << 2) | r.ft : -1, -1, &first_enc, sh);
-  block_excl_max(r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1, -1, &last_enc, sh);
+  const int fl_tot = block_or(r.flags, sh);
   if (threadIdx.x == 0) {
     int* s = p.ws_sum + ((int64_t)b * p.C + j) * kPosSumInts;
-    s[0] = nv_tot;
-    s[1] = nt_tot;
-    s[2] = ni_tot;
-    s[3] = nvd_tot;
+    s[0] = field(tot, 0);
+    s[1] = field(tot, 1);
+    s[2] = field(tot, 2);
+    s[3] = field(tot, 3);
     s[4] = first_enc >= 0 ? (first_enc & 3) : -1;
     s[5] = last_enc >= 0 ? (last_enc & 3) : -1;
-    s[6] = last_start >= 0 ? (int)(last_start >> 2) : -1;
-    s[7] = last_start >= 0 ? (int)(last_start & 3) : -1;
+    s[6] = last_start >= 0 ? (last_start >> 2) : -1;
+    s[7] = last_start >= 0 ? (last_start & 3) : -1;
     s[8] = fl_tot;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Grid helpers (tables built by the carry pass).
+// Grid helpers (tables built by the carry pass; global memory or an LDS copy).
 // ---------------------------------------------------------------------------
+
+struct Tables {
+  const int32_t* img;     // [n_images][3]
+  const int64_t* adv_i;   // [n_images + 1] image advances before k
+  const int32_t* vid;     // [n_videos][3]
+  const int32_t* cum_t;   // [n_videos + 1] slices before video v
+  const int64_t* adv_v;   // [n_videos + 1] their advances
+  int n_images, n_videos, merge;
+};
+
+__device__ __forceinline__ Tables global_tables(const RopeIndexParams& p) {
+  return Tables{p.image_grid, p.ws_adv_i, p.video_grid, p.ws_cum_t, p.ws_adv_v,
+                p.n_images, p.n_videos, p.merge};
+}
 
 struct Grid {
   int t, hm, wm, adv;   // slot grid and the advance max(h, w) / merge
-  int64_t slots;
+  int slots;            // t * hm * wm (grids with 2^31 slots or more are not usable)
+  int plane;            // hm * wm
   bool ok;
 };
 
-__device__ __forceinline__ int video_of_slice(const RopeIndexParams& p, int k) {
+__device__ __forceinline__ int video_of_slice(const Tables& tb, int k) {
   // largest v with cum_t[v] <= k, for 0 <= k < cum_t[n_videos]
-  int lo = 0, hi = p.n_videos - 1;
+  int lo = 0, hi = tb.n_videos - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.ws_cum_t[mid] <= k) lo = mid;
+    if (tb.cum_t[mid] <= k) lo = mid;
     else hi = mid - 1;
   }
   return lo;
 }
 
 // Grid of the k-th segment of type `ty` (1 image, 2 video slice).
-__device__ Grid grid_of(const RopeIndexParams& p, int ty, int k) {
+__device__ Grid grid_of(const Tables& tb, int ty, int k) {
   Grid g;
   g.ok = false;
   g.t = g.hm = g.wm = g.adv = 0;
   g.slots = 0;
+  g.plane = 1;
   int t, h, w;
   if (ty == 1) {
-    if (k < 0 || k >= p.n_images) return g;
-    t = p.image_grid[3 * k];
-    h = p.image_grid[3 * k + 1];
-    w = p.image_grid[3 * k + 2];
+    if (k < 0 || k >= tb.n_images) return g;
+    t = tb.img[3 * k];
+    h = tb.img[3 * k + 1];
+    w = tb.img[3 * k + 2];
   } else {
-    if (k < 0 || k >= p.ws_cum_t[p.n_videos]) return g;
-    const int v = video_of_slice(p, k);
+    if (k < 0 || k >= tb.cum_t[tb.n_videos]) return g;
+    const int v = video_of_slice(tb, k);
     t = 1;
-    h = p.video_grid[3 * v + 1];
-    w = p.video_grid[3 * v + 2];
+    h = tb.vid[3 * v + 1];
+    w = tb.vid[3 * v + 2];
   }
   g.t = t;
-  g.hm = h / p.merge;
-  g.wm = w / p.merge;
-  g.adv = (h > w ? h : w) / p.merge;
-  g.slots = (int64_t)t * g.hm * g.wm;
-  g.ok = t > 0 && g.hm > 0 && g.wm > 0;
+  g.hm = h / tb.merge;
+  g.wm = w / tb.merge;
+  g.adv = (h > w ? h : w) / tb.merge;
+  const int64_t slots = (int64_t)t * g.hm * g.wm;
+  g.ok = t > 0 && g.hm > 0 && g.wm > 0 && slots <= INT32_MAX;
+  g.slots = g.ok ? (int)slots : 0;
+  g.plane = g.ok ? g.hm * g.wm : 1;
   return g;
 }
 
 // Sum of the advances of image grids [0, k) and video slices [0, k).
-__device__ __forceinline__ int64_t image_adv_before(const RopeIndexParams& p, int k) {
-  k = k < p.n_images ? k : p.n_images;
-  return p.ws_adv_i[k];
+__device__ __forceinline__ int64_t image_adv_before(const Tables& tb, int k) {
+  k = k < tb.n_images ? k : tb.n_images;
+  return tb.adv_i[k];
 }
 
-__device__ __forceinline__ int64_t video_adv_before(const RopeIndexParams& p, int k) {
-  const int n = p.ws_cum_t[p.n_videos];
+__device__ __forceinline__ int64_t video_adv_before(const Tables& tb, int k) {
+  const int n = tb.cum_t[tb.n_videos];
   k = k < n ? k : n;
   if (k <= 0) return 0;
-  if (k == n) return p.ws_adv_v[p.n_videos];
-  const int v = video_of_slice(p, k);
-  const int h = p.video_grid[3 * v + 1], w = p.video_grid[3 * v + 2];
-  return p.ws_adv_v[v] + (int64_t)(k - p.ws_cum_t[v]) * ((h > w ? h : w) / p.merge);
+  if (k == n) return tb.adv_v[tb.n_videos];
+  const int v = video_of_slice(tb, k);
+  const int h = tb.vid[3 * v + 1], w = tb.vid[3 * v + 2];
+  return tb.adv_v[v] + (int64_t)(k - tb.cum_t[v]) * ((h > w ? h : w) / tb.merge);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: grid tables and chunk carries (one block).
+//
+// The carry of chunk c is a scan over the chunks before it.  Per-sample
+// quantities restart at each sample's first chunk b*C; they are taken as the
+// batch-wide prefix at c minus the prefix at b*C.  Each thread owns a
+// contiguous range of chunks; block scans combine the ranges in three rounds
+// (valid/text counts and the latest valid type; segment starts by type and
+// the latest start; the sample bases), with provisional per-chunk records in
+// the summary slots between rounds.  Batch-wide filtered indices are below
+// 2^29 (checked on the host), so (index << 2 | type) fits an int.
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p) {
+  __shared__ int sh[kWaves];
   __shared__ long long shl[kWaves];
-  __shared__ int tile[kPosCarryTile * kPosSumInts];
-  __shared__ int out[kPosCarryTile * kPosCarryInts];
   // Grid-advance prefix tables: adv_i[k] = sum of image advances before k;
   // cum_t[v] = slices before video v; adv_v[v] = their advances.
   long long carry = 0;
@@ -341,75 +376,131 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
     p.ws_cum_t[p.n_videos] = (int)ct;
     p.ws_adv_v[p.n_videos] = ca;
   }
+
+  const int n = p.B * p.C;
+  const int per = (n + kPT - 1) / kPT;
+  const int c0 = min(n, (int)threadIdx.x * per);
+  const int c1 = min(n, c0 + per);
+  const int C = p.C > 0 ? p.C : 1;
+  // The rounds below re-read the per-chunk records several times: keep them
+  // in LDS when they fit (the provisional records never go back to memory).
+  __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
+  int* const rec = n <= kPosCarryLds ? rec_lds : p.ws_sum;
+  if (n <= kPosCarryLds) {
+    for (int i = threadIdx.x; i < n * kPosSumInts; i += kPT) rec_lds[i] = p.ws_sum[i];
+    __syncthreads();
+  }
+
+  // Round 1: valid / text counts, the latest valid type, summary flags.
+  int t_nv = 0, t_nt = 0, t_lt = -1, t_flags = 0;
+  for (int c = c0; c < c1; ++c) {
+    const int* s = rec + (int64_t)c * kPosSumInts;
+    t_nv += s[0];
+    t_nt += s[1];
+    if (s[5] >= 0) t_lt = (c << 2) | s[5];
+    t_flags |= s[8];
+  }
+  int tot;
+  int gF = block_excl_sum(t_nv, &tot, sh);
+  int gA = block_excl_sum(t_nt, &tot, sh);
+  int lt = block_excl_max(t_lt, -1, &tot, sh);
+  const int flags = block_or(t_flags, sh);
+
+  // Round 2: segment starts (the first valid token of a chunk starts a
+  // segment when the latest valid type before it in its sample differs).
+  int t_ni = 0, t_nvd = 0, t_st = -1;
+  {
+    int b = c0 / C, first = b * C;
+    for (int c = c0; c < c1; ++c) {
+      if (c - first >= C) {
+        ++b;
+        first += C;
+      }
+      int* s = rec + (int64_t)c * kPosSumInts;
+      const int nv = s[0], nt = s[1], ni = s[2], nvd = s[3], ft = s[4], lts = s[5];
+      const int lsF = s[6], lsT = s[7];
+      const int prevT = (lt >= 0 && (lt >> 2) >= first) ? (lt & 3) : -1;
+      const bool fs = ft >= 0 && ft != prevT;
+      const int ni_all = ni + (fs && ft == 1);
+      const int nvd_all = nvd + (fs && ft == 2);
+      const int cand = lsF >= 0 ? ((gF + lsF) << 2) | lsT : (fs ? (gF << 2) | ft : -1);
+      // provisional record (the summary is not needed any more)
+      s[0] = gF;
+      s[1] = gA;
+      s[2] = prevT;
+      s[3] = ni_all;
+      s[4] = nvd_all;
+      s[5] = cand;
+      s[8] = nv;
+      t_ni += ni_all;
+      t_nvd += nvd_all;
+      if (cand > t_st) t_st = cand;
+      gF += nv;
+      gA += nt;
+      if (lts >= 0) lt = (c << 2) | lts;
+    }
+  }
+  int img_total, vid_total;
+  int img = block_excl_sum(t_ni, &img_total, sh);
+  int vid = block_excl_sum(t_nvd, &vid_total, sh);
+  int st = block_excl_max(t_st, -1, &tot, sh);
+
+  // Round 3a: grid counters per chunk.
+  for (int c = c0; c < c1; ++c) {
+    int* s = rec + (int64_t)c * kPosSumInts;
+    s[6] = img;
+    s[7] = vid;
+    img += s[3];
+    vid += s[4];
+  }
   __threadfence_block();
   __syncthreads();
 
-  // Sequential walk over the chunk summaries, a tile at a time through LDS.
-  // State lives in thread 0's registers between tiles.
-  int status = 0;
-  int img = 0, vid = 0;
-  int F = 0, A = 0, prevT = -1, S = -1, segT = -1, img_base = 0, vid_base = 0;
-  const int64_t n_chunks = (int64_t)p.B * p.C;
-  for (int64_t t0 = 0; t0 < n_chunks; t0 += kPosCarryTile) {
-    const int n = (int)((n_chunks - t0) < kPosCarryTile ? (n_chunks - t0) : kPosCarryTile);
-    for (int i = threadIdx.x; i < n * kPosSumInts; i += kPT) tile[i] = p.ws_sum[t0 * kPosSumInts + i];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int i = 0; i < n; ++i) {
-        const int64_t c = t0 + i;
-        const int b = (int)(c / p.C);
-        const int j = (int)(c - (int64_t)b * p.C);
-        if (j == 0) {
-          F = A = 0;
-          prevT = S = segT = -1;
-          img_base = img;
-          vid_base = vid;
-        }
-        int* o = out + i * kPosCarryInts;
-        o[0] = F;
-        o[1] = A;
-        o[2] = prevT;
-        o[3] = img;
-        o[4] = vid;
-        o[5] = img_base;
-        o[6] = vid_base;
-        o[7] = S;
-        o[8] = segT;
-        const int* s = tile + i * kPosSumInts;
-        status |= s[8];
-        const bool fs = s[4] >= 0 && s[4] != prevT;
-        img += s[2] + (fs && s[4] == 1);
-        vid += s[3] + (fs && s[4] == 2);
-        if (s[6] >= 0) {
-          S = F + s[6];
-          segT = s[7];
-        } else if (fs) {
-          S = F;
-          segT = s[4];
-        }
-        F += s[0];
-        A += s[1];
-        if (s[5] >= 0) prevT = s[5];
-        if (j == p.C - 1) {
-          p.ws_valid[b] = F;
-          p.rope_delta[b] = F == 0 ? 0 : INT32_MIN;
-          // the sample's last segment must be complete
-          if (segT == 1 || segT == 2) {
-            const Grid g = grid_of(p, segT, (segT == 1 ? img : vid) - 1);
-            if (g.ok && (int64_t)(F - S) != g.slots) status |= MROPE_POS_LENGTH;
-          }
-        }
+  // Round 3b: carries relative to each sample's first chunk.
+  {
+    int b = c0 / C, first = b * C;
+    for (int c = c0; c < c1; ++c) {
+      if (c - first >= C) {
+        ++b;
+        first += C;
+      }
+      const int* s = rec + (int64_t)c * kPosSumInts;
+      const int* s0 = rec + (int64_t)first * kPosSumInts;
+      const int F0 = s0[0];
+      const int S_in = (st >= 0 && (st >> 2) >= F0) ? (st >> 2) - F0 : -1;
+      const int segT_in = S_in >= 0 ? (st & 3) : -1;
+      int* o = p.ws_carry + (int64_t)c * kPosCarryInts;
+      o[0] = s[0] - F0;
+      o[1] = s[1] - s0[1];
+      o[2] = s[2];
+      o[3] = s[6];
+      o[4] = s[7];
+      o[5] = s0[6];
+      o[6] = s0[7];
+      o[7] = S_in;
+      o[8] = segT_in;
+      if (s[5] > st) st = s[5];
+      if (c - first == C - 1) {
+        // the sample's end: valid length, the open segment, the delta's seed
+        const int valid = s[0] + s[8] - F0;
+        const int S_end = (st >= 0 && (st >> 2) >= F0) ? (st >> 2) - F0 : -1;
+        const int segT_end = S_end >= 0 ? (st & 3) : -1;
+        p.ws_valid[b] = valid;
+        p.rope_delta[b] = valid == 0 ? 0 : INT32_MIN;
+        int* e = p.ws_end + 3 * b;
+        e[0] = valid - S_end;
+        e[1] = segT_end;
+        e[2] = segT_end == 1 ? s[6] + s[3] - 1 : s[7] + s[4] - 1;
       }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < n * kPosCarryInts; i += kPT)
-      p.ws_carry[t0 * kPosCarryInts + i] = out[i];
-    __syncthreads();
   }
   if (p.C == 0)   // empty sequences: every sample has delta 0
     for (int b = threadIdx.x; b < p.B; b += kPT) p.rope_delta[b] = 0;
+  // (each sample's last segment is checked by the apply pass, which has
+  // the grid tables at hand)
   if (threadIdx.x == 0) {
-    if (img > p.n_images || vid > p.ws_cum_t[p.n_videos]) status |= MROPE_POS_NO_GRID;
+    int status = flags;
+    if (img_total > p.n_images || vid_total > (int)ct) status |= MROPE_POS_NO_GRID;
     *p.status = status;
   }
 }
@@ -420,7 +511,32 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
 
 __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p) {
   __shared__ int sh[kWaves];
+  __shared__ unsigned long long shu[kWaves];
   __shared__ long long shl[kWaves];
+  // LDS copy of the grid tables when they are small (the common case): the
+  // segment starts of a chunk then look grids up without memory round trips.
+  __shared__ int32_t t_img[3 * kPosStageGrids];
+  __shared__ int64_t t_adv_i[kPosStageGrids + 1];
+  __shared__ int32_t t_vid[3 * kPosStageGrids];
+  __shared__ int32_t t_cum_t[kPosStageGrids + 1];
+  __shared__ int64_t t_adv_v[kPosStageGrids + 1];
+  Tables tb = global_tables(p);
+  if (p.n_images <= kPosStageGrids && p.n_videos <= kPosStageGrids) {
+    for (int i = threadIdx.x; i < 3 * p.n_images; i += kPT) t_img[i] = p.image_grid[i];
+    for (int i = threadIdx.x; i <= p.n_images; i += kPT) t_adv_i[i] = p.ws_adv_i[i];
+    for (int i = threadIdx.x; i < 3 * p.n_videos; i += kPT) t_vid[i] = p.video_grid[i];
+    for (int i = threadIdx.x; i <= p.n_videos; i += kPT) {
+      t_cum_t[i] = p.ws_cum_t[i];
+      t_adv_v[i] = p.ws_adv_v[i];
+    }
+    tb.img = t_img;
+    tb.adv_i = t_adv_i;
+    tb.vid = t_vid;
+    tb.cum_t = t_cum_t;
+    tb.adv_v = t_adv_v;
+    // the copies are ordered before their first use by the barriers of the
+    // block scans below
+  }
   const int b = (int)(blockIdx.x / (unsigned)p.C);
   const int j = (int)(blockIdx.x - (unsigned)b * (unsigned)p.C);
   const int* cin = p.ws_carry + ((int64_t)b * p.C + j) * kPosCarryInts;
@@ -431,31 +547,32 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
   const int64_t l0 = (int64_t)j * kPosChunk + (int64_t)threadIdx.x * kPer;
   Run r;
   read_run(p, b, l0, r);
-  const int pt_blk = prev_type_in_block(r, sh);
-  int prevT = pt_blk >= 0 ? pt_blk : prevT_in;
+  int lt_tot;
+  const int pe = block_excl_max(r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1, -1, &lt_tot, sh);
+  int prevT = pe >= 0 ? (pe & 3) : prevT_in;
   const bool fs = r.ft >= 0 && r.ft != prevT;
   const int ni = r.ni + (fs && r.ft == 1);
   const int nvd = r.nvd + (fs && r.ft == 2);
-  int tot;
-  int F = F_in + block_excl_sum(r.nv, &tot, sh);
-  int A = A_in + block_excl_sum(r.nt, &tot, sh);
-  int img = img_in + block_excl_sum(ni, &tot, sh);
-  int vid = vid_in + block_excl_sum(nvd, &tot, sh);
-  long long cand = -1;
-  const int f_run = F;   // filtered index of the run's first valid token
-  if (r.lsF >= 0) cand = ((long long)(f_run + r.lsF) << 2) | r.lsT;
-  else if (fs) cand = ((long long)f_run << 2) | r.ft;
-  long long ltot;
-  const long long before = block_excl_max(cand, -1LL, &ltot, shl);
-  int S = before >= 0 ? (int)(before >> 2) : S_in;
-  int segT = before >= 0 ? (int)(before & 3) : segT_in;
+  unsigned long long tot;
+  const unsigned long long ex = block_excl_sum(pack4(r.nv, r.nt, ni, nvd), &tot, shu);
+  int F = F_in + field(ex, 0);
+  int A = A_in + field(ex, 1);
+  int img = img_in + field(ex, 2);
+  int vid = vid_in + field(ex, 3);
+  // latest segment start before the run (filtered index << 2 | type)
+  int cand = -1;
+  if (r.lsF >= 0) cand = ((F + r.lsF) << 2) | r.lsT;
+  else if (fs) cand = (F << 2) | r.ft;
+  int ctot;
+  const int before = block_excl_max(cand, -1, &ctot, sh);
+  int S = before >= 0 ? (before >> 2) : S_in;
+  int segT = before >= 0 ? (before & 3) : segT_in;
 
   // the segment open at the start of the run
-  Grid g = {0, 0, 0, 0, 0, false};
-  if (segT == 1 || segT == 2) g = grid_of(p, segT, (segT == 1 ? img : vid) - 1);
-  const int64_t adv_i0 = image_adv_before(p, img_base);
-  const int64_t adv_v0 = video_adv_before(p, vid_base);
-  int64_t badv = image_adv_before(p, img) - adv_i0 + video_adv_before(p, vid) - adv_v0;
+  Grid g = {0, 0, 0, 0, 0, 1, false};
+  if (segT == 1 || segT == 2) g = grid_of(tb, segT, (segT == 1 ? img : vid) - 1);
+  const int64_t adv0 = image_adv_before(tb, img_base) + video_adv_before(tb, vid_base);
+  int64_t badv = image_adv_before(tb, img) + video_adv_before(tb, vid) - adv0;
 
   int flags = 0;   // bad types were reported by the summary pass
   int64_t mx = INT64_MIN;
@@ -467,15 +584,15 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
     int64_t pt = 0, ph = 0, pw = 0;
     if (ty >= 0) {
       if (ty != prevT) {
-        if ((segT == 1 || segT == 2) && g.ok && (int64_t)(F - S) != g.slots)
+        if ((segT == 1 || segT == 2) && g.ok && F - S != g.slots)
           flags |= MROPE_POS_LENGTH;
         S = F;
         segT = ty;
         if (ty == 1) ++img;
         if (ty == 2) ++vid;
         if (ty != 0) {
-          g = grid_of(p, ty, (ty == 1 ? img : vid) - 1);
-          badv = image_adv_before(p, img) - adv_i0 + video_adv_before(p, vid) - adv_v0;
+          g = grid_of(tb, ty, (ty == 1 ? img : vid) - 1);
+          badv = image_adv_before(tb, img) + video_adv_before(tb, vid) - adv0;
         }
       }
       prevT = ty;
@@ -483,19 +600,18 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
         if (ty != 0) flags |= MROPE_POS_NO_GRID;
         pt = ph = pw = (int64_t)A + badv;
       } else {
-        int64_t i = F - S;
+        int i = F - S;
         if (i >= g.slots) {
           flags |= MROPE_POS_LENGTH;
           i = g.slots - 1;
         }
         const int64_t base = (int64_t)A + badv - g.adv;
-        const int64_t plane = (int64_t)g.hm * g.wm;
-        const int64_t tt = i / plane;
-        const int64_t rem = i - tt * plane;
-        const int64_t row = rem / g.wm;
+        const unsigned tt = (unsigned)i / (unsigned)g.plane;
+        const unsigned rem = (unsigned)i - tt * (unsigned)g.plane;
+        const unsigned row = rem / (unsigned)g.wm;
         pt = base + tt;
         ph = base + row;
-        pw = base + (rem - row * g.wm);
+        pw = base + (rem - row * (unsigned)g.wm);
       }
       A += ty == 0;
       ++F;
@@ -507,6 +623,15 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
     p.pos[o] = (int32_t)pt;
     p.pos[p.pos_stride + o] = (int32_t)ph;
     p.pos[2 * p.pos_stride + o] = (int32_t)pw;
+  }
+  // the sample's last segment must be complete (checked once, by the block
+  // of its last chunk)
+  if (j == p.C - 1 && threadIdx.x == 0) {
+    const int* e = p.ws_end + 3 * b;
+    if (e[1] == 1 || e[1] == 2) {
+      const Grid ge = grid_of(tb, e[1], e[2]);
+      if (ge.ok && e[0] != ge.slots) flags |= MROPE_POS_LENGTH;
+    }
   }
   long long bmax;
   block_excl_max((long long)mx, (long long)INT64_MIN, &bmax, shl);

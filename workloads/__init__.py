@@ -373,3 +373,60 @@ def random_mm_batch(rng, B: int, L: int, pad: bool = True, merge: int = 2):
             types[b, cut + hole:] = flat[cut:]
             mask[b, cut + hole:] = 1
     return types, mask, images, videos
+
+
+@dataclasses.dataclass(frozen=True)
+class PositionWorkload:
+    """A batch of multimodal prompts for the position builder."""
+    name: str
+    index: int
+    batch: int
+    seq_len: int
+    description: str = ""
+
+    @property
+    def T(self) -> int:
+        return self.batch * self.seq_len
+
+    def algorithmic_bytes(self) -> int:
+        # token types and mask read once (int32), three int32 positions
+        # written, one delta per sample
+        return self.T * (4 + 4 + 12) + 4 * self.batch
+
+
+POSITION_WORKLOADS = {
+    w.name: w for w in [
+        PositionWorkload("mm_prompt_positions", 7, 8, 8192,
+                         description="8 prompts x 8192 slots: system text, a 48x64-patch image, "
+                                     "text, a 4-slice 32x32 video with timestamps, text, left "
+                                     "padding"),
+    ]
+}
+
+
+def mm_prompt_batch(wl: PositionWorkload | str, seed: int | None = None):
+    """Seeded batch of chat-style multimodal prompts: per sample, a system
+    text run, one image (1, 48, 64) -> 768 slots, a text run, one video of 4
+    slices (4, 32, 32) -> 4 runs of 256 slots each preceded by 3 timestamp
+    tokens, then text, with 0..1023 tokens of left padding.  Returns types,
+    mask [B, L] int32 and the image / video grids in batch order."""
+    if isinstance(wl, str):
+        wl = POSITION_WORKLOADS[wl]
+    rng = np.random.default_rng(wl.index if seed is None else seed)
+    B, L = wl.batch, wl.seq_len
+    types = np.zeros((B, L), dtype=np.int32)
+    mask = np.zeros((B, L), dtype=np.int32)
+    images, videos = [], []
+    for b in range(B):
+        pad = int(rng.integers(0, 1024))
+        sys_len = int(rng.integers(50, 400))
+        mid = int(rng.integers(20, 300))
+        seq = [0] * sys_len + [1] * 768 + [0] * mid
+        for _ in range(4):
+            seq += [0] * 3 + [2] * 256
+        seq += [0] * (L - pad - len(seq))
+        types[b, pad:] = seq
+        mask[b, pad:] = 1
+        images.append((1, 48, 64))
+        videos.append((4, 32, 32))
+    return types, mask, np.array(images, dtype=np.int32), np.array(videos, dtype=np.int32)
