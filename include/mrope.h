@@ -238,6 +238,34 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq,
                     void* k_cache, int64_t k_cache_seq_stride, int64_t k_cache_tok_stride,
                     int k_cache_capacity, void* stream);
 
+/*
+ * mrope_vision_qkv — the vision tower's rotary step on a packed qkv in one
+ * pass ([Q3V] attention: the packed projection is [n, 3, heads, hd] with the
+ * head axis innermost; q and k are rotated split-half over the head and
+ * written, with v copied, to per-head planes for the attention kernel;
+ * [QVL] apply_rotary_pos_emb_vision for the rotation and its precision):
+ *   q_out[h][t][j] = rotate(qkv[t][0][h][:])[j], k_out likewise from
+ *   qkv[t][1], v_out[h][t][j] = qkv[t][2][h][j],
+ * with the rotation and cos/sin of rmsnorm_mrope_qk for the vision 2-D
+ * layout (positions [2][n]: row, col; inv_freq = mrope_inv_freq(
+ * rotary_dim/2, theta) for both), dims past rotary_dim passed through, and
+ * the precision argument as there.
+ *   qkv:        device [n][3][heads][D], token stride qkv_tok_stride
+ *               (elements, >= 3*heads*D).
+ *   q_out, k_out, v_out: device; element (h, t, j) at
+ *               h*out_head_stride + t*out_tok_stride + j.  Head-major planes:
+ *               out_head_stride = n*D, out_tok_stride = D; token-major rows:
+ *               out_head_stride = D, out_tok_stride >= heads*D.  v_out may be
+ *               NULL (v not written).
+ * The outputs may not overlap the input or each other.  EINVAL on bad
+ * shapes or strides (rows that would overlap), null pointers, overlap;
+ * EUNSUPPORTED when one token's output rows span 2^31 bytes or more.
+ */
+int mrope_vision_qkv(const void* qkv, int64_t qkv_tok_stride, int64_t n, int heads, int D,
+                     int rotary_dim, const int32_t* pos, int64_t pos_axis_stride, double theta,
+                     int dtype, int precision, void* q_out, void* k_out, void* v_out,
+                     int64_t out_head_stride, int64_t out_tok_stride, void* stream);
+
 /* Status bits written by the position builders into their device `status`
  * word (0 = the inputs describe a sequence the walkthrough can build). */
 #define MROPE_POS_BAD_TYPE      1   /* a valid token's type is not 0, 1 or 2 (taken as text) */

@@ -417,6 +417,31 @@ def rmsnorm_mrope_qk(q, k, pos, *, rotary_dim: int, theta: float, section, layou
 
 
 # ---------------------------------------------------------------------------
+# Vision tower: packed qkv to per-head planes
+# ---------------------------------------------------------------------------
+
+def vision_qkv(qkv, pos, *, rotary_dim: int, theta: float, dtype: str = "f32",
+               precision: str = "exact"):
+    """The vision attention's rotary step on a packed projection.
+
+    cortiq-engine ``qwen3vis.rs`` (``attention``): the projection is
+    [n, 3, heads, hd] with the head axis innermost; q and k of every head are
+    rotated split-half over the head with the patch's (row, col) angles and
+    laid out as per-head planes [heads, n, hd] for the attention kernel; v is
+    copied into its plane unchanged.  The rotation is this oracle's fused
+    path for the vision 2-D layout (no RMSNorm), so the planes are the
+    token-major results transposed.  Returns (q, k, v) planes in the stored
+    representation.
+    """
+    qkv = np.asarray(qkv)
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    qo, ko = rmsnorm_mrope_qk(q, k, pos, rotary_dim=rotary_dim, theta=theta, section=None,
+                              layout=LAYOUT_VISION_2D, dtype=dtype, precision=precision)
+    return (np.ascontiguousarray(qo.transpose(1, 0, 2)), np.ascontiguousarray(ko.transpose(1, 0, 2)),
+            np.ascontiguousarray(v.transpose(1, 0, 2)))
+
+
+# ---------------------------------------------------------------------------
 # Decode: positions from the cache length, rotated K appended to a KV cache
 # ---------------------------------------------------------------------------
 

@@ -1,0 +1,112 @@
+"""GPU parity of the vision qkv fusion (packed [n, 3, heads, D] -> rotated q,
+k and copied v in per-head planes) against the CPU oracle.
+
+Bars: as for the fused path (bf16 within 1 ulp, fp32 within 1e-5, v and
+pass-through dims bit-exact); the kernel is expected to match bit for bit.
+"""
+import numpy as np
+import pytest
+
+from oracle import mrope_oracle as O
+import workloads as W
+from tests._helpers import assert_close, from_dev, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import vlm_multimodal_rotary_amd as lib
+    lib.load()
+    return lib
+
+
+def _dev_qkv(qkv, dtype):
+    n, _, H, D = qkv.shape
+    return to_dev(qkv.reshape(n, 3 * H * D), dtype).reshape(n, 3, H, D)
+
+
+def _run(M, qkv, pos, dtype, rd, theta, **kw):
+    import torch
+    q, k, v = M.vision_qkv(_dev_qkv(qkv, dtype), to_dev(pos, "i32"), rd, theta, **kw)
+    torch.cuda.synchronize()
+    return from_dev(q), from_dev(k), None if v is None else from_dev(v)
+
+
+@pytest.mark.parametrize("dtype,n,H,D,rd", [("f32", 777, 16, 72, 72), ("bf16", 777, 16, 72, 72),
+                                             ("bf16", 300, 6, 128, 64), ("f32", 129, 5, 80, 80),
+                                             ("bf16", 1, 4, 72, 72)])
+def test_vision_qkv_planes(M, dtype, n, H, D, rd):
+    rng = np.random.default_rng(n + D)
+    qkv = W._store(rng.standard_normal((n, 3, H, D)).astype(np.float32), dtype)
+    pos = W.vision_patch_positions(1, 64, 64)[:, :n].astype(np.int32)
+    note(f"vision_qkv {dtype} n={n} H={H} D={D} rd={rd}")
+    gq, gk, gv = _run(M, qkv, pos, dtype, rd, 1e4)
+    oq, ok, ov = O.vision_qkv(qkv, pos, rotary_dim=rd, theta=1e4, dtype=dtype)
+    assert_close(gq, oq, dtype, "vision q planes")
+    assert_close(gk, ok, dtype, "vision k planes")
+    assert np.array_equal(gv.view(np.uint8), ov.view(np.uint8))
+
+
+@pytest.mark.parametrize("precision", ["dtype", "fp32"])
+def test_vision_qkv_precisions_bit_exact(M, precision):
+    rng = np.random.default_rng(71)
+    qkv = W._store(rng.standard_normal((500, 3, 16, 72)).astype(np.float32), "bf16")
+    pos = W.vision_patch_positions(1, 64, 64)[:, 1000:1500].astype(np.int32)
+    note(f"vision_qkv precision {precision}")
+    gq, gk, _ = _run(M, qkv, pos, "bf16", 72, 1e4, precision=precision)
+    oq, ok, _ = O.vision_qkv(qkv, pos, rotary_dim=72, theta=1e4, dtype="bf16", precision=precision)
+    assert np.array_equal(gq, oq) and np.array_equal(gk, ok)
+
+
+def test_vision_qkv_token_major_and_without_v(M):
+    rng = np.random.default_rng(72)
+    qkv = W._store(rng.standard_normal((400, 3, 16, 72)).astype(np.float32), "f32")
+    pos = W.vision_patch_positions(1, 64, 64)[:, :400].astype(np.int32)
+    note("vision_qkv token-major, no v")
+    gq, gk, gv = _run(M, qkv, pos, "f32", 72, 1e4, head_major=False, with_v=False)
+    oq, ok, _ = O.vision_qkv(qkv, pos, rotary_dim=72, theta=1e4, dtype="f32")
+    assert gv is None
+    assert_close(gq, oq.transpose(1, 0, 2), "f32", "token-major q")
+    assert_close(gk, ok.transpose(1, 0, 2), "f32", "token-major k")
+
+
+def test_vision_qkv_equals_the_fused_path(M):
+    """The planes hold exactly what rmsnorm_mrope_qk writes for the same q/k
+    views of the packed buffer (vision layout), transposed."""
+    import torch
+    wl = W.VISION_QKV_WORKLOADS["vision_qkv_planes"]
+    inp = W.make_vision_qkv_inputs(wl, n=3000)
+    qkv = _dev_qkv(inp["qkv"], wl.dtype)
+    pos = to_dev(inp["pos"], "i32")
+    q, k, v = M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta)
+    fq, fk = M.rmsnorm_mrope_qk(qkv[:, 0], qkv[:, 1], pos, wl.rotary_dim, wl.theta, None,
+                                "vision_2d")
+    torch.cuda.synchronize()
+    assert torch.equal(q, fq.transpose(0, 1)) and torch.equal(k, fk.transpose(0, 1))
+    assert torch.equal(v, qkv[:, 2].transpose(0, 1))
+
+
+@pytest.mark.parametrize("name", list(W.VISION_QKV_WORKLOADS))
+def test_vision_qkv_full_size_sampled(M, name):
+    wl = W.VISION_QKV_WORKLOADS[name]
+    inp = W.make_vision_qkv_inputs(wl)
+    note(f"vision_qkv full {name} n={wl.T}")
+    gq, gk, gv = _run(M, inp["qkv"], inp["pos"], wl.dtype, wl.rotary_dim, wl.theta)
+    rng = np.random.default_rng(73)
+    rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 160, replace=False)]))
+    oq, ok, ov = O.vision_qkv(inp["qkv"][rows], inp["pos"][:, rows], rotary_dim=wl.rotary_dim,
+                              theta=wl.theta, dtype=wl.dtype)
+    assert_close(gq[:, rows], oq, wl.dtype, f"{name} q sampled")
+    assert_close(gk[:, rows], ok, wl.dtype, f"{name} k sampled")
+    assert np.array_equal(gv.view(np.uint8), inp["qkv"][:, 2].transpose(1, 0, 2).view(np.uint8))
+
+
+def test_vision_qkv_empty(M):
+    import torch
+    qkv = torch.empty((0, 3, 16, 72), dtype=torch.float32, device="cuda")
+    q, k, v = M.vision_qkv(qkv, torch.empty((2, 0), dtype=torch.int32, device="cuda"), 72, 1e4)
+    torch.cuda.synchronize()
+    assert q.shape == (16, 0, 72)

@@ -43,7 +43,7 @@ def plan(T, D, rd, es, fused=True, wave_tokens=WAVE_TOKENS, heads=(1, 1), min_wa
     nt_cap = max(1, min(16, 512 // half)) if half else 16
     nt = max(1, min(nt_cap, wave_tokens))
     tiles = -(-T // nt)
-    tile_steps = -(-nt * heads[0] // rpw) + -(-nt * heads[1] // rpw)
+    tile_steps = sum(-(-nt * H // rpw) for H in heads)
     parts = max(1, min(tile_steps, -(-min_waves // tiles)))
     return dict(v=v, half=half, lpr=lpr, rpw=rpw, lrot=lrot, nt=nt, nwaves=tiles * parts,
                 parts=parts, lds_doubles=2 * nt * half if fused else 0)
@@ -59,8 +59,11 @@ def first_row_split(r, H):
     return tl, r - tl * H
 
 
-def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_waves=MIN_WAVES):
-    """Returns per-slot write counts of q/k outputs; asserts read bounds."""
+def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_waves=MIN_WAVES,
+             head_major=False):
+    """Returns per-slot write counts of the outputs (q, k and, with three
+    head counts, the copied v of a packed qkv); asserts read and write
+    bounds.  head_major puts the outputs in per-head planes."""
     p = plan(T, D, rd, es, fused=fused, wave_tokens=wave_tokens, heads=heads,
              min_waves=min_waves)
     v, half, lpr, rpw, lrot, nt = p["v"], p["half"], p["lpr"], p["rpw"], p["lrot"], p["nt"]
@@ -74,6 +77,12 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
     col_b = np.where(l < lrot, half + l * v, rd + (lpr - lrot + (l - lrot)) * v)
     assert np.all(col_a + v <= D) and np.all(col_b + v <= D)
     xts = [H * D + 8 * v for H in heads]          # a token stride wider than the rows
+    if head_major:
+        yts = [D for H in heads]
+        yhs = [T * D + 4 * v for H in heads]       # planes with a gap between them
+    else:
+        yts = [H * D + 4 * v for H in heads]
+        yhs = [D for H in heads]
     for w in range(p["nwaves"]):
         tile, part = divmod(w, parts)
         t0 = tile * nt
@@ -81,18 +90,21 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
         ntok = min(nt, T - t0)
         if fused:
             assert ntok * half <= p["lds_doubles"] // 2
-        steps_q = -(-ntok * heads[0] // rpw)
-        steps_all = steps_q + -(-ntok * heads[1] // rpw)
+        pre = [0]
+        for H in heads:
+            pre.append(pre[-1] + -(-ntok * H // rpw))
+        steps_all = pre[-1]
         sb, se = steps_all * part // parts, steps_all * (part + 1) // parts
         for s, H in enumerate(heads):
             if H == 0:
                 continue
-            lo = sb if s == 0 else max(sb, steps_q) - steps_q
-            hi = min(se, steps_q) if s == 0 else se - steps_q
+            lo = max(sb, pre[s]) - pre[s]
+            hi = min(se, pre[s + 1]) - pre[s]
             if lo >= hi:
                 continue
             extent = ((ntok - 1) * xts[s] + H * D) * es   # tile buffer size in bytes
-            assert extent < OUT_OF_RANGE
+            out_extent = ((ntok - 1) * yts[s] + (H - 1) * yhs[s] + D) * es
+            assert extent < OUT_OF_RANGE and out_extent < OUT_OF_RANGE
             nrows = ntok * H
             split = [first_row_split(int(lo * rpw + g), H) for g in grp]
             tl = np.array([a for a, _ in split])
@@ -101,6 +113,9 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
             xo = (tl * xts[s] + h * D) * es
             xinc = (dq * xts[s] + dr * D) * es
             xwrap = (xts[s] - H * D) * es
+            yo = (tl * yts[s] + h * yhs[s]) * es
+            yinc = (dq * yts[s] + dr * yhs[s]) * es
+            ywrap = (yts[s] - H * yhs[s]) * es
             full = (hi - lo) // U
             batches = [U] * full + [1] * ((hi - lo) - full * U)
             r0 = lo * rpw
@@ -113,6 +128,12 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
                     # live rows stay inside the tile buffer, masked ones outside it
                     assert np.all(off[ok] + col_b[ok] * es + v * es <= extent)
                     assert np.all(off[~ok] >= extent)
+                    yoff = np.where(ok, yo, OUT_OF_RANGE)
+                    assert np.all(yoff[ok] + col_b[ok] * es + v * es <= out_extent)
+                    assert np.all(yoff[ok] >= 0)
+                    assert np.all(yoff[~ok] >= out_extent)
+                    # the store address is the element (t, h, col) of the view
+                    assert np.all(yoff[ok] == (tl[ok] * yts[s] + h[ok] * yhs[s]) * es)
                     tlr = np.where(ok, tl, 0)
                     if fused:
                         o = tlr * half + col_a
@@ -122,12 +143,14 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
                         writes[s][tok, h[i], col_a[i]:col_a[i] + v] += 1
                         writes[s][tok, h[i], col_b[i]:col_b[i] + v] += 1
                     xo = xo + xinc
+                    yo = yo + yinc
                     h = h + dr
                     tl = tl + dq
                     wrap = h >= H
                     h = np.where(wrap, h - H, h)
                     tl = np.where(wrap, tl + 1, tl)
                     xo = np.where(wrap, xo + xwrap, xo)
+                    yo = np.where(wrap, yo + ywrap, yo)
                 r0 += uu * rpw
     return writes, p
 
@@ -196,3 +219,19 @@ def test_full_size_plans():
         assert p["lds_doubles"] * WPB * 8 <= 32 * 1024
         if wl.T >= MIN_WAVES:
             assert p["parts"] == 1
+
+
+@pytest.mark.parametrize("head_major", [False, True])
+@pytest.mark.parametrize("T,heads,D,rd,es,min_waves", [
+    (777, (16, 16, 16), 72, 72, 4, 2048),    # vision packed qkv, fp32
+    (777, (16, 16, 16), 72, 72, 2, 2048),    # bf16
+    (300, (6, 6, 6), 128, 64, 2, 2048),
+    (129, (5, 5, 5), 80, 80, 4, 1),
+    (1, (4, 4, 4), 72, 72, 2, 2048),
+    (50, (16, 16, 0), 72, 72, 4, 2048),      # without v
+])
+def test_three_slot_packed_qkv(T, heads, D, rd, es, min_waves, head_major):
+    writes, p = simulate(T, heads, D, rd, es, min_waves=min_waves, head_major=head_major)
+    for s, H in enumerate(heads):
+        if H:
+            assert np.all(writes[s] == 1), (s, np.unique(writes[s]))

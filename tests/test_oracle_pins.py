@@ -709,3 +709,55 @@ def test_decode_equals_prefill_on_the_same_positions():
     untouched = np.ones((B, cap), bool)
     untouched[0, 0:2] = untouched[1, 5:7] = untouched[2, 11] = False
     assert np.array_equal(newc[untouched], cache[untouched])
+
+
+# ---------------------------------------------------------------------------
+# Vision tower: packed qkv to per-head planes
+# ---------------------------------------------------------------------------
+
+def _vision_case(dtype="f32", n=40, H=3, D=16, seed=44):
+    rng = np.random.default_rng(seed)
+    qkv = O.encode(rng.standard_normal((n, 3, H, D)), dtype)
+    pos = np.stack([rng.integers(0, 30, n), rng.integers(0, 30, n)]).astype(np.int32)
+    return qkv, pos
+
+
+def test_vision_qkv_planes_are_the_rotated_heads_and_a_copied_v():
+    qkv, pos = _vision_case()
+    n, _, H, D = qkv.shape
+    q, k, v = O.vision_qkv(qkv, pos, rotary_dim=D, theta=1e4)
+    assert q.shape == k.shape == v.shape == (H, n, D)
+    # v: the plane of head h is the v slot of head h, bit for bit
+    assert np.array_equal(v, qkv[:, 2].transpose(1, 0, 2))
+    # q, k: each plane row is a rotation of its own head's slot: pair norms
+    # (j, j + D/2) are kept, and slot 0 / slot 1 are not mixed up
+    for plane, slot in ((q, 0), (k, 1)):
+        src = qkv[:, slot].transpose(1, 0, 2).astype(np.float64)
+        out = plane.astype(np.float64)
+        h = D // 2
+        n_in = src[..., :h] ** 2 + src[..., h:] ** 2
+        n_out = out[..., :h] ** 2 + out[..., h:] ** 2
+        assert np.max(np.abs(n_in - n_out) / (n_in + 1e-30)) < 1e-6
+    # a patch at (0, 0) is not rotated
+    pos0 = pos.copy()
+    pos0[:, 0] = 0
+    q0, _, _ = O.vision_qkv(qkv, pos0, rotary_dim=D, theta=1e4)
+    assert np.array_equal(q0[:, 0], qkv[0, 0])
+
+
+def test_vision_qkv_relative_positions_per_head():
+    """Per head, q.k after rotation depends only on the 2-D offset between
+    the two patches (the vision rotary is a relative encoding on both axes)."""
+    rng = np.random.default_rng(45)
+    H, D = 2, 16
+    qkv = rng.standard_normal((2, 3, H, D)).astype(np.float32)
+    def score(pa, pb):
+        q, _, _ = O.vision_qkv(qkv[:1], np.array(pa, dtype=np.int32).reshape(2, 1),
+                               rotary_dim=D, theta=1e4)
+        _, k, _ = O.vision_qkv(qkv[1:], np.array(pb, dtype=np.int32).reshape(2, 1),
+                               rotary_dim=D, theta=1e4)
+        return (q[:, 0].astype(np.float64) * k[:, 0].astype(np.float64)).sum(-1)
+    base = score((3, 5), (7, 2))
+    moved = score((3 + 4, 5 + 9), (7 + 4, 2 + 9))
+    assert np.max(np.abs(moved - base)) < 1e-4 * (1 + np.max(np.abs(base)))
+    assert np.max(np.abs(score((4, 5), (7, 2)) - base)) > 1e-3

@@ -17,7 +17,7 @@ from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, PRECISIONS, MropeError, check
                    float_array, int_array, load)
 
 __all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "rms_norm",
-           "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "rope_index",
+           "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "vision_qkv", "rope_index",
            "vision_pos_ids", "MropeError", "load"]
 
 
@@ -198,6 +198,36 @@ def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: in
         _heads_view(q_out, "q_out"),
         _ptr(k_cache), k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _stream(q)))
     return q_out
+
+
+def vision_qkv(qkv, pos, rotary_dim: int, theta: float, q_out=None, k_out=None, v_out=None,
+               precision="exact", head_major: bool = True, with_v: bool = True):
+    """Vision rotary on a packed qkv [n, 3, heads, D] (token stride free, the
+    rest contiguous): q and k rotated with the 2-D (row, col) positions pos
+    int32 [2, n], v copied.  Outputs are per-head planes [heads, n, D] (or
+    token-major [n, heads, D] with head_major=False)."""
+    torch = _torch()
+    if qkv.dim() != 4 or qkv.shape[1] != 3:
+        raise MropeError(_lib.MROPE_EINVAL, "qkv must be [n, 3, heads, D]")
+    n, _, H, D = qkv.shape
+    if n > 0 and (qkv.stride(3) != 1 or qkv.stride(2) != D or qkv.stride(1) != H * D):
+        raise MropeError(_lib.MROPE_EINVAL, "qkv must be contiguous within a token")
+    shape = (H, n, D) if head_major else (n, H, D)
+    q_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device) if q_out is None else q_out
+    k_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device) if k_out is None else k_out
+    if with_v and v_out is None:
+        v_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    for t in (q_out, k_out) + ((v_out,) if with_v else ()):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise MropeError(_lib.MROPE_EINVAL, f"outputs must be contiguous {shape}")
+    hs, ts = (n * D, D) if head_major else (D, H * D)
+    if pos.dtype != torch.int32 or (n > 0 and pos.stride(1) != 1):
+        raise MropeError(_lib.MROPE_EINVAL, "positions must be int32, contiguous along n")
+    check(load().mrope_vision_qkv(
+        _ptr(qkv), qkv.stride(0) if n > 0 else 3 * H * D, n, H, D, int(rotary_dim), _ptr(pos),
+        pos.stride(0) if n > 0 else n, float(theta), _dtype_code(qkv), _precision_code(precision),
+        _ptr(q_out), _ptr(k_out), _ptr(v_out) if with_v else None, hs, ts, _stream(qkv)))
+    return q_out, k_out, (v_out if with_v else None)
 
 
 def _int32_device(t, name, shape_len):

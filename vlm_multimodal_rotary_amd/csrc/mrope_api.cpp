@@ -169,17 +169,35 @@ int pick_vec(int dtype, int D, int rd, const void* const* ptrs, int nptrs,
   return 0;
 }
 
+// Up to three tensors (q, k, and the v of a packed qkv that is only copied).
+// Inputs have contiguous heads (head stride D); outputs have a head stride
+// (0 = D, token-major rows).
+constexpr int kSlots = mrope::kSlots;
+
 struct QKArgs {
-  const void* x[2];
-  int64_t x_ts[2];
-  int heads[2];
-  void* y[2];
-  int64_t y_ts[2];
-  const void* w[2];
+  const void* x[kSlots];
+  int64_t x_ts[kSlots];
+  int heads[kSlots];
+  void* y[kSlots];
+  int64_t y_ts[kSlots];
+  int64_t y_hs[kSlots];
+  const void* w[kSlots];
   int64_t T;
   int D, rd, dtype;
   int precision;  // MROPE_PRECISION_*; EXACT for RMSNorm only
 };
+
+int64_t head_stride(const QKArgs& a, int s) { return a.y_hs[s] != 0 ? a.y_hs[s] : a.D; }
+
+// Byte extent of an output [T][H][D] view with token and head strides.
+Extent out_extent(const QKArgs& a, int s, int es) {
+  Extent e;
+  if (a.y[s] == nullptr || a.T <= 0 || a.heads[s] <= 0) return e;
+  e.lo = reinterpret_cast<uintptr_t>(a.y[s]);
+  e.hi = e.lo + (uintptr_t)(((a.T - 1) * a.y_ts[s] + (int64_t)(a.heads[s] - 1) * head_stride(a, s) +
+                             a.D) * es);
+  return e;
+}
 
 int check_qk_tensors(const QKArgs& a, bool need_rd) {
   int rc = check_dtype(a.dtype);
@@ -196,8 +214,8 @@ int check_qk_tensors(const QKArgs& a, bool need_rd) {
     if (a.rd > MROPE_MAX_ROTARY_DIM)
       return fail(MROPE_EUNSUPPORTED, "rotary_dim = %d exceeds %d", a.rd, MROPE_MAX_ROTARY_DIM);
   }
-  const char* nm[2] = {"q", "k"};
-  for (int s = 0; s < 2; ++s) {
+  const char* nm[kSlots] = {"q", "k", "v"};
+  for (int s = 0; s < kSlots; ++s) {
     if (a.heads[s] < 0) return fail(MROPE_EINVAL, "%s heads = %d is negative", nm[s], a.heads[s]);
     if (a.heads[s] == 0 || a.T == 0) continue;
     if (a.x[s] == nullptr) return fail(MROPE_EINVAL, "%s input is NULL", nm[s]);
@@ -206,33 +224,42 @@ int check_qk_tensors(const QKArgs& a, bool need_rd) {
     if (a.x_ts[s] < row)
       return fail(MROPE_EINVAL, "%s token stride %lld < heads*D = %lld", nm[s],
                   (long long)a.x_ts[s], (long long)row);
-    if (a.y_ts[s] < row)
-      return fail(MROPE_EINVAL, "%s output token stride %lld < heads*D = %lld", nm[s],
-                  (long long)a.y_ts[s], (long long)row);
+    // output rows must not overlap one another: heads inside tokens
+    // (token-major) or tokens inside heads (head-major planes)
+    const int64_t hs = head_stride(a, s);
+    const bool token_major = hs >= a.D && a.y_ts[s] >= (int64_t)a.heads[s] * hs;
+    const bool head_major = a.y_ts[s] >= a.D && (a.heads[s] == 1 || hs >= a.T * a.y_ts[s]);
+    if (!token_major && !head_major)
+      return fail(MROPE_EINVAL, "%s output strides (token %lld, head %lld) overlap rows of "
+                  "heads*D = %lld", nm[s], (long long)a.y_ts[s], (long long)hs, (long long)row);
   }
   // Overlap rules.
   const int es = elem_bytes_of(a.dtype);
-  Extent xin[2], yout[2];
-  for (int s = 0; s < 2; ++s) {
+  Extent xin[kSlots], yout[kSlots];
+  for (int s = 0; s < kSlots; ++s) {
     const bool live = a.heads[s] > 0 && a.T > 0;
     const int64_t row = (int64_t)a.heads[s] * a.D;
     if (live) {
       xin[s] = extent_of(a.x[s], a.T, a.x_ts[s], row, es);
-      yout[s] = extent_of(a.y[s], a.T, a.y_ts[s], row, es);
+      yout[s] = out_extent(a, s, es);
     }
   }
-  for (int s = 0; s < 2; ++s) {
-    const bool same = a.x[s] == a.y[s] && a.x_ts[s] == a.y_ts[s];
+  for (int s = 0; s < kSlots; ++s) {
+    const bool same = a.x[s] == a.y[s] && a.x_ts[s] == a.y_ts[s] && head_stride(a, s) == a.D;
     if (bad_alias(yout[s], xin[s], same))
       return fail(MROPE_EINVAL, "%s output partially overlaps its input", nm[s]);
-    if (overlaps(yout[s], xin[1 - s]))
-      return fail(MROPE_EINVAL, "%s output overlaps the %s input", nm[s], nm[1 - s]);
+    for (int o = 0; o < kSlots; ++o) {
+      if (o == s) continue;
+      if (overlaps(yout[s], xin[o]))
+        return fail(MROPE_EINVAL, "%s output overlaps the %s input", nm[s], nm[o]);
+      if (o > s && overlaps(yout[s], yout[o]))
+        return fail(MROPE_EINVAL, "%s and %s outputs overlap", nm[s], nm[o]);
+    }
   }
-  if (overlaps(yout[0], yout[1])) return fail(MROPE_EINVAL, "q and k outputs overlap");
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kSlots; ++s) {
     if (a.w[s] == nullptr) continue;
     Extent we = extent_of(a.w[s], 1, a.D, a.D, es);
-    for (int o = 0; o < 2; ++o)
+    for (int o = 0; o < kSlots; ++o)
       if (overlaps(yout[o], we)) return fail(MROPE_EINVAL, "an output overlaps a weight vector");
   }
   return MROPE_OK;
@@ -252,28 +279,29 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
            int64_t cs_ts, float eps, void* stream, const Extent* extra, int n_extra,
            const DecodeArgs* dec = nullptr) {
   const int es = elem_bytes_of(a.dtype);
-  const void* ptrs[6] = {a.x[0], a.x[1], a.y[0], a.y[1], a.w[0], a.w[1]};
-  int64_t strides[6] = {a.x_ts[0], a.x_ts[1], a.y_ts[0], a.y_ts[1],
-                        dec ? dec->kc_seq : 0, dec ? dec->kc_tok : 0};
-  const int v = pick_vec(a.dtype, a.D, a.rd, ptrs, 6, strides, 6);
+  const void* ptrs[9] = {a.x[0], a.x[1], a.x[2], a.y[0], a.y[1], a.y[2], a.w[0], a.w[1], a.w[2]};
+  int64_t strides[11] = {a.x_ts[0], a.x_ts[1], a.x_ts[2], a.y_ts[0], a.y_ts[1], a.y_ts[2],
+                         head_stride(a, 0), head_stride(a, 1), head_stride(a, 2),
+                         dec ? dec->kc_seq : 0, dec ? dec->kc_tok : 0};
+  const int v = pick_vec(a.dtype, a.D, a.rd, ptrs, 9, strides, 11);
   if (v == 0)
     return fail(MROPE_EUNSUPPORTED,
                 "no vector width fits D = %d, rotary_dim = %d and the buffer alignment "
                 "(need element-aligned pointers and D/2 lanes or fewer per row)",
                 a.D, a.rd);
   for (int i = 0; i < n_extra; ++i)
-    for (int o = 0; o < 2; ++o)
-      if (a.heads[o] > 0 &&
-          overlaps(extent_of(a.y[o], a.T, a.y_ts[o], (int64_t)a.heads[o] * a.D, es), extra[i]))
+    for (int o = 0; o < kSlots; ++o)
+      if (overlaps(out_extent(a, o, es), extra[i]))
         return fail(MROPE_EINVAL, "an output overlaps a positions or cos/sin buffer");
-  if (a.T == 0 || a.heads[0] + a.heads[1] == 0) return ok();
+  if (a.T == 0 || a.heads[0] + a.heads[1] + a.heads[2] == 0) return ok();
 
   mrope::QKParams p;
   std::memset(&p, 0, sizeof(p));
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kSlots; ++s) {
     p.x[s] = a.x[s];
     p.y[s] = a.y[s];
     p.w[s] = a.w[s];
+    p.y_hs[s] = head_stride(a, s);
     p.x_ts[s] = a.x_ts[s];
     p.y_ts[s] = a.y_ts[s];
     p.heads[s] = a.heads[s];
@@ -308,15 +336,18 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   if (nt_cap > 16) nt_cap = 16;
   // The kernels address a tile of each tensor through a buffer descriptor
   // with 32-bit byte offsets: a tile's extent must stay below 2^31 bytes.
-  for (int s = 0; s < 2; ++s) {
+  const int64_t limit = int64_t(1) << 31;
+  for (int s = 0; s < kSlots; ++s) {
     if (a.heads[s] == 0) continue;
-    const int64_t row = (int64_t)a.heads[s] * a.D;
-    for (const int64_t ts : {a.x_ts[s], a.y_ts[s]}) {
-      while (nt_cap > 1 && ((int64_t)(nt_cap - 1) * ts + row) * es >= (int64_t(1) << 31)) --nt_cap;
-      if ((ts + row) * es >= (int64_t(1) << 31))
-        return fail(MROPE_EUNSUPPORTED, "a token stride of %lld elements is too large",
-                    (long long)ts);
-    }
+    const int64_t H = a.heads[s];
+    auto in_ext = [&](int64_t nt) { return ((nt - 1) * a.x_ts[s] + H * a.D) * es; };
+    auto out_ext = [&](int64_t nt) {
+      return ((nt - 1) * a.y_ts[s] + (H - 1) * head_stride(a, s) + a.D) * es;
+    };
+    while (nt_cap > 1 && (in_ext(nt_cap) >= limit || out_ext(nt_cap) >= limit)) --nt_cap;
+    if (in_ext(1) >= limit || out_ext(1) >= limit)
+      return fail(MROPE_EUNSUPPORTED, "one token's rows of %s span 2^31 bytes or more",
+                  s == 0 ? "q" : (s == 1 ? "k" : "v"));
   }
   // For binary32 tensors the cast of cos/sin to the dtype is the identity.
   const int prec = (a.dtype == MROPE_DTYPE_F32 && a.precision == MROPE_PRECISION_FP32)
@@ -367,6 +398,49 @@ Extent bytes_at(const void* base, int64_t n, int elem_bytes) {
 }  // namespace
 
 extern "C" {
+
+int mrope_vision_qkv(const void* qkv, int64_t qkv_tok_stride, int64_t n, int heads, int D,
+                     int rotary_dim, const int32_t* pos, int64_t pos_axis_stride, double theta,
+                     int dtype, int precision, void* q_out, void* k_out, void* v_out,
+                     int64_t out_head_stride, int64_t out_tok_stride, void* stream) {
+  if (heads < 0) return fail(MROPE_EINVAL, "heads = %d is negative", heads);
+  QKArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const int es = elem_bytes_of(dtype);
+  const int64_t plane = (int64_t)heads * D;
+  if (qkv_tok_stride < 3 * plane)
+    return fail(MROPE_EINVAL, "qkv token stride %lld < 3*heads*D = %lld",
+                (long long)qkv_tok_stride, (long long)(3 * plane));
+  void* outs[3] = {q_out, k_out, v_out};
+  for (int s = 0; s < 3; ++s) {
+    a.x[s] = qkv == nullptr ? nullptr : static_cast<const char*>(qkv) + s * plane * es;
+    a.x_ts[s] = qkv_tok_stride;
+    a.heads[s] = (s == 2 && v_out == nullptr) ? 0 : heads;
+    a.y[s] = outs[s];
+    a.y_ts[s] = out_tok_stride;
+    a.y_hs[s] = out_head_stride;
+  }
+  if (n > 0 && (out_head_stride <= 0 || out_tok_stride <= 0))
+    return fail(MROPE_EINVAL, "output strides must be positive");
+  a.T = n;
+  a.D = D;
+  a.rd = rotary_dim;
+  a.dtype = dtype;
+  a.precision = precision;
+  int rc = check_qk_tensors(a, true);
+  if (rc) return rc;
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(MROPE_EINVAL, "theta must be positive and finite");
+  mrope::ColTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  rc = build_table(rotary_dim, theta, nullptr, 0, MROPE_LAYOUT_VISION_2D, nullptr, tab);
+  if (rc) return rc;
+  if (pos_axis_stride < 0) return fail(MROPE_EINVAL, "pos_axis_stride is negative");
+  if (n > 0 && heads > 0 && pos == nullptr) return fail(MROPE_EINVAL, "pos is NULL");
+  Extent extra[1] = {extent_of(pos, 2, pos_axis_stride, n, 4)};
+  return run_qk(a, mrope::kCsFromPositions, false, tab, pos, pos_axis_stride, nullptr, nullptr, 0,
+                0.0f, stream, extra, 1);
+}
 
 size_t mrope_rope_index_workspace_size(int batch, int64_t seq_len, int n_images, int n_videos) {
   RopeWs w;

@@ -30,15 +30,20 @@ enum CsMode : int {
                          // k written to a KV cache (one token per wavefront)
 };
 
-// One launch processes up to two tensors (slot 0 = q, slot 1 = k) that share
-// T, D, rotary_dim and the per-token cos/sin.
+// One launch processes up to three tensors (slot 0 = q, slot 1 = k, slot 2 =
+// v of a packed qkv, copied only) that share T, D, rotary_dim and the
+// per-token cos/sin.  Inputs have contiguous heads; outputs have a head
+// stride (D for token-major rows, T*D for head-major planes).
+constexpr int kSlots = 3;
+
 struct QKParams {
-  const void* x[2];
-  void* y[2];
-  const void* w[2];      // RMSNorm weights (dtype of x) or null
-  int64_t x_ts[2];       // token strides, elements
-  int64_t y_ts[2];
-  int heads[2];
+  const void* x[kSlots];
+  void* y[kSlots];
+  const void* w[kSlots];   // RMSNorm weights (dtype of x) or null
+  int64_t x_ts[kSlots];    // token strides, elements
+  int64_t y_ts[kSlots];
+  int64_t y_hs[kSlots];    // output head strides, elements
+  int heads[kSlots];
   int64_t T;
   int D;
   int rd;                // rotary dim (0 for RMSNorm only)
@@ -48,8 +53,8 @@ struct QKParams {
   int lrot;              // rotary lanes per row: half / V
   int nt;                // tokens per tile (set by the launcher)
   int parts;             // wavefronts per tile (set by the launcher)
-  int dq[2], dr[2];      // rpw = dq * heads + dr, per tensor (launcher)
-  float inv_heads[2];    // 1 / heads, per tensor (launcher)
+  int dq[kSlots], dr[kSlots];   // rpw = dq * heads + dr, per tensor (launcher)
+  float inv_heads[kSlots];      // 1 / heads, per tensor (launcher)
   const int32_t* pos;
   int64_t pos_stride;
   const float* cos;

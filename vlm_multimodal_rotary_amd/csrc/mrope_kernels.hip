@@ -373,6 +373,12 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
   }
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
+    if constexpr (CS == kCsNone && !NORM) {
+      // plain copy: the loaded words go back out unchanged
+      buf_store<BF16, CB>(st.ry, you[u] + ca, ra[u]);
+      buf_store<BF16, CB>(st.ry, you[u] + cb, rb[u]);
+      continue;
+    }
     float a[V], b[V];
     unpack<BF16, V>(ra[u], a);
     unpack<BF16, V>(rb[u], b);
@@ -489,7 +495,8 @@ qk_kernel(const QKParams p, const ColTable tab) {
   const uint32_t cb = (uint32_t)(col_b * ES);
 
   // This wavefront's tile (tokens [t0, t0 + ntok)) and its part of the
-  // tile's row-steps (q steps first, then k steps), p.parts parts per tile.
+  // tile's row-steps (q steps, then k steps, then v steps), p.parts parts per
+  // tile.
   const uint32_t wave = blockIdx.x * (uint32_t)kWavesPerBlock + (uint32_t)wib;
   // Large launches have one part per tile; the divisions are skipped there.
   const bool split = p.parts > 1;
@@ -498,8 +505,11 @@ qk_kernel(const QKParams p, const ColTable tab) {
   const int64_t t0 = (int64_t)tile * p.nt;
   if (t0 >= p.T) return;
   const int ntok = (int)((p.T - t0) < p.nt ? (p.T - t0) : p.nt);
-  const int steps_q = (ntok * p.heads[0] + rpw - 1) / rpw;
-  const int steps_all = steps_q + (ntok * p.heads[1] + rpw - 1) / rpw;
+  int pre[kSlots + 1];   // first step of each tensor
+  pre[0] = 0;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) pre[s + 1] = pre[s] + (ntok * p.heads[s] + rpw - 1) / rpw;
+  const int steps_all = pre[kSlots];
   const int step_begin = split ? steps_all * part / p.parts : 0;
   const int step_end = split ? steps_all * (part + 1) / p.parts : steps_all;
   {
@@ -541,21 +551,22 @@ qk_kernel(const QKParams p, const ColTable tab) {
     }
 
 #pragma unroll 1
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
       const int H = p.heads[s];
       if (H == 0) continue;
       // This part's steps of tensor s.
-      const int lo = s == 0 ? step_begin : (step_begin > steps_q ? step_begin : steps_q) - steps_q;
-      const int hi = s == 0 ? (step_end < steps_q ? step_end : steps_q) : step_end - steps_q;
+      const int lo = (step_begin > pre[s] ? step_begin : pre[s]) - pre[s];
+      const int hi = (step_end < pre[s + 1] ? step_end : pre[s + 1]) - pre[s];
       if (lo >= hi) continue;
       const int64_t xts = p.x_ts[s];
       const int64_t yts = p.y_ts[s];
+      const int64_t yhs = p.y_hs[s];
       SlotState<CB> st;
       // Tile-local buffers: byte offsets below stay within 32 bits.
       st.rx = buffer_of(static_cast<const char*>(p.x[s]) + t0 * xts * ES,
                         (uint32_t)(((int64_t)(ntok - 1) * xts + (int64_t)H * p.D) * ES));
       st.ry = buffer_of(static_cast<const char*>(p.y[s]) + t0 * yts * ES,
-                        (uint32_t)(((int64_t)(ntok - 1) * yts + (int64_t)H * p.D) * ES));
+                        (uint32_t)(((int64_t)(ntok - 1) * yts + (int64_t)(H - 1) * yhs + p.D) * ES));
       if constexpr (CS == kCsDecode) {
         if (s == 1) {
           // Rotated k goes to its cache row; a row outside [0, capacity) gets
@@ -578,11 +589,29 @@ qk_kernel(const QKParams p, const ColTable tab) {
       if ((st.tl + 1) * H <= r_first) ++st.tl;
       st.h = r_first - st.tl * H;
       st.xo = (uint32_t)(((int64_t)st.tl * xts + (int64_t)st.h * p.D) * ES);
-      st.yo = (uint32_t)(((int64_t)st.tl * yts + (int64_t)st.h * p.D) * ES);
+      st.yo = (uint32_t)(((int64_t)st.tl * yts + (int64_t)st.h * yhs) * ES);
       st.xinc = (uint32_t)(((int64_t)st.dq * xts + (int64_t)st.dr * p.D) * ES);
-      st.yinc = (uint32_t)(((int64_t)st.dq * yts + (int64_t)st.dr * p.D) * ES);
+      st.yinc = (uint32_t)(((int64_t)st.dq * yts + (int64_t)st.dr * yhs) * ES);
       st.xwrap = (uint32_t)((xts - (int64_t)H * p.D) * ES);
-      st.ywrap = (uint32_t)((yts - (int64_t)H * p.D) * ES);
+      st.ywrap = (uint32_t)((yts - (int64_t)H * yhs) * ES);
+
+      // The third tensor (v of a packed qkv) is copied: no norm, no rotation.
+      if constexpr (CS == kCsFromPositions) {
+        if (s == 2) {
+          const float none[V] = {};
+          const int full = (hi - lo) / U;
+          int r0 = lo * rpw;
+          for (int g = 0; g < full; ++g, r0 += U * rpw)
+            process_steps<BF16, V, kCsNone, false, LPR, PREC, U>(st, r0, p, grp, rpw, lpr,
+                                                                 lane_on, false, ca, cb, col_a,
+                                                                 none, none, lc, ls, t0);
+          for (; r0 < hi * rpw; r0 += rpw)
+            process_steps<BF16, V, kCsNone, false, LPR, PREC, 1>(st, r0, p, grp, rpw, lpr,
+                                                                 lane_on, false, ca, cb, col_a,
+                                                                 none, none, lc, ls, t0);
+          continue;
+        }
+      }
 
       float wa[V], wb[V];
       if constexpr (NORM) {
@@ -628,7 +657,7 @@ int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
   p.nt = nt_cap < MROPE_WAVE_TOKENS ? nt_cap : MROPE_WAVE_TOKENS;
   if (p.nt < 1 || CS == kCsDecode) p.nt = 1;
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kSlots; ++s) {
     const int H = p.heads[s] > 0 ? p.heads[s] : 1;
     p.dq[s] = p.rpw / H;
     p.dr[s] = p.rpw - p.dq[s] * H;
@@ -637,8 +666,8 @@ int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   // Small launches split each tile's row-steps over several wavefronts so
   // that about kMinWaves are in flight; large ones keep one per tile.
   const int64_t tiles = (p.T + p.nt - 1) / p.nt;
-  const int tile_steps = (p.nt * p.heads[0] + p.rpw - 1) / p.rpw +
-                         (p.nt * p.heads[1] + p.rpw - 1) / p.rpw;
+  int tile_steps = 0;
+  for (int s = 0; s < kSlots; ++s) tile_steps += (p.nt * p.heads[s] + p.rpw - 1) / p.rpw;
   int64_t parts = (kMinWaves + tiles - 1) / tiles;
   if (parts > tile_steps) parts = tile_steps;
   if (parts < 1) parts = 1;

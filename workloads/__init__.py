@@ -430,3 +430,58 @@ def mm_prompt_batch(wl: PositionWorkload | str, seed: int | None = None):
         images.append((1, 48, 64))
         videos.append((4, 32, 32))
     return types, mask, np.array(images, dtype=np.int32), np.array(videos, dtype=np.int32)
+
+
+@dataclasses.dataclass(frozen=True)
+class VisionQKVWorkload:
+    """Packed vision qkv [n, 3, heads, D] rotated into per-head planes."""
+    name: str
+    index: int
+    dtype: str
+    n_images: int
+    side: int             # patches per image side (before merging)
+    heads: int
+    D: int
+    rotary_dim: int
+    theta: float
+    description: str = ""
+
+    @property
+    def T(self) -> int:
+        return self.n_images * self.side * self.side
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self) -> int:
+        # read q, k, v of every patch once, write the three planes once,
+        # read the (row, col) positions
+        return 2 * self.T * 3 * self.heads * self.D * self.elem_bytes + 8 * self.T
+
+
+VISION_QKV_WORKLOADS = {
+    w.name: w for w in [
+        VisionQKVWorkload("vision_qkv_planes", 8, "f32", 8, 64, 16, 72, 72, 1e4,
+                          description="Vision tower packed qkv of 8 images x 64x64 patches, "
+                                      "16 heads x 72, to head-major planes (q, k rotated)"),
+        VisionQKVWorkload("vision_qkv_planes_bf16", 9, "bf16", 8, 64, 16, 72, 72, 1e4,
+                          description="The same in bfloat16"),
+    ]
+}
+
+
+def make_vision_qkv_inputs(wl: VisionQKVWorkload | str, n: int | None = None,
+                           seed: int | None = None) -> dict:
+    """Seeded packed qkv [n, 3, heads, D] (standard normal, stored in the
+    workload dtype) and the patches' (row, col) positions [2, n] in
+    merge-block order (the first n patches of the workload's images)."""
+    if isinstance(wl, str):
+        wl = VISION_QKV_WORKLOADS[wl]
+    n = wl.T if n is None else n
+    rng = np.random.default_rng(wl.index if seed is None else seed)
+    qkv = rng.standard_normal((n, 3, wl.heads, wl.D), dtype=np.float32)
+    pos = vision_patch_positions(wl.n_images, wl.side, wl.side)
+    reps = -(-n // pos.shape[1])
+    pos = np.tile(pos, (1, reps))[:, :n].astype(np.int32)
+    return dict(qkv=_store(qkv, wl.dtype), pos=np.ascontiguousarray(pos), T=n, workload=wl)
