@@ -194,6 +194,67 @@ def bench_positions(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_vision_qkv(args):
+    """One step = one mrope_vision_qkv call: packed qkv in, rotated q/k and
+    copied v in per-head planes out."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import vlm_multimodal_rotary_amd as M
+
+    wl = W.VISION_QKV_WORKLOADS[args.workload]
+    inp = W.make_vision_qkv_inputs(wl)
+    n = wl.T
+    flat = inp["qkv"].reshape(n, -1)
+    if wl.dtype == "bf16":
+        qkv = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        qkv = torch.from_numpy(flat).cuda()
+    qkv = qkv.reshape(n, 3, wl.heads, wl.D)
+    pos = torch.from_numpy(inp["pos"]).cuda()
+    shape = (wl.heads, n, wl.D)
+    qo, ko, vo = (torch.empty(shape, dtype=qkv.dtype, device="cuda") for _ in range(3))
+
+    def step():
+        M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta, q_out=qo, k_out=ko, v_out=vo,
+                     precision=args.precision)
+
+    ms, n_timed, warm, wall_ms = time_steps(step, args)
+    alg = wl.algorithmic_bytes()
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "vision patches/s, packed qkv to rotated head-major planes (mrope_vision_qkv)",
+        "value": n / (ms * 1e-3), "unit": "patches/s", "n_gpus": 1, "steps": n_timed,
+        "warmup": warm, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "graph_steps": args.graph, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded normal qkv, merge-block patch positions)",
+        "config": {"workload": wl.name, "patches": n, "heads": wl.heads, "D": wl.D,
+                   "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": "vision_2d",
+                   "output": "head-major planes", "precision": args.precision},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name)
+                     if args.precision == "exact" else None,
+                     "algorithmic_bytes": alg, "kernel": "qk_kernel (mrope_vision_qkv)"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mrope_oracle as O
+        chunk, done, t0 = 64, 0, 0
+        start = time.perf_counter()
+        while time.perf_counter() - start < 12.0:
+            sl = slice(t0, t0 + chunk)
+            O.vision_qkv(inp["qkv"][sl], inp["pos"][:, sl], rotary_dim=wl.rotary_dim,
+                         theta=wl.theta, dtype=wl.dtype, precision=args.precision)
+            done += chunk
+            t0 = (t0 + chunk) % (n - chunk + 1)
+        el = time.perf_counter() - start
+        line["cpu_baseline"] = {"value": done / el, "unit": "patches/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{done} patches ({done // chunk} windows of {chunk}), "
+                                          f"{el:.1f} s, one thread"}
+    print(json.dumps(line), flush=True)
+
+
 def copy_calib(nbytes: int, steps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -236,6 +297,9 @@ def main():
 
     if args.workload in W.POSITION_WORKLOADS:
         bench_positions(args)
+        return
+    if args.workload in W.VISION_QKV_WORKLOADS:
+        bench_vision_qkv(args)
         return
     decode = args.workload in W.DECODE_WORKLOADS
     wl = W.DECODE_WORKLOADS[args.workload] if decode else W.WORKLOADS[args.workload]

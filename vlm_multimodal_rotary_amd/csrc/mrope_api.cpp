@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -265,6 +266,27 @@ int check_qk_tensors(const QKArgs& a, bool need_rd) {
   return MROPE_OK;
 }
 
+// Resident wavefronts per SIMD for a launch (0 = as many as registers allow).
+// Measured on MI355X: per-head-plane outputs (many short scattered row
+// writes per wavefront) run best with few wavefronts -- 3 for 8-byte chunks,
+// 4 for 16-byte chunks; token-major launches with 16 lanes per head row or
+// more (D >= 256 bf16) gain a little from 5; everything else runs unbounded.
+// MROPE_WAVES_PER_SIMD in the environment overrides the choice (tuning).
+int waves_per_simd(const QKArgs& a, int v, int es) {
+  static const int env = [] {
+    const char* e = std::getenv("MROPE_WAVES_PER_SIMD");
+    return e != nullptr ? std::atoi(e) : -1;
+  }();
+  if (env >= 0) return env > 8 ? 8 : env;
+  bool planes = false;
+  for (int s = 0; s < kSlots; ++s)
+    if (a.heads[s] > 0 && head_stride(a, s) != a.D) planes = true;
+  const int chunk_bytes = v * es;
+  if (planes) return chunk_bytes < 16 ? 3 : 4;
+  if (a.D / (2 * v) >= 16 && chunk_bytes == 16 && es == 2) return 5;
+  return 0;
+}
+
 // Launch geometry and the remaining per-launch fields.
 struct DecodeArgs {
   const int32_t* cache_len = nullptr;
@@ -349,6 +371,7 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
       return fail(MROPE_EUNSUPPORTED, "one token's rows of %s span 2^31 bytes or more",
                   s == 0 ? "q" : (s == 1 ? "k" : "v"));
   }
+  p.waves_cap = waves_per_simd(a, v, es);
   // For binary32 tensors the cast of cos/sin to the dtype is the identity.
   const int prec = (a.dtype == MROPE_DTYPE_F32 && a.precision == MROPE_PRECISION_FP32)
                        ? MROPE_PRECISION_DTYPE : a.precision;

@@ -53,6 +53,7 @@ struct QKParams {
   int lrot;              // rotary lanes per row: half / V
   int nt;                // tokens per tile (set by the launcher)
   int parts;             // wavefronts per tile (set by the launcher)
+  int waves_cap;         // resident wavefronts per SIMD at most (0 = no bound)
   int dq[kSlots], dr[kSlots];   // rpw = dq * heads + dr, per tensor (launcher)
   float inv_heads[kSlots];      // 1 / heads, per tensor (launcher)
   const int32_t* pos;

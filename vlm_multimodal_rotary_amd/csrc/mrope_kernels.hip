@@ -38,6 +38,11 @@
 #define MROPE_ROWS_IN_FLIGHT_F32 4
 #endif
 // Non-temporal (streaming) hint on the row stores, by element type.
+// Row-steps in flight for chunks narrower than 16 bytes (e.g. bf16 with a
+// half head of 36: 8-byte chunks).
+#ifndef MROPE_ROWS_IN_FLIGHT_NARROW
+#define MROPE_ROWS_IN_FLIGHT_NARROW 2
+#endif
 #ifndef MROPE_NT_STORES_BF16
 #define MROPE_NT_STORES_BF16 1
 #endif
@@ -57,6 +62,7 @@ namespace mrope {
 namespace {
 
 constexpr int64_t kMinWaves = MROPE_MIN_WAVES;
+constexpr int kLdsPerCu = 160 * 1024;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -465,7 +471,8 @@ __global__ void __launch_bounds__(kBlockThreads)
 qk_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int CB = ES * V;
-  constexpr int U = BF16 ? MROPE_ROWS_IN_FLIGHT_BF16 : MROPE_ROWS_IN_FLIGHT_F32;
+  constexpr int U = CB < 16 ? MROPE_ROWS_IN_FLIGHT_NARROW
+                            : (BF16 ? MROPE_ROWS_IN_FLIGHT_BF16 : MROPE_ROWS_IN_FLIGHT_F32);
   typedef double cs_t;
   extern __shared__ double lds[];
 
@@ -674,7 +681,13 @@ int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   p.parts = (int)parts;
   const int64_t waves = tiles * parts;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(double) : 0;
+  int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(double) : 0;
+  if (p.waves_cap > 0) {
+    // Bound the resident wavefronts per SIMD: a block asks for enough LDS
+    // that at most waves_cap blocks of four wavefronts share a compute unit.
+    const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
+    if (cap_lds > lds) lds = cap_lds;
+  }
   hipLaunchKernelGGL((qk_kernel<BF16, V, CS, NORM, LPR, PREC>), dim3((unsigned)blocks),
                      dim3(kBlockThreads), lds, st, p, tab);
   return (int)hipGetLastError();
