@@ -132,6 +132,23 @@ def time_steps(step, args, stream=None):
     return ev0.elapsed_time(ev1) / n, n, done, wall * 1e3 / n
 
 
+def build_cache(M, dim: int, theta: float, rows: int):
+    """The cos/sin cache by position, built once; its build time (HIP events,
+    median of 5 builds) goes into the JSON line beside the step time."""
+    import torch
+    cache = M.mrope_cos_sin_cache(dim, theta, rows)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.mrope_cos_sin_cache(dim, theta, rows, out=cache)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return cache, {"rows": rows, "dim": dim, "bytes": rows * dim * 4,
+                   "build_ms": sorted(times)[2]}
+
+
 def bench_positions(args):
     """One step = one mrope_rope_index call (three kernels) over the batch."""
     import numpy as np
@@ -214,10 +231,14 @@ def bench_vision_qkv(args):
     pos = torch.from_numpy(inp["pos"]).cuda()
     shape = (wl.heads, n, wl.D)
     qo, ko, vo = (torch.empty(shape, dtype=qkv.dtype, device="cuda") for _ in range(3))
+    cache, cache_info = None, None
+    if args.cs_cache:
+        cache, cache_info = build_cache(M, wl.rotary_dim // 2, wl.theta,
+                                        int(inp["pos"].max()) + 1)
 
     def step():
         M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta, q_out=qo, k_out=ko, v_out=vo,
-                     precision=args.precision)
+                     precision=args.precision, cs_cache=cache)
 
     ms, n_timed, warm, wall_ms = time_steps(step, args)
     alg = wl.algorithmic_bytes()
@@ -231,10 +252,11 @@ def bench_vision_qkv(args):
         "data": "synthetic (seeded normal qkv, merge-block patch positions)",
         "config": {"workload": wl.name, "patches": n, "heads": wl.heads, "D": wl.D,
                    "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": "vision_2d",
-                   "output": "head-major planes", "precision": args.precision},
+                   "output": "head-major planes", "precision": args.precision,
+                   "cs_cache": cache_info},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name)
-                     if args.precision == "exact" else None,
+                     if args.precision == "exact" and not args.cs_cache else None,
                      "algorithmic_bytes": alg, "kernel": "qk_kernel (mrope_vision_qkv)"},
     }
     if not args.no_cpu_baseline:
@@ -273,6 +295,9 @@ def main():
     ap.add_argument("--min-warmup-s", type=float, default=0.5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cs-cache", action="store_true",
+                    help="gather cos/sin from a cache by position (built once before the timed "
+                         "steps; its build time is reported separately)")
     ap.add_argument("--precision", default="exact", choices=["exact", "dtype", "fp32"],
                     help="rotation rounding: exact (default), dtype (cos/sin cast to the "
                          "tensor dtype, bf16 tensor ops) or fp32 (fp32 tensor ops)")
@@ -326,11 +351,16 @@ def main():
     else:
         pos = dev(inp["pos"])
         k_out = torch.empty_like(k)
+        cache = None
+        if args.cs_cache:
+            rows = int(inp["pos"].max()) + 1
+            dim = wl.rotary_dim // 2 if wl.layout == "vision_2d" else wl.rotary_dim
+            cache, cache_info = build_cache(M, dim, wl.theta, rows)
 
         def step():
             M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
                                wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out,
-                               precision=args.precision)
+                               precision=args.precision, cs_cache=cache)
 
     ms, n_timed, done, wall_ms = time_steps(step, args)   # one kernel launch per step
 
@@ -371,6 +401,9 @@ def main():
                      "kernel": "qk_kernel (mrope_decode_qk)" if decode
                      else "qk_kernel (rmsnorm_mrope_qk)"},
     }
+    if not decode and args.cs_cache:
+        line["config"]["cs_cache"] = cache_info
+        line["roofline"]["traffic"] = None
     if not args.no_cpu_baseline and not decode:
         line["cpu_baseline"] = cpu_baseline(inp, wl, precision=args.precision)
     print(json.dumps(line), flush=True)

@@ -206,6 +206,41 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq,
                      void* stream);
 
 /*
+ * mrope_cos_sin_cache — a cos/sin table by position value ([RoPE] the
+ * "method 2" listing: the outer product of arange(max + 1) and inv_freq,
+ * gathered by position afterwards):
+ *   cache[2*(p*(dim/2) + i)]     = fl32(cos(fl32(float(p) * inv[i])))
+ *   cache[2*(p*(dim/2) + i) + 1] = fl32(sin(...)),   0 <= p < rows,
+ * with inv = mrope_inv_freq(dim, theta): the values mrope_cos_sin computes
+ * for position p, bit for bit.  dim = rotary_dim for the text layouts,
+ * rotary_dim/2 for the vision layout.  The table depends on (dim, theta,
+ * rows) only, so a model builds it once and reuses it for every layer.
+ *   cache: device binary32 [rows][dim/2][2], 8-byte aligned.
+ * EINVAL on dim odd, <= 0 or > MROPE_MAX_ROTARY_DIM, theta <= 0, rows < 0,
+ * NULL or misaligned cache.
+ */
+int mrope_cos_sin_cache(int dim, double theta, int rows, float* cache, void* stream);
+
+/*
+ * rmsnorm_mrope_qk_cached — rmsnorm_mrope_qk taking cos/sin from a cache by
+ * position (mrope_cos_sin_cache with the matching dim and theta, rows
+ * cache_rows) for positions in [0, cache_rows), and computing them as
+ * rmsnorm_mrope_qk does for any other position: the result is bit-identical
+ * to rmsnorm_mrope_qk whenever the cache was built with the same theta.
+ * cs_cache NULL (and cache_rows 0) is rmsnorm_mrope_qk.  The cache may not
+ * overlap an output.
+ */
+int rmsnorm_mrope_qk_cached(const void* q, int64_t q_tok_stride, int hq,
+                            const void* k, int64_t k_tok_stride, int hk,
+                            int64_t T, int D, int rotary_dim,
+                            const int32_t* pos, int64_t pos_axis_stride, int n_axes,
+                            const int* section, int n_sections, int layout, double theta,
+                            const void* wq, const void* wk, float eps, int dtype, int precision,
+                            void* q_out, int64_t q_out_tok_stride,
+                            void* k_out, int64_t k_out_tok_stride,
+                            const float* cs_cache, int cache_rows, void* stream);
+
+/*
  * mrope_decode_qk — one decode step of the fused path ([RoPE] Qwen3.5 call
  * chain, compute_3d_position_ids: with rope_deltas stored and a non-empty
  * cache, positions are recovered from the sequence index counted from the
@@ -257,14 +292,20 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq,
  *               out_head_stride = n*D, out_tok_stride = D; token-major rows:
  *               out_head_stride = D, out_tok_stride >= heads*D.  v_out may be
  *               NULL (v not written).
- * The outputs may not overlap the input or each other.  EINVAL on bad
- * shapes or strides (rows that would overlap), null pointers, overlap;
- * EUNSUPPORTED when one token's output rows span 2^31 bytes or more.
+ *   cs_cache, cache_rows: optional cos/sin cache by position
+ *               (mrope_cos_sin_cache(rotary_dim/2, theta, cache_rows));
+ *               positions outside [0, cache_rows) are computed.  NULL, 0 =
+ *               compute all.
+ * The outputs may not overlap the input, the cache or each other.  EINVAL
+ * on bad shapes or strides (rows that would overlap), null pointers,
+ * overlap; EUNSUPPORTED when one token's output rows span 2^31 bytes or
+ * more.
  */
 int mrope_vision_qkv(const void* qkv, int64_t qkv_tok_stride, int64_t n, int heads, int D,
                      int rotary_dim, const int32_t* pos, int64_t pos_axis_stride, double theta,
                      int dtype, int precision, void* q_out, void* k_out, void* v_out,
-                     int64_t out_head_stride, int64_t out_tok_stride, void* stream);
+                     int64_t out_head_stride, int64_t out_tok_stride, const float* cs_cache,
+                     int cache_rows, void* stream);
 
 /* Status bits written by the position builders into their device `status`
  * word (0 = the inputs describe a sequence the walkthrough can build). */

@@ -263,6 +263,20 @@ def mrope_cos_sin(pos, inv, section, layout, rotary_dim):
     return np.concatenate([c, c], axis=1), np.concatenate([s, s], axis=1)
 
 
+def cos_sin_cache(dim: int, theta: float, rows: int) -> np.ndarray:
+    """cos/sin by position value, [rows, dim/2, 2] binary32 (cos, sin).
+
+    RoPE post, "method 2" under the Qwen3-VL rotary: the binary32 outer
+    product of arange(rows) and inv_freq, whose cos/sin are gathered by
+    position afterwards; the angle fl32(p * inv[i]) is the same product the
+    per-token path forms, so the gathered values equal ``cos_sin_half``'s.
+    """
+    inv = inv_freq(dim, theta).astype(np.float64)
+    p = np.arange(rows, dtype=np.float64)
+    ang = fl32(p[:, None] * inv[None, :]).astype(np.float64)
+    return np.stack([fl32(np.cos(ang)), fl32(np.sin(ang))], axis=-1)
+
+
 # ---------------------------------------------------------------------------
 # RMSNorm and rotation
 # ---------------------------------------------------------------------------

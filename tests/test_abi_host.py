@@ -298,3 +298,25 @@ def test_position_builders_reject_bad_arguments():
     assert vcall(ps=63) == _lib.MROPE_EINVAL
     assert vcall(status=0) == _lib.MROPE_EINVAL
     assert vcall(pos=FAKE + 8) == _lib.MROPE_EINVAL           # pos overlaps the grids
+
+
+@fake_ptr_test
+def test_cache_arguments_are_checked():
+    lib = _lib.load()
+    assert lib.mrope_cos_sin_cache(7, 1e4, 10, FAKE, None) == _lib.MROPE_EINVAL     # odd dim
+    assert lib.mrope_cos_sin_cache(16, 0.0, 10, FAKE, None) == _lib.MROPE_EINVAL
+    assert lib.mrope_cos_sin_cache(16, 1e4, -1, FAKE, None) == _lib.MROPE_EINVAL
+    assert lib.mrope_cos_sin_cache(16, 1e4, 10, FAKE + 4, None) == _lib.MROPE_EINVAL  # alignment
+    assert lib.mrope_cos_sin_cache(16, 1e4, 0, None, None) == _lib.MROPE_OK          # nothing
+    sec = _lib.int_array([24, 20, 20])
+
+    def fused(cache, rows, qo=FAKE + 0x20000000):
+        return lib.rmsnorm_mrope_qk_cached(
+            FAKE, 32 * 128, 32, FAKE + 0x4000000, 4 * 128, 4, 16, 128, 128, FAKE + 0x8000000, 16,
+            3, sec, 3, _lib.LAYOUT_INTERLEAVED, 1e6, None, None, 1e-6, _lib.DTYPE_BF16, 0, qo,
+            32 * 128, FAKE + 0x24000000, 4 * 128, cache, rows, None)
+
+    assert fused(None, 5) == _lib.MROPE_EINVAL                  # rows without a cache
+    assert fused(FAKE + 0x30000004, 10) == _lib.MROPE_EINVAL    # misaligned cache
+    assert fused(FAKE + 0x30000000, -1) == _lib.MROPE_EINVAL
+    assert fused(FAKE + 0x20000000, 10) == _lib.MROPE_EINVAL    # cache overlaps q_out

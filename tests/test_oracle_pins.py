@@ -761,3 +761,30 @@ def test_vision_qkv_relative_positions_per_head():
     moved = score((3 + 4, 5 + 9), (7 + 4, 2 + 9))
     assert np.max(np.abs(moved - base)) < 1e-4 * (1 + np.max(np.abs(base)))
     assert np.max(np.abs(score((4, 5), (7, 2)) - base)) > 1e-3
+
+
+def test_cos_sin_cache_gathered_by_position_is_the_per_token_table():
+    """Method 2 (a table by position value, gathered) gives the per-token
+    cos/sin of method 1 bit for bit, for every layout's column-to-axis map."""
+    rng = np.random.default_rng(46)
+    for layout, section, rd, n_axes, dim in [("interleaved", (24, 20, 20), 128, 3, 128),
+                                             ("chunked", (16, 24, 24), 128, 3, 128),
+                                             ("vision_2d", None, 72, 2, 36)]:
+        pos = rng.integers(0, 300, (n_axes, 50)).astype(np.int32)
+        cache = O.cos_sin_cache(dim, 1e4, 300)
+        half = rd // 2
+        axis = O.axis_table(half, section, layout)
+        fidx = np.arange(half) % (half // 2) if layout == "vision_2d" else np.arange(half)
+        c, s = O.mrope_cos_sin(pos, O.inv_freq(dim, 1e4), section, layout, rd)
+        p_col = pos[axis, :].T                           # [T, half] position per column
+        gathered = cache[p_col, fidx[None, :]]           # [T, half, 2]
+        assert np.array_equal(gathered[..., 0], c[:, :half])
+        assert np.array_equal(gathered[..., 1], s[:, :half])
+    # and the table itself is cos/sin of the binary32 product, rounded once
+    cache = O.cos_sin_cache(8, 100.0, 5)
+    inv = O.inv_freq(8, 100.0)
+    for p_ in range(5):
+        for i in range(4):
+            a = float(np.float32(np.float32(p_) * inv[i]))
+            assert cache[p_, i, 0] == np.float32(math.cos(a))
+            assert cache[p_, i, 1] == np.float32(math.sin(a))

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, PRECISIONS, MropeError, check,  # noqa: F401
                    float_array, int_array, load)
 
-__all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "rms_norm",
+__all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "mrope_cos_sin_cache", "rms_norm",
            "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "vision_qkv", "rope_index",
            "vision_pos_ids", "MropeError", "load"]
 
@@ -136,18 +136,32 @@ def apply_rotary_qk(q, k, cos, sin, rotary_dim: int, q_out=None, k_out=None,
     check(load().apply_rotary_qk(_ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"),
                                  hk, T, D, int(rotary_dim), _ptr(cos), _ptr(sin),
                                  cos.stride(0) if T > 0 else rotary_dim, _dtype_code(q),
-                                 _precision_code(precision), _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out),
+                                 _precision_code(precision), _ptr(q_out),
+                                 _heads_view(q_out, "q_out"), _ptr(k_out),
                                  _heads_view(k_out, "k_out"), _stream(q)))
     return q_out, k_out
 
 
+def mrope_cos_sin_cache(dim: int, theta: float, rows: int, device="cuda", out=None):
+    """cos/sin table by position [rows, dim/2, 2] float32 (cos, sin) for
+    inv_freq = mrope_inv_freq(dim, theta); dim = rotary_dim for text layouts,
+    rotary_dim/2 for the vision layout."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((rows, dim // 2, 2), dtype=torch.float32, device=device)
+    check(load().mrope_cos_sin_cache(int(dim), float(theta), int(rows), _ptr(out), _stream(out)))
+    return out
+
+
 def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
                      wq=None, wk=None, eps: float = 1e-6, q_out=None, k_out=None,
-                     precision="exact"):
+                     precision="exact", cs_cache=None):
     """Fused per-head RMSNorm (if weights are given) + MRoPE on q and k.
 
     pos: int32 [n_axes, T] on the device (3 axes for interleaved, 2 for
     vision_2d, len(section) for chunked).  precision as in apply_rotary_qk.
+    cs_cache: optional table from mrope_cos_sin_cache (same theta), read for
+    positions inside it.
     """
     torch = _torch()
     q_out = torch.empty_like(q) if q_out is None else q_out
@@ -161,11 +175,12 @@ def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
         raise MropeError(_lib.MROPE_EINVAL, "positions must be contiguous along T")
     pos_stride = pos.stride(0) if n_axes > 1 else T
     sec = list(section) if section is not None else []
-    check(load().rmsnorm_mrope_qk(
+    check(load().rmsnorm_mrope_qk_cached(
         _ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"), hk, T, D,
         int(rotary_dim), _ptr(pos), pos_stride, n_axes, int_array(sec), len(sec),
         _layout_code(layout), float(theta), _ptr(wq), _ptr(wk), float(eps), _dtype_code(q),
-        _precision_code(precision), _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out), _heads_view(k_out, "k_out"),
+        _precision_code(precision), _ptr(q_out), _heads_view(q_out, "q_out"), _ptr(k_out),
+        _heads_view(k_out, "k_out"), _ptr(cs_cache), 0 if cs_cache is None else cs_cache.shape[0],
         _stream(q)))
     return q_out, k_out
 
@@ -201,7 +216,7 @@ def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: in
 
 
 def vision_qkv(qkv, pos, rotary_dim: int, theta: float, q_out=None, k_out=None, v_out=None,
-               precision="exact", head_major: bool = True, with_v: bool = True):
+               precision="exact", head_major: bool = True, with_v: bool = True, cs_cache=None):
     """Vision rotary on a packed qkv [n, 3, heads, D] (token stride free, the
     rest contiguous): q and k rotated with the 2-D (row, col) positions pos
     int32 [2, n], v copied.  Outputs are per-head planes [heads, n, D] (or
@@ -226,7 +241,8 @@ def vision_qkv(qkv, pos, rotary_dim: int, theta: float, q_out=None, k_out=None, 
     check(load().mrope_vision_qkv(
         _ptr(qkv), qkv.stride(0) if n > 0 else 3 * H * D, n, H, D, int(rotary_dim), _ptr(pos),
         pos.stride(0) if n > 0 else n, float(theta), _dtype_code(qkv), _precision_code(precision),
-        _ptr(q_out), _ptr(k_out), _ptr(v_out) if with_v else None, hs, ts, _stream(qkv)))
+        _ptr(q_out), _ptr(k_out), _ptr(v_out) if with_v else None, hs, ts, _ptr(cs_cache),
+        0 if cs_cache is None else cs_cache.shape[0], _stream(qkv)))
     return q_out, k_out, (v_out if with_v else None)
 
 

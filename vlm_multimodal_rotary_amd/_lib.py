@@ -65,11 +65,17 @@ SIGNATURES = {
                                   _c_int, _vp, _c_i64, _c_int, _ip, _c_int, _c_int, _c_double,
                                   _vp, _vp, _c_float, _c_int, _c_int, _vp, _c_i64, _vp, _c_i64,
                                   _vp]),
+    "mrope_cos_sin_cache": (_c_int, [_c_int, _c_double, _c_int, _vp, _vp]),
+    "rmsnorm_mrope_qk_cached": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_i64, _c_int,
+                                         _c_int, _vp, _c_i64, _c_int, _ip, _c_int, _c_int,
+                                         _c_double, _vp, _vp, _c_float, _c_int, _c_int, _vp,
+                                         _c_i64, _vp, _c_i64, _vp, _c_int, _vp]),
     "mrope_decode_qk": (_c_int, [_vp, _c_i64, _c_int, _vp, _c_i64, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _vp, _vp, _c_double, _vp, _vp, _c_float, _c_int,
                                  _c_int, _vp, _c_i64, _vp, _c_i64, _c_i64, _c_int, _vp]),
     "mrope_vision_qkv": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _vp, _c_i64,
-                                  _c_double, _c_int, _c_int, _vp, _vp, _vp, _c_i64, _c_i64, _vp]),
+                                  _c_double, _c_int, _c_int, _vp, _vp, _vp, _c_i64, _c_i64, _vp,
+                                  _c_int, _vp]),
     "mrope_rope_index_workspace_size": (ctypes.c_size_t, [_c_int, _c_i64, _c_int, _c_int]),
     "mrope_rope_index": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
                                   _vp, _c_i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),

@@ -131,6 +131,8 @@ int build_table(int rotary_dim, double theta, const int* section, int n_sections
   const int half = rotary_dim / 2;
   int rc = build_axis(half, section, n_sections, layout, tab.axis);
   if (rc) return rc;
+  for (int j = 0; j < half; ++j)
+    tab.fidx[j] = (uint8_t)(layout == MROPE_LAYOUT_VISION_2D ? j % (half / 2) : j);
   if (inv_given != nullptr) {
     for (int j = 0; j < half; ++j)
       tab.inv[j] = layout == MROPE_LAYOUT_VISION_2D ? inv_given[j % (half / 2)] : inv_given[j];
@@ -266,6 +268,34 @@ int check_qk_tensors(const QKArgs& a, bool need_rd) {
   return MROPE_OK;
 }
 
+// An optional cos/sin cache by position for the positions path.
+struct CacheArgs {
+  const float* cache = nullptr;
+  int rows = 0;
+  int n_freq = 0;
+};
+
+// Checks an optional cos/sin cache argument of the positions path: rows of
+// n_freq (cos, sin) pairs, 8-byte aligned, not overlapping any output.
+int check_cache(const float* cache, int rows, int n_freq, const QKArgs& a, CacheArgs& out,
+                Extent& ext) {
+  out = CacheArgs();
+  ext = Extent();
+  if (cache == nullptr) {
+    if (rows != 0) return fail(MROPE_EINVAL, "cache_rows must be 0 without a cache");
+    return MROPE_OK;
+  }
+  if (rows < 0) return fail(MROPE_EINVAL, "cache_rows is negative");
+  if (reinterpret_cast<uintptr_t>(cache) % 8 != 0)
+    return fail(MROPE_EINVAL, "the cos/sin cache must be 8-byte aligned");
+  ext = extent_of(cache, 1, 0, (int64_t)rows * n_freq * 2, 4);
+  out.cache = cache;
+  out.rows = rows;
+  out.n_freq = n_freq;
+  (void)a;
+  return MROPE_OK;
+}
+
 // Resident wavefronts per SIMD for a launch (0 = as many as registers allow).
 // Measured on MI355X: per-head-plane outputs (many short scattered row
 // writes per wavefront) run best with few wavefronts -- 3 for 8-byte chunks,
@@ -299,7 +329,7 @@ struct DecodeArgs {
 int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
            const int32_t* pos, int64_t pos_stride, const float* cos, const float* sin,
            int64_t cs_ts, float eps, void* stream, const Extent* extra, int n_extra,
-           const DecodeArgs* dec = nullptr) {
+           const DecodeArgs* dec = nullptr, const CacheArgs* cache = nullptr) {
   const int es = elem_bytes_of(a.dtype);
   const void* ptrs[9] = {a.x[0], a.x[1], a.x[2], a.y[0], a.y[1], a.y[2], a.w[0], a.w[1], a.w[2]};
   int64_t strides[11] = {a.x_ts[0], a.x_ts[1], a.x_ts[2], a.y_ts[0], a.y_ts[1], a.y_ts[2],
@@ -342,6 +372,11 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   p.cs_ts = cs_ts;
   p.eps = eps;
   p.inv_d = 1.0 / (double)a.D;
+  if (cache != nullptr && cache->cache != nullptr) {
+    p.cs_cache = cache->cache;
+    p.cache_rows = cache->rows;
+    p.n_freq = cache->n_freq;
+  }
   if (dec != nullptr) {
     p.cache_len = dec->cache_len;
     p.rope_delta = dec->rope_delta;
@@ -425,7 +460,8 @@ extern "C" {
 int mrope_vision_qkv(const void* qkv, int64_t qkv_tok_stride, int64_t n, int heads, int D,
                      int rotary_dim, const int32_t* pos, int64_t pos_axis_stride, double theta,
                      int dtype, int precision, void* q_out, void* k_out, void* v_out,
-                     int64_t out_head_stride, int64_t out_tok_stride, void* stream) {
+                     int64_t out_head_stride, int64_t out_tok_stride, const float* cs_cache,
+                     int cache_rows, void* stream) {
   if (heads < 0) return fail(MROPE_EINVAL, "heads = %d is negative", heads);
   QKArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -460,9 +496,32 @@ int mrope_vision_qkv(const void* qkv, int64_t qkv_tok_stride, int64_t n, int hea
   if (rc) return rc;
   if (pos_axis_stride < 0) return fail(MROPE_EINVAL, "pos_axis_stride is negative");
   if (n > 0 && heads > 0 && pos == nullptr) return fail(MROPE_EINVAL, "pos is NULL");
-  Extent extra[1] = {extent_of(pos, 2, pos_axis_stride, n, 4)};
+  CacheArgs ca;
+  Extent cache_ext;
+  rc = check_cache(cs_cache, cache_rows, rotary_dim / 4, a, ca, cache_ext);
+  if (rc) return rc;
+  Extent extra[2] = {extent_of(pos, 2, pos_axis_stride, n, 4), cache_ext};
   return run_qk(a, mrope::kCsFromPositions, false, tab, pos, pos_axis_stride, nullptr, nullptr, 0,
-                0.0f, stream, extra, 1);
+                0.0f, stream, extra, 2, nullptr, &ca);
+}
+
+int mrope_cos_sin_cache(int dim, double theta, int rows, float* cache, void* stream) {
+  if (dim <= 0 || dim % 2 != 0 || dim > MROPE_MAX_ROTARY_DIM)
+    return fail(MROPE_EINVAL, "dim = %d must be even and in (0, %d]", dim, MROPE_MAX_ROTARY_DIM);
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(MROPE_EINVAL, "theta must be positive and finite");
+  if (rows < 0) return fail(MROPE_EINVAL, "rows is negative");
+  if (rows > 0 && cache == nullptr) return fail(MROPE_EINVAL, "cache is NULL");
+  if (reinterpret_cast<uintptr_t>(cache) % 8 != 0)
+    return fail(MROPE_EINVAL, "cache must be 8-byte aligned");
+  if (rows == 0) return ok();
+  mrope::ColTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  fill_inv(dim, theta, tab.inv);
+  const int hrc = mrope::launch_cos_sin_cache(tab, dim / 2, rows, cache, stream);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
 }
 
 size_t mrope_rope_index_workspace_size(int batch, int64_t seq_len, int n_images, int n_videos) {
@@ -709,6 +768,20 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
                      const void* wq, const void* wk, float eps, int dtype, int precision,
                      void* q_out, int64_t q_out_tok_stride, void* k_out,
                      int64_t k_out_tok_stride, void* stream) {
+  return rmsnorm_mrope_qk_cached(q, q_tok_stride, hq, k, k_tok_stride, hk, T, D, rotary_dim, pos,
+                                 pos_axis_stride, n_axes, section, n_sections, layout, theta, wq,
+                                 wk, eps, dtype, precision, q_out, q_out_tok_stride, k_out,
+                                 k_out_tok_stride, nullptr, 0, stream);
+}
+
+int rmsnorm_mrope_qk_cached(const void* q, int64_t q_tok_stride, int hq, const void* k,
+                            int64_t k_tok_stride, int hk, int64_t T, int D, int rotary_dim,
+                            const int32_t* pos, int64_t pos_axis_stride, int n_axes,
+                            const int* section, int n_sections, int layout, double theta,
+                            const void* wq, const void* wk, float eps, int dtype, int precision,
+                            void* q_out, int64_t q_out_tok_stride, void* k_out,
+                            int64_t k_out_tok_stride, const float* cs_cache, int cache_rows,
+                            void* stream) {
   QKArgs a;
   std::memset(&a, 0, sizeof(a));
   a.x[0] = q;
@@ -746,9 +819,15 @@ int rmsnorm_mrope_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
                 expected_axes(layout, n_sections));
   if (pos_axis_stride < 0) return fail(MROPE_EINVAL, "pos_axis_stride is negative");
   if (T > 0 && hq + hk > 0 && pos == nullptr) return fail(MROPE_EINVAL, "pos is NULL");
-  Extent extra[1] = {extent_of(pos, n_axes, pos_axis_stride, T, 4)};
+  const int half = rotary_dim / 2;
+  CacheArgs ca;
+  Extent cache_ext;
+  rc = check_cache(cs_cache, cache_rows, layout == MROPE_LAYOUT_VISION_2D ? half / 2 : half, a, ca,
+                   cache_ext);
+  if (rc) return rc;
+  Extent extra[2] = {extent_of(pos, n_axes, pos_axis_stride, T, 4), cache_ext};
   return run_qk(a, mrope::kCsFromPositions, norm, tab, pos, pos_axis_stride, nullptr, nullptr, 0,
-                eps, stream, extra, 1);
+                eps, stream, extra, 2, nullptr, &ca);
 }
 
 int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,

@@ -19,6 +19,7 @@ constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
 struct ColTable {
   float inv[kMaxHalf];
   uint8_t axis[kMaxHalf];
+  uint8_t fidx[kMaxHalf];   // index of inv[j] among the distinct frequencies
 };
 
 // How the cos/sin of a row's token are obtained.
@@ -63,6 +64,11 @@ struct QKParams {
   int64_t cs_ts;
   float eps;
   double inv_d;          // 1.0 / D
+  // optional cos/sin cache by position: (cos, sin) of fl32(p * inv) at
+  // cs_cache[2 * (p * n_freq + fidx[j])], for 0 <= p < cache_rows
+  const float* cs_cache;
+  int cache_rows;
+  int n_freq;
   // decode mode
   const int32_t* cache_len;   // [batch]
   const int32_t* rope_delta;  // [batch] or null
@@ -139,5 +145,8 @@ int launch_vision_pos_ids(const VisionPosParams& p, void* stream);
 int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKParams& p,
               const ColTable& tab, int nt_cap, void* stream);
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
+// cos/sin cache by position: cache[(p * n_freq + i) * 2 + {0, 1}] = (cos, sin)
+// of fl32(float(p) * tab.inv[i]) for p < rows, i < n_freq.
+int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream);
 
 }  // namespace mrope

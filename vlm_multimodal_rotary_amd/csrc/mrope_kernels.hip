@@ -546,7 +546,15 @@ qk_kernel(const QKParams p, const ColTable tab) {
         const int j = idx - tl * half;
         const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t0 + tl];
         float c, s;
-        angle_cos_sin(pp, tab.inv[j], c, s);
+        if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
+          // the cache holds the same rounded values the computation gives
+          const float2 cs = *reinterpret_cast<const float2*>(
+              p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
+          c = cs.x;
+          s = cs.y;
+        } else {
+          angle_cos_sin(pp, tab.inv[j], c, s);
+        }
         lc[idx] = (cs_t)c;
         ls[idx] = (cs_t)s;
       }
@@ -659,6 +667,21 @@ __global__ void __launch_bounds__(256) cos_sin_kernel(const CosSinParams p, cons
   sr[j + p.half] = s;
 }
 
+// cos/sin cache by position: one thread per (position, frequency).
+__global__ void __launch_bounds__(256) cos_sin_cache_kernel(const ColTable tab, int n_freq,
+                                                            int64_t n, float* cache) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int64_t pos = idx / n_freq;
+  const int i = (int)(idx - pos * n_freq);
+  float c, s;
+  angle_cos_sin((int32_t)pos, tab.inv[i], c, s);
+  float2 v;
+  v.x = c;
+  v.y = s;
+  *reinterpret_cast<float2*>(cache + 2 * idx) = v;
+}
+
 template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
@@ -766,6 +789,14 @@ int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKPara
     }
   }
   return (int)hipErrorInvalidValue;
+}
+
+int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream) {
+  const int64_t n = (int64_t)rows * n_freq;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(cos_sin_cache_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), tab, n_freq, n, cache);
+  return (int)hipGetLastError();
 }
 
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream) {
