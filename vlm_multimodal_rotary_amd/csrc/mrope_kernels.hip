@@ -296,22 +296,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
 }
 
-#ifndef MROPE_LOAD_AUX
-#define MROPE_LOAD_AUX 0
-#endif
 template <int CB>
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t rs, uint32_t off, Words<CB>& r) {
-  constexpr int aux = MROPE_LOAD_AUX;
   if constexpr (CB == 16) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, aux);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (CB == 8) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, aux);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
     r.w[0] = v.x; r.w[1] = v.y;
   } else if constexpr (CB == 4) {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, aux);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
   } else {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, aux);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
   }
 }
 
@@ -470,11 +466,8 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
 // cos/sin (in its LDS slice), then the tile's q rows and k rows, U row-steps
 // per batch of loads.  Wavefronts are short-lived and many; the hardware
 // overlaps them, and the chip's active window of rows stays contiguous.
-#ifndef MROPE_QK_MIN_WAVES_PER_EU
-#define MROPE_QK_MIN_WAVES_PER_EU 1
-#endif
 template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
-__global__ void __launch_bounds__(kBlockThreads, MROPE_QK_MIN_WAVES_PER_EU)
+__global__ void __launch_bounds__(kBlockThreads)
 qk_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int CB = ES * V;
