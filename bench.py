@@ -310,6 +310,33 @@ def bench_vision_qkv(args):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_decode(inp, wl, budget_s: float = 10.0, precision: str = "exact"):
+    """The oracle's decode step on groups of 8 consecutive sequences of the
+    same batch (their q, k, cache rows and lengths), until about budget_s of
+    CPU time; single thread."""
+    from oracle import mrope_oracle as O
+    group = 8
+    B = wl.batch
+    done = 0
+    b0 = 0
+    start = time.perf_counter()
+    while True:
+        rows = slice(b0 * wl.new_tokens, (b0 + group) * wl.new_tokens)
+        O.mrope_decode_qk(inp["q"][rows], inp["k"][rows], inp["cache_len"][b0:b0 + group],
+                          wl.new_tokens, inp["rope_delta"][b0:b0 + group],
+                          inp["k_cache"][b0:b0 + group], rotary_dim=wl.rotary_dim,
+                          theta=wl.theta, wq=inp["wq"], wk=inp["wk"], eps=wl.eps,
+                          dtype=wl.dtype, precision=precision)
+        done += group * wl.new_tokens
+        b0 = (b0 + group) % (B - group + 1)
+        elapsed = time.perf_counter() - start
+        if elapsed >= budget_s:
+            break
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode tokens (groups of {group} sequences with their cache "
+                      f"rows) of {wl.name}, {elapsed:.1f} s, one thread"}
+
+
 def copy_calib(nbytes: int, steps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -444,8 +471,9 @@ def main():
     if not decode and args.cs_cache:
         line["config"]["cs_cache"] = cache_info
         line["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline and not decode:
-        line["cpu_baseline"] = cpu_baseline(inp, wl, precision=args.precision)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = (cpu_baseline_decode(inp, wl, precision=args.precision) if decode
+                                else cpu_baseline(inp, wl, precision=args.precision))
     print(json.dumps(line), flush=True)
 
 

@@ -277,8 +277,7 @@ struct CacheArgs {
 
 // Checks an optional cos/sin cache argument of the positions path: rows of
 // n_freq (cos, sin) pairs, 8-byte aligned, not overlapping any output.
-int check_cache(const float* cache, int rows, int n_freq, const QKArgs& a, CacheArgs& out,
-                Extent& ext) {
+int check_cache(const float* cache, int rows, int n_freq, CacheArgs& out, Extent& ext) {
   out = CacheArgs();
   ext = Extent();
   if (cache == nullptr) {
@@ -292,7 +291,6 @@ int check_cache(const float* cache, int rows, int n_freq, const QKArgs& a, Cache
   out.cache = cache;
   out.rows = rows;
   out.n_freq = n_freq;
-  (void)a;
   return MROPE_OK;
 }
 
@@ -498,7 +496,7 @@ int mrope_vision_qkv(const void* qkv, int64_t qkv_tok_stride, int64_t n, int hea
   if (n > 0 && heads > 0 && pos == nullptr) return fail(MROPE_EINVAL, "pos is NULL");
   CacheArgs ca;
   Extent cache_ext;
-  rc = check_cache(cs_cache, cache_rows, rotary_dim / 4, a, ca, cache_ext);
+  rc = check_cache(cs_cache, cache_rows, rotary_dim / 4, ca, cache_ext);
   if (rc) return rc;
   Extent extra[2] = {extent_of(pos, 2, pos_axis_stride, n, 4), cache_ext};
   return run_qk(a, mrope::kCsFromPositions, false, tab, pos, pos_axis_stride, nullptr, nullptr, 0,
@@ -822,7 +820,7 @@ int rmsnorm_mrope_qk_cached(const void* q, int64_t q_tok_stride, int hq, const v
   const int half = rotary_dim / 2;
   CacheArgs ca;
   Extent cache_ext;
-  rc = check_cache(cs_cache, cache_rows, layout == MROPE_LAYOUT_VISION_2D ? half / 2 : half, a, ca,
+  rc = check_cache(cs_cache, cache_rows, layout == MROPE_LAYOUT_VISION_2D ? half / 2 : half, ca,
                    cache_ext);
   if (rc) return rc;
   Extent extra[2] = {extent_of(pos, n_axes, pos_axis_stride, T, 4), cache_ext};
