@@ -1,0 +1,136 @@
+"""Seeded random sweep of the fused path's geometry against the oracle:
+head dims from 2 to 512, partial rotary, every layout with a random valid
+section, token strides wider than the rows (so the chunk width drops below
+16 bytes when the stride is not a multiple of it), with and without the
+norm, all three precisions, in place and out of place, wide position
+ranges.
+
+Bars: as for the fused path (bf16 within 1 ulp, fp32 within 1e-5) in exact
+precision; bit-exact for the tensor-op precisions.
+"""
+import numpy as np
+import pytest
+
+from oracle import mrope_oracle as O
+import workloads as W
+from tests._helpers import assert_close, from_dev, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [2, 4, 6, 8, 12, 16, 24, 32, 40, 48, 64, 72, 80, 96, 128, 160, 192, 256, 320, 384, 512]
+
+
+def _random_case(rng):
+    while True:
+        dtype = ["bf16", "f32"][rng.integers(2)]
+        D = int(rng.choice(DIMS))
+        rd = 2 * int(rng.integers(1, D // 2 + 1))
+        half = rd // 2
+        layout = ["interleaved", "chunked", "vision_2d"][rng.integers(3)]
+        if layout == "vision_2d":
+            if half % 2:
+                continue
+            section = None
+        elif layout == "chunked":
+            n = int(rng.integers(1, 4))
+            cuts = np.sort(rng.integers(0, half + 1, n - 1))
+            section = tuple(int(x) for x in np.diff(np.concatenate([[0], cuts, [half]])))
+        else:
+            sh = int(rng.integers(0, half // 3 + 1))
+            sw = int(rng.integers(0, half // 3 + 1))
+            section = (half - sh - sw, sh, sw)
+            try:
+                O.axis_table(half, section, layout)
+            except AssertionError:
+                continue
+        return dict(dtype=dtype, D=D, rd=rd, layout=layout, section=section,
+                    hq=int(rng.integers(1, 41)), hk=int(rng.integers(0, 9)),
+                    T=int(rng.integers(1, 301)), pad=int(rng.choice([0, 1, 2, 8, 24])),
+                    norm=bool(rng.integers(2)),
+                    precision=["exact", "dtype", "fp32"][rng.integers(3)],
+                    inplace=bool(rng.integers(2)), seed=int(rng.integers(1 << 30)))
+
+
+_RNG = np.random.default_rng(2024)
+CASES = [_random_case(_RNG) for _ in range(48)]
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import vlm_multimodal_rotary_amd as lib
+    lib.load()
+    return lib
+
+
+def _vector_width(es, D, rd, strides):
+    """The chunk width the library can use (the host's rule; 0 = none)."""
+    half = rd // 2
+    v = 16 // es
+    while v >= 1:
+        if (D % (2 * v) == 0 and half % v == 0 and (D - rd) % (2 * v) == 0
+                and D // (2 * v) <= 64 and all(x % v == 0 for x in strides)):
+            return v
+        v //= 2
+    return 0
+
+
+def _strided(buf, T, H, D, stride):
+    return buf.as_strided((T, H, D), (stride, D, 1))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_random_geometry(M, case):
+    import torch
+    c = case
+    rng = np.random.default_rng(c["seed"])
+    T, D, rd, dtype = c["T"], c["D"], c["rd"], c["dtype"]
+    hq, hk = c["hq"], c["hk"]
+    q, k = W.random_qk(rng, T, hq, hk, D, dtype, scale=float(2.0 ** rng.integers(-4, 5)))
+    n_axes = 2 if c["layout"] == "vision_2d" else (len(c["section"]) if c["layout"] == "chunked"
+                                                   else 3)
+    pos = rng.integers(-1000, 100000, (n_axes, T)).astype(np.int32)
+    wq = W.random_weight(rng, D, dtype) if c["norm"] else None
+    wk = W.random_weight(rng, D, dtype) if c["norm"] else None
+    note(f"random {c}")
+    qs, ks = hq * D + c["pad"], hk * D + c["pad"]
+    qbuf = torch.zeros((T * qs + D,), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                       device="cuda")
+    kbuf = torch.zeros((T * max(ks, 1) + D,), dtype=qbuf.dtype, device="cuda")
+    qv, kv = _strided(qbuf, T, hq, D, qs), _strided(kbuf, T, hk, D, max(ks, 1))
+    qv.copy_(to_dev(q, dtype))
+    if hk:
+        kv.copy_(to_dev(k, dtype))
+    qo, ko = (qv, kv) if c["inplace"] else (None, None)
+    es = 2 if dtype == "bf16" else 4
+    strides = [qs] + ([max(ks, 1)] if hk else [])
+    if not c["inplace"]:
+        strides += [hq * D] + ([hk * D] if hk else [])
+    if _vector_width(es, D, rd, strides) == 0:
+        # no chunk width fits the strides: the call is refused before any work
+        with pytest.raises(M.MropeError) as err:
+            M.rmsnorm_mrope_qk(qv, kv, to_dev(pos, "i32"), rd, 1e4, c["section"], c["layout"],
+                               wq=to_dev(wq, dtype), wk=to_dev(wk, dtype), q_out=qo, k_out=ko)
+        assert err.value.code == -2
+        return
+    gq, gk = M.rmsnorm_mrope_qk(qv, kv, to_dev(pos, "i32"), rd, 1e4, c["section"], c["layout"],
+                                wq=to_dev(wq, dtype), wk=to_dev(wk, dtype), eps=1e-6,
+                                q_out=qo, k_out=ko, precision=c["precision"])
+    torch.cuda.synchronize()
+    oq, ok = O.rmsnorm_mrope_qk(q, k, pos, rotary_dim=rd, theta=1e4, section=c["section"],
+                                layout=c["layout"], wq=wq, wk=wk, eps=1e-6, dtype=dtype,
+                                precision=c["precision"])
+    got_q = from_dev(gq.contiguous())
+    got_k = from_dev(gk.contiguous()) if hk else ok
+    if c["precision"] == "exact":
+        assert_close(got_q, oq, dtype, "random q")
+        if hk:
+            assert_close(got_k, ok, dtype, "random k")
+    else:
+        assert np.array_equal(got_q.view(np.uint8), oq.view(np.uint8))
+        assert np.array_equal(got_k.view(np.uint8), ok.view(np.uint8))
+    # rows of the padding stay untouched
+    if c["pad"] and T > 1:
+        tail = from_dev(qbuf[hq * D:qs].contiguous())
+        assert np.all(tail.view(np.uint8) == 0)
