@@ -365,3 +365,36 @@ def test_extreme_positions(M):
                                 layout="interleaved", dtype="f32")
     assert_f32_close(from_dev(qo), oq, 1e-5, "extreme q")
     assert_f32_close(from_dev(ko), ok, 1e-5, "extreme k")
+
+
+# Geometries that take the flat kernel (positions path, no norm, at least
+# 2048 tokens, rows that are not a whole number of 256-byte lines pairs).
+FLAT = [("f32", 72, 72, (16, 16), "vision_2d", None),
+        ("bf16", 72, 72, (16, 16), "vision_2d", None),
+        ("f32", 80, 48, (5, 3), "interleaved", (12, 6, 6)),
+        ("bf16", 96, 32, (12, 2), "chunked", (8, 4, 4)),
+        ("bf16", 160, 160, (9, 1), "interleaved", (40, 20, 20)),
+        ("f32", 48, 48, (7, 0), "vision_2d", None)]
+
+
+@pytest.mark.parametrize("dtype,D,rd,heads,layout,section", FLAT,
+                         ids=[f"{d}-D{D}-rd{r}-{l}" for d, D, r, _, l, _ in FLAT])
+def test_flat_kernel_geometries(M, dtype, D, rd, heads, layout, section):
+    import torch
+    T = 2100
+    rng = np.random.default_rng(D * 7 + rd)
+    q, k = W.random_qk(rng, T, heads[0], heads[1], D, dtype)
+    n_axes = 2 if layout == "vision_2d" else 3
+    pos = rng.integers(0, 5000, (n_axes, T)).astype(np.int32)
+    note(f"flat {dtype} D={D} rd={rd} heads={heads} {layout}")
+    qo, ko = M.rmsnorm_mrope_qk(to_dev(q, dtype), to_dev(k, dtype), to_dev(pos, "i32"), rd, 1e4,
+                                section, layout)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 200, replace=False)]))
+    oq, ok = O.rmsnorm_mrope_qk(q[rows], k[rows], pos[:, rows], rotary_dim=rd, theta=1e4,
+                                section=section, layout=layout, dtype=dtype)
+    assert_close(from_dev(qo)[rows], oq, dtype, "flat q")
+    if heads[1]:
+        assert_close(from_dev(ko)[rows], ok, dtype, "flat k")
+    if rd < D:
+        assert np.array_equal(from_dev(qo)[..., rd:], q[..., rd:])

@@ -235,3 +235,75 @@ def test_three_slot_packed_qkv(T, heads, D, rd, es, min_waves, head_major):
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))
+
+
+# ---------------------------------------------------------------------------
+# The flat kernel: chunks of the token's block lane after lane, with the
+# rotary partner loaded by the same lane.
+# ---------------------------------------------------------------------------
+
+FLAT_STEPS = 6
+
+
+def f32(x):
+    return np.float32(x)
+
+
+def simulate_flat(T, heads, D, rd, es, v, head_major=False):
+    half = rd // 2
+    cpr, hc, rc = D // v, half // v, rd // v
+    cb = v * es
+    inv_cpr = f32(f32(1.0) / f32(cpr))
+    writes = [np.zeros((T, H, D), dtype=np.int32) for H in heads]
+    lanes = np.arange(WAVE)
+    for t in range(T):
+        for s, H in enumerate(heads):
+            if H == 0:
+                continue
+            rotate = s < 2
+            nch = H * cpr
+            in_extent = nch * cb
+            yhs = T * D + 4 * v if head_major else D
+            yts = D if head_major else H * D + 4 * v
+            out_extent = ((H - 1) * yhs + D) * es
+            assert in_extent < OUT_OF_RANGE and out_extent < OUT_OF_RANGE
+            for base in range(0, nch, WAVE * FLAT_STEPS):
+                for u in range(FLAT_STEPS):
+                    f = base + u * WAVE + lanes
+                    ok = f < nch
+                    row = (f.astype(np.float32) * inv_cpr).astype(np.int64)
+                    row = np.where(row * cpr > f, row - 1, row)
+                    row = np.where((row + 1) * cpr <= f, row + 1, row)
+                    assert np.all(row == f // cpr)
+                    c = f - row * cpr
+                    k = np.where(~rotate | (c >= rc), 2, np.where(c < hc, 0, 1))
+                    fp = np.where(k == 2, f, np.where(k == 0, f + hc, f - hc))
+                    col = np.where(ok & (k < 2), np.where(k == 1, c - hc, c) * v, 0)
+                    assert np.all(col + v <= half) or half == 0
+                    xo = np.where(ok, f * cb, OUT_OF_RANGE)
+                    xp = np.where(ok & (k < 2), fp * cb, OUT_OF_RANGE)
+                    assert np.all(xo[ok] + cb <= in_extent) and np.all(xp[ok & (k < 2)] + cb <= in_extent)
+                    assert np.all(fp[ok] // cpr == row[ok])          # partner in the same row
+                    yoff = np.where(ok, (row * yhs + c * v) * es, OUT_OF_RANGE)
+                    assert np.all(yoff[ok] + cb <= out_extent)
+                    for i in np.nonzero(ok)[0]:
+                        writes[s][t, row[i], c[i] * v:c[i] * v + v] += 1
+    return writes
+
+
+@pytest.mark.parametrize("T,heads,D,rd,es,v", [
+    (3, (16, 16, 0), 72, 72, 4, 4),       # vision_2d fp32
+    (3, (16, 16, 16), 72, 72, 4, 4),      # vision qkv fp32
+    (3, (16, 16, 16), 72, 72, 2, 4),      # vision qkv bf16 (8-byte chunks)
+    (2, (28, 4, 0), 128, 128, 2, 8),
+    (2, (24, 4, 0), 256, 64, 2, 8),       # partial rotary: pass-through chunks
+    (2, (5, 3, 2), 80, 48, 4, 4),
+    (2, (40, 8, 0), 384, 384, 4, 4),      # several batches per tensor
+    (2, (3, 1, 0), 2, 2, 2, 1),
+])
+@pytest.mark.parametrize("head_major", [False, True])
+def test_flat_every_output_written_once(T, heads, D, rd, es, v, head_major):
+    writes = simulate_flat(T, heads, D, rd, es, v, head_major=head_major)
+    for s, H in enumerate(heads):
+        if H:
+            assert np.all(writes[s] == 1), (s, np.unique(writes[s]))

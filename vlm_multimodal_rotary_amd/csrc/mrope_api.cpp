@@ -176,6 +176,7 @@ int pick_vec(int dtype, int D, int rd, const void* const* ptrs, int nptrs,
 // Inputs have contiguous heads (head stride D); outputs have a head stride
 // (0 = D, token-major rows).
 constexpr int kSlots = mrope::kSlots;
+constexpr int64_t kFlatMinTokens = 2048;   // one wavefront per token fills the chip
 
 struct QKArgs {
   const void* x[kSlots];
@@ -315,6 +316,33 @@ int waves_per_simd(const QKArgs& a, int v, int es) {
   return 0;
 }
 
+int env_int(const char* name, int fallback) {
+  const char* e = std::getenv(name);
+  return e != nullptr ? std::atoi(e) : fallback;
+}
+
+// The flat kernel (chunks of the token's block lane after lane) serves the
+// positions path without RMSNorm for launches of at least one wavefront per
+// token over the whole chip.  It is chosen where the per-row mapping leaves
+// rows straddling cache lines (row bytes not a multiple of 256).
+// MROPE_FLAT=0/1 in the environment forces the choice (tuning).
+bool use_flat(const QKArgs& a, int cs_mode, bool norm, int v, int es) {
+  if (cs_mode != mrope::kCsFromPositions || norm || a.T < kFlatMinTokens) return false;
+  static const int env = env_int("MROPE_FLAT", -1);
+  if (env >= 0) return env != 0;
+  (void)v;
+  return (a.D * es) % 256 != 0;
+}
+
+// Resident wavefronts per SIMD for the flat kernel (0 = unbounded).  Four
+// measured best on the 72-wide vision rows in f32 and bf16, token-major and
+// head-major (two and three trail by 10%, unbounded by 1-10%).
+int waves_per_simd_flat() {
+  static const int env = env_int("MROPE_WAVES_PER_SIMD", -1);
+  if (env >= 0) return env > 8 ? 8 : env;
+  return 4;
+}
+
 // Launch geometry and the remaining per-launch fields.
 struct DecodeArgs {
   const int32_t* cache_len = nullptr;
@@ -404,11 +432,18 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
       return fail(MROPE_EUNSUPPORTED, "one token's rows of %s span 2^31 bytes or more",
                   s == 0 ? "q" : (s == 1 ? "k" : "v"));
   }
-  p.waves_cap = waves_per_simd(a, v, es);
   // For binary32 tensors the cast of cos/sin to the dtype is the identity.
   const int prec = (a.dtype == MROPE_DTYPE_F32 && a.precision == MROPE_PRECISION_FP32)
                        ? MROPE_PRECISION_DTYPE : a.precision;
-  const int hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, prec, p, tab, nt_cap, stream);
+  int hrc;
+  if (use_flat(a, cs_mode, norm, v, es)) {
+    p.inv_cpr = 1.0f / (float)(a.D / v);
+    p.waves_cap = waves_per_simd_flat();
+    hrc = mrope::launch_flat(a.dtype, v, prec, p, tab, stream);
+  } else {
+    p.waves_cap = waves_per_simd(a, v, es);
+    hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, prec, p, tab, nt_cap, stream);
+  }
   if (hrc != (int)hipSuccess)
     return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
   return ok();

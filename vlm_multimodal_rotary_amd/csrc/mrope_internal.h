@@ -55,6 +55,7 @@ struct QKParams {
   int nt;                // tokens per tile (set by the launcher)
   int parts;             // wavefronts per tile (set by the launcher)
   int waves_cap;         // resident wavefronts per SIMD at most (0 = no bound)
+  float inv_cpr;         // flat kernel: 1 / (D / V), chunks per head row
   int dq[kSlots], dr[kSlots];   // rpw = dq * heads + dr, per tensor (launcher)
   float inv_heads[kSlots];      // 1 / heads, per tensor (launcher)
   const int32_t* pos;
@@ -145,6 +146,10 @@ int launch_vision_pos_ids(const VisionPosParams& p, void* stream);
 int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKParams& p,
               const ColTable& tab, int nt_cap, void* stream);
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
+// The flat q/k kernel: positions path without RMSNorm, one token per
+// wavefront, the token's blocks read as consecutive chunks.
+int launch_flat(int dtype, int vec, int prec, const QKParams& p, const ColTable& tab,
+                void* stream);
 // cos/sin cache by position: cache[(p * n_freq + i) * 2 + {0, 1}] = (cos, sin)
 // of fl32(float(p) * tab.inv[i]) for p < rows, i < n_freq.
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream);
