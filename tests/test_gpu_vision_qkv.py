@@ -110,3 +110,53 @@ def test_vision_qkv_empty(M):
     q, k, v = M.vision_qkv(qkv, torch.empty((2, 0), dtype=torch.int32, device="cuda"), 72, 1e4)
     torch.cuda.synchronize()
     assert q.shape == (16, 0, 72)
+
+
+# bfloat16 planes of 2048 tokens or more take the staged kernel (rows through
+# LDS a few tokens per block); token counts leave a ragged last block.
+STAGED = [(2051, 16, 72, 72), (2100, 6, 128, 64), (2049, 5, 80, 48), (2053, 3, 16, 8)]
+
+
+@pytest.mark.parametrize("n,H,D,rd", STAGED, ids=[f"n{n}-H{H}-D{D}-rd{r}" for n, H, D, r in STAGED])
+def test_vision_qkv_staged_planes(M, n, H, D, rd):
+    rng = np.random.default_rng(n * 3 + D)
+    qkv = W._store(rng.standard_normal((n, 3, H, D)).astype(np.float32), "bf16")
+    pos = rng.integers(0, 4096, (2, n)).astype(np.int32)
+    note(f"vision_qkv staged bf16 n={n} H={H} D={D} rd={rd}")
+    gq, gk, gv = _run(M, qkv, pos, "bf16", rd, 1e4)
+    oq, ok, ov = O.vision_qkv(qkv, pos, rotary_dim=rd, theta=1e4, dtype="bf16")
+    assert_close(gq, oq, "bf16", "staged q planes")
+    assert_close(gk, ok, "bf16", "staged k planes")
+    assert np.array_equal(gv.view(np.uint8), ov.view(np.uint8))
+    assert np.array_equal(gq[..., rd:], qkv[:, 0, :, rd:].transpose(1, 0, 2))
+
+
+@pytest.mark.parametrize("precision", ["dtype", "fp32"])
+def test_vision_qkv_staged_precisions_bit_exact(M, precision):
+    rng = np.random.default_rng(74)
+    n = 2500
+    qkv = W._store(rng.standard_normal((n, 3, 16, 72)).astype(np.float32), "bf16")
+    pos = rng.integers(0, 4096, (2, n)).astype(np.int32)
+    note(f"vision_qkv staged precision {precision}")
+    gq, gk, _ = _run(M, qkv, pos, "bf16", 72, 1e4, precision=precision)
+    oq, ok, _ = O.vision_qkv(qkv, pos, rotary_dim=72, theta=1e4, dtype="bf16", precision=precision)
+    assert np.array_equal(gq, oq) and np.array_equal(gk, ok)
+
+
+def test_vision_qkv_staged_without_v_and_cached(M):
+    """No v plane (two tensors), and cos/sin gathered from a cache that covers
+    only part of the positions (the rest computed): same planes as without."""
+    import torch
+    rng = np.random.default_rng(75)
+    n = 2222
+    qkv = W._store(rng.standard_normal((n, 3, 16, 72)).astype(np.float32), "bf16")
+    pos = rng.integers(0, 4096, (2, n)).astype(np.int32)
+    note("vision_qkv staged without v, cos/sin cache of 3000 rows")
+    gq, gk, gv = _run(M, qkv, pos, "bf16", 72, 1e4, with_v=False)
+    oq, ok, _ = O.vision_qkv(qkv, pos, rotary_dim=72, theta=1e4, dtype="bf16")
+    assert gv is None
+    assert_close(gq, oq, "bf16", "staged q without v")
+    assert_close(gk, ok, "bf16", "staged k without v")
+    cache = M.mrope_cos_sin_cache(36, 1e4, 3000, device="cuda")   # vision: dim = rotary_dim / 2
+    cq, ck, _ = _run(M, qkv, pos, "bf16", 72, 1e4, cs_cache=cache)
+    assert np.array_equal(cq, gq) and np.array_equal(ck, gk)

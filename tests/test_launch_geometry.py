@@ -307,3 +307,125 @@ def test_flat_every_output_written_once(T, heads, D, rd, es, v, head_major):
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))
+
+
+BLOCK = WAVE * WPB
+STAGE_LDS_MAX = 64 * 1024   # LDS bytes a staged block may take (kStageLdsMax)
+
+
+def stage_slot_bytes(G, H, D, es):
+    chunks = G * H * D * es // 16
+    return -(-chunks // WAVE) * WAVE * 16
+
+
+def div_small(n, d, inv):
+    """The staged kernel's quotient through a binary32 reciprocal."""
+    q = (n.astype(np.float32) * inv).astype(np.int64)
+    q = np.where(q * d > n, q - 1, q)
+    q = np.where((q + 1) * d <= n, q + 1, q)
+    return q
+
+
+def simulate_stage(T, heads, D, rd, es, G, head_major, x_pad=0):
+    """Model of the staged kernel: per block, the LDS transfers of phase 1,
+    the cos/sin indices of phase 2 and the reads and stores of phase 3."""
+    half = rd // 2
+    ec = 16 // es
+    cpr = D * es // 16
+    f32 = np.float32
+    inv_cpr = f32(f32(1.0) / f32(cpr))
+    inv_half = f32(f32(1.0) / f32(half))
+    writes = [np.zeros((T, H, D), dtype=np.int32) for H in heads]
+    offs, off = [], 0
+    for H in heads:
+        offs.append(off)
+        if H:
+            off += stage_slot_bytes(G, H, D, es)
+    cs_bytes = G * half * 8
+    assert off % 16 == 0 and off + cs_bytes <= STAGE_LDS_MAX
+    lanes = np.arange(WAVE)
+    tid = np.arange(BLOCK)
+    for blk in range(-(-T // G)):
+        t0 = blk * G
+        nvalid = min(G, T - t0)
+        # phase 1
+        for s, H in enumerate(heads):
+            if H == 0:
+                continue
+            rcs = H * cpr
+            nch = G * rcs
+            x_ts = H * D + x_pad
+            tsb = x_ts * es
+            extent = (nvalid - 1) * tsb + rcs * 16
+            inv = f32(f32(1.0) / f32(rcs))
+            landed = np.zeros(nch, dtype=np.int32)
+            for wib in range(BLOCK // WAVE):
+                for kb in range(wib * WAVE, nch, BLOCK):
+                    k = kb + lanes
+                    g = div_small(k, rcs, inv)
+                    ok = (k < nch) & (g < nvalid)
+                    vo = g * tsb + (k - g * rcs) * 16
+                    assert np.all(vo[ok] + 16 <= extent)
+                    assert offs[s] + kb * 16 + WAVE * 16 <= offs[s] + stage_slot_bytes(G, H, D, es)
+                    assert np.all(g[k < nch] == k[k < nch] // rcs)
+                    landed[k[k < nch]] += 1
+            assert np.all(landed == 1)
+        # phase 2
+        i = np.arange(G * half)
+        g = div_small(i, half, inv_half)
+        assert np.all(g == i // half) and np.all(g < G)
+        # phase 3
+        for s, H in enumerate(heads):
+            if H == 0:
+                continue
+            nch = H * G * cpr
+            yhs = T * D + 8 * ec if head_major else D
+            yts = D if head_major else H * D + 8 * ec
+            extent = ((H - 1) * yhs + (nvalid - 1) * yts + D) * es
+            inv_h = f32(f32(1.0) / f32(H))
+            row_bytes = D * es
+            for kb in range(0, nch, BLOCK):
+                k = kb + tid
+                live = k < nch
+                o = div_small(k, cpr, inv_cpr)
+                c = k - o * cpr
+                if head_major:
+                    h, g = o // G, o % G
+                else:
+                    g = div_small(o, H, inv_h)
+                    h = o - g * H
+                assert np.all(o[live] == k[live] // cpr)
+                row = (g * H + h) * row_bytes
+                assert np.all(row[live] + c[live] * 16 + 16 <= stage_slot_bytes(G, H, D, es))
+                for m in range(ec // 2):
+                    col = c * ec + 2 * m
+                    rot = live & (s < 2) & (col < rd)
+                    first = col < half
+                    pcol = np.where(first, col + half, col - half)
+                    j = np.where(first, col, col - half)
+                    assert np.all(pcol[rot] * es + 2 * es <= row_bytes)
+                    assert np.all(j[rot] % 2 == 0) and np.all(g[rot] * half + j[rot] + 2 <= G * half)
+                st = live & (g < nvalid)
+                yo = (h * yhs + g * yts) * es + c * 16
+                assert np.all(yo[st] + 16 <= extent)
+                for q in np.nonzero(st)[0]:
+                    writes[s][t0 + g[q], h[q], c[q] * ec:c[q] * ec + ec] += 1
+    return writes
+
+
+@pytest.mark.parametrize("T,heads,D,rd,es,G", [
+    (20, (16, 16, 16), 72, 72, 2, 8),      # vision qkv bf16 planes
+    (9, (16, 16, 16), 72, 72, 4, 4),       # vision qkv fp32 planes
+    (11, (16, 16, 0), 72, 72, 4, 4),       # vision_2d fp32
+    (5, (28, 4, 0), 128, 128, 2, 2),
+    (7, (5, 3, 2), 80, 48, 4, 4),          # partial rotary
+    (3, (10, 2, 0), 384, 384, 4, 2),
+    (37, (3, 1, 0), 8, 4, 2, 16),          # the smallest even half            # the smallest even half
+])
+@pytest.mark.parametrize("head_major", [False, True])
+@pytest.mark.parametrize("x_pad", [0, 8])
+def test_stage_every_output_written_once(T, heads, D, rd, es, G, head_major, x_pad):
+    writes = simulate_stage(T, heads, D, rd, es, G, head_major, x_pad=x_pad)
+    for s, H in enumerate(heads):
+        if H:
+            assert np.all(writes[s] == 1), (s, np.unique(writes[s]))

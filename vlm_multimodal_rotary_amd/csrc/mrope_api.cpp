@@ -177,6 +177,8 @@ int pick_vec(int dtype, int D, int rd, const void* const* ptrs, int nptrs,
 // (0 = D, token-major rows).
 constexpr int kSlots = mrope::kSlots;
 constexpr int64_t kFlatMinTokens = 2048;   // one wavefront per token fills the chip
+constexpr int kStageLdsTarget = 32 * 1024;  // LDS of a staged block: five or more per CU
+constexpr int kStageLdsMax = 64 * 1024;     // ... at most (two per CU), with G forced
 
 struct QKArgs {
   const void* x[kSlots];
@@ -343,6 +345,56 @@ int waves_per_simd_flat() {
   return 4;
 }
 
+// The staged kernel (rows copied to LDS G tokens at a time, written back in
+// output order) serves the positions path without RMSNorm when every base,
+// stride and row is 16-byte aligned and the rotary half is even.  It is
+// chosen for bfloat16 head-major outputs (per-head planes), where it writes
+// each head's G rows as one run: 69% of HBM peak on 16 x 72 bf16 planes
+// against 51% for the flat kernel.  For binary32 planes and token-major rows
+// the flat kernel measured faster (65% and 72% against 60% and 61%).
+// Returns the largest G to try (the caller shrinks it to the LDS budget), or
+// 0 for another kernel.  MROPE_STAGE=0/1 and MROPE_STAGE_G in the
+// environment force the choice.
+int pick_stage(const QKArgs& a, int cs_mode, bool norm, int es, bool& head_major) {
+  if (cs_mode != mrope::kCsFromPositions || norm || a.T < kFlatMinTokens) return 0;
+  if (a.rd <= 0 || (a.rd / 2) % 2 != 0 || (a.D * es) % 16 != 0) return 0;
+  bool hm = false, tm = false;
+  for (int s = 0; s < kSlots; ++s) {
+    if (a.heads[s] == 0) continue;
+    const int64_t hs = head_stride(a, s);
+    if ((reinterpret_cast<uintptr_t>(a.x[s]) | reinterpret_cast<uintptr_t>(a.y[s])) % 16 != 0)
+      return 0;
+    if ((a.x_ts[s] * es) % 16 != 0 || (a.y_ts[s] * es) % 16 != 0 || (hs * es) % 16 != 0)
+      return 0;
+    if (hs == a.D && a.heads[s] > 1) tm = true;
+    else hm = true;
+  }
+  if (hm && tm) return 0;
+  head_major = hm;
+  static const int env = env_int("MROPE_STAGE", -1);
+  static const int env_g = env_int("MROPE_STAGE_G", 0);
+  if (env == 0 || (env < 0 && !(hm && es == 2))) return 0;
+  const int G = env_g > 0 ? env_g : 16;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return 0;
+  // a block's rows of each tensor are addressed with 32-bit byte offsets
+  const int64_t limit = int64_t(1) << 31;
+  for (int s = 0; s < kSlots; ++s) {
+    if (a.heads[s] == 0) continue;
+    const int64_t H = a.heads[s];
+    if (((G - 1) * a.x_ts[s] + H * a.D) * es >= limit ||
+        ((G - 1) * a.y_ts[s] + (H - 1) * head_stride(a, s) + a.D) * es >= limit)
+      return 0;
+  }
+  return G;
+}
+
+// Resident wavefronts per SIMD for the staged kernel (0 = as LDS allows).
+int waves_per_simd_stage() {
+  static const int env = env_int("MROPE_WAVES_PER_SIMD", -1);
+  if (env >= 0) return env > 8 ? 8 : env;
+  return 0;
+}
+
 // Launch geometry and the remaining per-launch fields.
 struct DecodeArgs {
   const int32_t* cache_len = nullptr;
@@ -436,7 +488,21 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   const int prec = (a.dtype == MROPE_DTYPE_F32 && a.precision == MROPE_PRECISION_FP32)
                        ? MROPE_PRECISION_DTYPE : a.precision;
   int hrc;
-  if (use_flat(a, cs_mode, norm, v, es)) {
+  bool head_major = false;
+  int G = pick_stage(a, cs_mode, norm, es, head_major);
+  // Fewer tokens per block where their rows would take more than the LDS
+  // budget: five or more resident blocks per compute unit keep enough bytes
+  // in flight (a block holds its LDS from its first load to its last store).
+  const int budget = env_int("MROPE_STAGE_G", 0) > 0 ? kStageLdsMax : kStageLdsTarget;
+  while (G > 1 && mrope::stage_lds_bytes(a.dtype, G, p) > budget) G /= 2;
+  if (G > 0 && mrope::stage_lds_bytes(a.dtype, G, p) > budget) G = 0;
+  if (G > 0) {
+    p.stage_hm = head_major ? 1 : 0;
+    p.inv_cpr = 1.0f / (float)(a.D * es / 16);
+    for (int s = 0; s < kSlots; ++s) p.inv_heads[s] = 1.0f / (float)(a.heads[s] > 0 ? a.heads[s] : 1);
+    p.waves_cap = waves_per_simd_stage();
+    hrc = mrope::launch_stage(a.dtype, prec, G, p, tab, stream);
+  } else if (use_flat(a, cs_mode, norm, v, es)) {
     p.inv_cpr = 1.0f / (float)(a.D / v);
     p.waves_cap = waves_per_simd_flat();
     hrc = mrope::launch_flat(a.dtype, v, prec, p, tab, stream);

@@ -55,7 +55,8 @@ struct QKParams {
   int nt;                // tokens per tile (set by the launcher)
   int parts;             // wavefronts per tile (set by the launcher)
   int waves_cap;         // resident wavefronts per SIMD at most (0 = no bound)
-  float inv_cpr;         // flat kernel: 1 / (D / V), chunks per head row
+  float inv_cpr;         // flat kernel: 1 / (D / V); staged kernel: 1 / (D * ES / 16)
+  int stage_hm;          // staged kernel: write head-major order (1) or token-major (0)
   int dq[kSlots], dr[kSlots];   // rpw = dq * heads + dr, per tensor (launcher)
   float inv_heads[kSlots];      // 1 / heads, per tensor (launcher)
   const int32_t* pos;
@@ -150,6 +151,11 @@ int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
 // wavefront, the token's blocks read as consecutive chunks.
 int launch_flat(int dtype, int vec, int prec, const QKParams& p, const ColTable& tab,
                 void* stream);
+// The staged kernel with G tokens per block (G in 1, 2, 4, 8, 16), and the
+// LDS bytes one block of it takes.
+int launch_stage(int dtype, int prec, int G, const QKParams& p, const ColTable& tab,
+                 void* stream);
+int stage_lds_bytes(int dtype, int G, const QKParams& p);
 // cos/sin cache by position: cache[(p * n_freq + i) * 2 + {0, 1}] = (cos, sin)
 // of fl32(float(p) * tab.inv[i]) for p < rows, i < n_freq.
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream);

@@ -808,6 +808,239 @@ int launch_flat_v(int prec, const QKParams& p, const ColTable& tab, hipStream_t 
   return (int)hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// The staged q/k kernel (no RMSNorm, cos/sin from positions).  A block owns G
+// consecutive tokens.  It first copies their rows of every tensor into LDS
+// with direct buffer-to-LDS loads (one wavefront instruction moves 64 chunks
+// of 16 bytes, consecutive in LDS) while it forms the G tokens' cos/sin,
+// then writes the output 16 bytes per lane: in head-major order the G rows
+// of a head go out back to back, one contiguous run per plane, and in
+// token-major order a token's heads do.  This is the layout transposition of
+// the vision tower's packed qkv into per-head planes; rows whose width is not
+// a whole number of cache lines also gain from writing whole runs.
+// Requirements (checked by the host): 16-byte aligned bases, strides and row
+// widths (D * ES), an even rotary half.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// floor(n / d) for n < 2^23 through the binary32 reciprocal inv ~ 1/d,
+// corrected to the exact quotient.
+__device__ __forceinline__ int div_small(int n, int d, float inv) {
+  int q = (int)((float)n * inv);
+  if (q * d > n) --q;
+  if ((q + 1) * d <= n) ++q;
+  return q;
+}
+
+// Bytes of LDS a slot's G token-rows take, padded to whole 1 KB wavefront
+// transfers so that no lane of the last transfer writes past the region.
+__host__ __device__ __forceinline__ int stage_slot_bytes(int G, int heads, int D, int es) {
+  const int chunks = G * heads * D * es / 16;
+  return ((chunks + kWaveSize - 1) / kWaveSize) * kWaveSize * 16;
+}
+
+template <bool BF16, int PREC, int G>
+__global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, const ColTable tab) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EC = 16 / ES;          // elements per 16-byte chunk
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWaveSize - 1);
+  const int wib = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
+  const int64_t t0 = (int64_t)blockIdx.x * G;
+  const int64_t left = p.T - t0;
+  const int nvalid = left < G ? (int)left : G;
+  const int D = p.D, half = p.half, rd = p.rd;
+  const int cpr = D * ES / 16;         // chunks per head row
+
+  int lds_off[kSlots];
+  int off = 0;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    lds_off[s] = off;
+    if (p.heads[s] > 0) off += stage_slot_bytes(G, p.heads[s], D, ES);
+  }
+  float2* cs = reinterpret_cast<float2*>(smem + off);   // [G][half]
+
+  // 1. token rows of each tensor to LDS, in memory order [g][head][D]
+#pragma unroll 1
+  for (int s = 0; s < kSlots; ++s) {
+    const int H = p.heads[s];
+    if (H == 0) continue;
+    const int rcs = H * cpr;                            // chunks per token
+    const int nch = G * rcs;
+    const uint32_t tsb = (uint32_t)(p.x_ts[s] * ES);    // token stride, bytes
+    const __amdgpu_buffer_rsrc_t rx = buffer_of(
+        static_cast<const char*>(p.x[s]) + t0 * p.x_ts[s] * ES,
+        (uint32_t)(nvalid - 1) * tsb + (uint32_t)rcs * 16u);
+    const float inv = 1.0f / (float)rcs;
+    unsigned char* dst = smem + lds_off[s];
+#pragma unroll 1
+    for (int kb = wib * kWaveSize; kb < nch; kb += kBlockThreads) {
+      const int k = kb + lane;
+      const int g = div_small(k, rcs, inv);
+      const uint32_t vo = k < nch && g < nvalid ? (uint32_t)g * tsb + (uint32_t)(k - g * rcs) * 16u
+                                                : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + kb * 16), 16, vo, 0, 0, 0);
+    }
+  }
+
+  // 2. cos/sin of the block's tokens (tokens past T repeat the last one)
+  {
+    const float inv = 1.0f / (float)half;
+#pragma unroll 1
+    for (int i = tid; i < G * half; i += kBlockThreads) {
+      const int g = div_small(i, half, inv);
+      const int j = i - g * half;
+      const int64_t t = t0 + (g < nvalid ? g : nvalid - 1);
+      const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t];
+      float c, sn;
+      if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
+        const float2 v = *reinterpret_cast<const float2*>(
+            p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
+        c = v.x;
+        sn = v.y;
+      } else {
+        angle_cos_sin(pp, tab.inv[j], c, sn);
+      }
+      cs[i] = make_float2(c, sn);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // 3. rotate (q, k) or copy (v) 16 bytes per lane; write in output order
+  const float inv_cpr = p.inv_cpr;
+#pragma unroll 1
+  for (int s = 0; s < kSlots; ++s) {
+    const int H = p.heads[s];
+    if (H == 0) continue;
+    const bool rotate = s < 2;
+    const int nch = H * G * cpr;
+    const __amdgpu_buffer_rsrc_t ry = buffer_of(
+        static_cast<char*>(p.y[s]) + t0 * p.y_ts[s] * ES,
+        (uint32_t)(((int64_t)(H - 1) * p.y_hs[s] + (int64_t)(nvalid - 1) * p.y_ts[s] + D) * ES));
+    const unsigned char* src = smem + lds_off[s];
+    const float inv_h = p.inv_heads[s];
+#pragma unroll 1
+    for (int k = tid; k < nch; k += kBlockThreads) {
+      const int o = div_small(k, cpr, inv_cpr);
+      const int c = k - o * cpr;
+      int h, g;
+      if (p.stage_hm) {
+        h = o / G;
+        g = o - h * G;
+      } else {
+        g = div_small(o, H, inv_h);
+        h = o - g * H;
+      }
+      const unsigned char* row = src + (g * H + h) * (D * ES);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c * 16);
+      Words<16> own;
+      own.w[0] = v.x; own.w[1] = v.y; own.w[2] = v.z; own.w[3] = v.w;
+      Words<16> out = own;
+      if (rotate && c * EC < rd) {
+        float a[EC];
+        unpack<BF16, EC>(own, a);
+#pragma unroll
+        for (int m = 0; m < EC / 2; ++m) {
+          const int col = c * EC + 2 * m;
+          if (col < rd) {
+            const bool first = col < half;
+            const int pcol = first ? col + half : col - half;
+            const int j = first ? col : col - half;
+            float b0, b1;
+            if constexpr (BF16) {
+              const uint32_t w = *reinterpret_cast<const uint32_t*>(row + pcol * 2);
+              b0 = bf_lo(w);
+              b1 = bf_hi(w);
+            } else {
+              const float2 w = *reinterpret_cast<const float2*>(row + pcol * 4);
+              b0 = w.x;
+              b1 = w.y;
+            }
+            const float4 cc = *reinterpret_cast<const float4*>(cs + g * half + j);
+            const float bb[2] = {b0, b1};
+            const float cv[2] = {cc.x, cc.z};
+            const float sv[2] = {cc.y, cc.w};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float y = a[2 * m + e];
+              if constexpr (PREC == MROPE_PRECISION_EXACT) {
+                const double sg = first ? -1.0 : 1.0;
+                a[2 * m + e] = (float)__builtin_fma((double)y, (double)cv[e],
+                                                    sg * ((double)bb[e] * (double)sv[e]));
+              } else {
+#pragma clang fp contract(off)
+                constexpr bool CAST = BF16 && PREC == MROPE_PRECISION_DTYPE;
+                float cf = cv[e], sf = sv[e];
+                if constexpr (CAST) {
+                  cf = round_bf16(cf);
+                  sf = round_bf16(sf);
+                }
+                float po = y * cf;
+                float pq = bb[e] * sf;
+                if constexpr (CAST) {
+                  po = round_bf16(po);
+                  pq = round_bf16(pq);
+                }
+                a[2 * m + e] = first ? po - pq : po + pq;
+              }
+            }
+          }
+        }
+        pack<BF16, EC>(a, out);
+      }
+      const uint32_t yo = g < nvalid
+          ? (uint32_t)(((int64_t)h * p.y_hs[s] + (int64_t)g * p.y_ts[s]) * ES) + (uint32_t)c * 16u
+          : kOutOfRange;
+      buf_store<BF16, 16>(ry, yo, out);
+    }
+  }
+}
+
+template <bool BF16, int PREC, int G>
+int launch_stage_t(const QKParams& p, const ColTable& tab, hipStream_t st) {
+  constexpr int ES = BF16 ? 2 : 4;
+  const int64_t blocks = (p.T + G - 1) / G;
+  int lds = G * p.half * (int)sizeof(float2);
+  for (int s = 0; s < kSlots; ++s)
+    if (p.heads[s] > 0) lds += stage_slot_bytes(G, p.heads[s], p.D, ES);
+  if (lds > kLdsPerCu) return (int)hipErrorInvalidValue;
+  if (p.waves_cap > 0) {
+    const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
+    if (cap_lds > lds) lds = cap_lds;
+  }
+  hipLaunchKernelGGL((stage_kernel<BF16, PREC, G>), dim3((unsigned)blocks), dim3(kBlockThreads),
+                     lds, st, p, tab);
+  return (int)hipGetLastError();
+}
+
+template <bool BF16, int G>
+int launch_stage_g(int prec, const QKParams& p, const ColTable& tab, hipStream_t st) {
+  switch (prec) {
+    case MROPE_PRECISION_EXACT: return launch_stage_t<BF16, MROPE_PRECISION_EXACT, G>(p, tab, st);
+    case MROPE_PRECISION_DTYPE: return launch_stage_t<BF16, MROPE_PRECISION_DTYPE, G>(p, tab, st);
+    case MROPE_PRECISION_FP32:
+      if constexpr (BF16) return launch_stage_t<BF16, MROPE_PRECISION_FP32, G>(p, tab, st);
+      break;
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <bool BF16>
+int launch_stage_d(int prec, int G, const QKParams& p, const ColTable& tab, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_stage_g<BF16, 1>(prec, p, tab, st);
+    case 2: return launch_stage_g<BF16, 2>(prec, p, tab, st);
+    case 4: return launch_stage_g<BF16, 4>(prec, p, tab, st);
+    case 8: return launch_stage_g<BF16, 8>(prec, p, tab, st);
+    case 16: return launch_stage_g<BF16, 16>(prec, p, tab, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
 // cos/sin tables [T][rd]: one thread per (token, column < half).
 __global__ void __launch_bounds__(256) cos_sin_kernel(const CosSinParams p, const ColTable tab) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -967,6 +1200,21 @@ int launch_flat(int dtype, int vec, int prec, const QKParams& p, const ColTable&
     }
   }
   return (int)hipErrorInvalidValue;
+}
+
+int launch_stage(int dtype, int prec, int G, const QKParams& p, const ColTable& tab,
+                 void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return dtype == MROPE_DTYPE_BF16 ? launch_stage_d<true>(prec, G, p, tab, st)
+                                   : launch_stage_d<false>(prec, G, p, tab, st);
+}
+
+int stage_lds_bytes(int dtype, int G, const QKParams& p) {
+  const int es = dtype == MROPE_DTYPE_BF16 ? 2 : 4;
+  int lds = G * p.half * 8;
+  for (int s = 0; s < kSlots; ++s)
+    if (p.heads[s] > 0) lds += stage_slot_bytes(G, p.heads[s], p.D, es);
+  return lds;
 }
 
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream) {
