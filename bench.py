@@ -290,7 +290,8 @@ def bench_vision_qkv(args):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name)
                      if args.precision == "exact" and not args.cs_cache else None,
-                     "algorithmic_bytes": alg, "kernel": "qk_kernel (mrope_vision_qkv)"},
+                     "algorithmic_bytes": alg,
+                     "kernel": f"{M.last_kernel()} (mrope_vision_qkv)"},
     }
     if not args.no_cpu_baseline:
         from oracle import mrope_oracle as O
@@ -465,8 +466,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "kernel": "qk_kernel (mrope_decode_qk)" if decode
-                     else "qk_kernel (rmsnorm_mrope_qk)"},
+                     "kernel": f"{M.last_kernel()} (mrope_decode_qk)" if decode
+                     else f"{M.last_kernel()} (rmsnorm_mrope_qk)"},
     }
     if not decode and args.cs_cache:
         line["config"]["cs_cache"] = cache_info

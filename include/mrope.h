@@ -384,6 +384,18 @@ int mrope_vision_pos_ids(const int32_t* grid_thw, int n_images, int spatial_merg
  */
 const char* mrope_last_error(void);
 
+/*
+ * mrope_last_kernel — name of the kernel that the last q/k launch on this
+ * thread (rms_norm, apply_rotary_qk, rmsnorm_mrope_qk[_cached],
+ * mrope_decode_qk, mrope_vision_qkv) enqueued: "qk_kernel" (rows spread over
+ * lane groups, the general path), "flat_kernel" (a token's block of rows
+ * lane after lane) or "stage_kernel" (rows staged through LDS, written in
+ * output order); empty string before the first launch.  A diagnostic for
+ * profiles and benchmarks: the choice depends on the shapes, dtype and
+ * layout only, never on the values.  Static storage; no ownership.
+ */
+const char* mrope_last_kernel(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,6 +168,13 @@ def test_fused_T_zero_is_a_noop():
 
 
 @fake_ptr_test
+def test_last_kernel_names_no_launch_without_one():
+    # argument checks and T = 0 launch nothing, so the name stays empty
+    assert _fused(T=0) == _lib.MROPE_OK
+    assert _lib.load().mrope_last_kernel() == b""
+
+
+@fake_ptr_test
 def test_in_place_alias_is_allowed_by_the_checks():
     # exact alias passes every check; with T = 0 nothing is launched
     assert _fused(T=0, qo=FAKE, ko=FAKE + 0x4000000) == _lib.MROPE_OK

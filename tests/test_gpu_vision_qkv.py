@@ -160,3 +160,19 @@ def test_vision_qkv_staged_without_v_and_cached(M):
     cache = M.mrope_cos_sin_cache(36, 1e4, 3000, device="cuda")   # vision: dim = rotary_dim / 2
     cq, ck, _ = _run(M, qkv, pos, "bf16", 72, 1e4, cs_cache=cache)
     assert np.array_equal(cq, gq) and np.array_equal(ck, gk)
+
+
+def test_kernel_choice_by_shape(M):
+    """bf16 planes of 2048+ tokens take the staged kernel, fp32 planes and
+    token-major vision rows the flat one, short launches the general one."""
+    import torch
+    for dtype, n, head_major, want in [("bf16", 2048, True, "stage_kernel"),
+                                       ("f32", 2048, True, "flat_kernel"),
+                                       ("bf16", 2048, False, "flat_kernel"),
+                                       ("bf16", 2047, True, "qk_kernel")]:
+        qkv = torch.zeros((n, 3, 16, 72), dtype=torch.bfloat16 if dtype == "bf16"
+                          else torch.float32, device="cuda")
+        pos = torch.zeros((2, n), dtype=torch.int32, device="cuda")
+        M.vision_qkv(qkv, pos, 72, 1e4, head_major=head_major)
+        torch.cuda.synchronize()
+        assert M.last_kernel() == want, (dtype, n, head_major, M.last_kernel())

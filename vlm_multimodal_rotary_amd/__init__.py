@@ -18,7 +18,7 @@ from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUTS, PRECISIONS, MropeError, check
 
 __all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "mrope_cos_sin_cache", "rms_norm",
            "apply_rotary_qk", "rmsnorm_mrope_qk", "mrope_decode_qk", "vision_qkv", "rope_index",
-           "vision_pos_ids", "MropeError", "load"]
+           "vision_pos_ids", "last_kernel", "MropeError", "load"]
 
 
 def _torch():
@@ -307,3 +307,9 @@ def vision_pos_ids(grid_thw, n_tokens: int, merge: int = 2, check: bool = True):
     if check:
         _raise_on_status(status)
     return pos, status
+
+
+def last_kernel() -> str:
+    """Name of the kernel the last q/k call on this thread launched
+    ("qk_kernel", "flat_kernel" or "stage_kernel"; "" before any)."""
+    return load().mrope_last_kernel().decode()

@@ -81,6 +81,7 @@ SIGNATURES = {
                                   _vp, _c_i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "mrope_vision_pos_ids": (_c_int, [_vp, _c_int, _c_int, _c_i64, _vp, _c_i64, _vp, _vp]),
     "mrope_last_error": (ctypes.c_char_p, []),
+    "mrope_last_kernel": (ctypes.c_char_p, []),
 }
 
 _LIB = None

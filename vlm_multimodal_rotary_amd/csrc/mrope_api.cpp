@@ -16,6 +16,7 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local const char* g_last_kernel = "";
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -502,13 +503,16 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
     for (int s = 0; s < kSlots; ++s) p.inv_heads[s] = 1.0f / (float)(a.heads[s] > 0 ? a.heads[s] : 1);
     p.waves_cap = waves_per_simd_stage();
     hrc = mrope::launch_stage(a.dtype, prec, G, p, tab, stream);
+    g_last_kernel = "stage_kernel";
   } else if (use_flat(a, cs_mode, norm, v, es)) {
     p.inv_cpr = 1.0f / (float)(a.D / v);
     p.waves_cap = waves_per_simd_flat();
     hrc = mrope::launch_flat(a.dtype, v, prec, p, tab, stream);
+    g_last_kernel = "flat_kernel";
   } else {
     p.waves_cap = waves_per_simd(a, v, es);
     hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, prec, p, tab, nt_cap, stream);
+    g_last_kernel = "qk_kernel";
   }
   if (hrc != (int)hipSuccess)
     return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
@@ -1013,5 +1017,7 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
 }
 
 const char* mrope_last_error(void) { return g_err.c_str(); }
+
+const char* mrope_last_kernel(void) { return g_last_kernel; }
 
 }  // extern "C"
