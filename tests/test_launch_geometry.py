@@ -311,6 +311,7 @@ def test_flat_every_output_written_once(T, heads, D, rd, es, v, head_major):
 
 BLOCK = WAVE * WPB
 STAGE_LDS_MAX = 64 * 1024   # LDS bytes a staged block may take (kStageLdsMax)
+STAGE_V = 3                 # v chunks per lane in registers (kStageV)
 
 
 def stage_slot_bytes(G, H, D, es):
@@ -337,19 +338,20 @@ def simulate_stage(T, heads, D, rd, es, G, head_major, x_pad=0):
     inv_half = f32(f32(1.0) / f32(half))
     writes = [np.zeros((T, H, D), dtype=np.int32) for H in heads]
     offs, off = [], 0
-    for H in heads:
+    for H in heads[:2]:                 # q and k go through LDS, v through registers
         offs.append(off)
         if H:
             off += stage_slot_bytes(G, H, D, es)
     cs_bytes = G * half * 8
     assert off % 16 == 0 and off + cs_bytes <= STAGE_LDS_MAX
+    assert G * heads[2] * cpr <= STAGE_V * BLOCK
     lanes = np.arange(WAVE)
     tid = np.arange(BLOCK)
     for blk in range(-(-T // G)):
         t0 = blk * G
         nvalid = min(G, T - t0)
-        # phase 1
-        for s, H in enumerate(heads):
+        # phase 1 (q and k to LDS)
+        for s, H in enumerate(heads[:2]):
             if H == 0:
                 continue
             rcs = H * cpr
@@ -374,8 +376,35 @@ def simulate_stage(T, heads, D, rd, es, G, head_major, x_pad=0):
         i = np.arange(G * half)
         g = div_small(i, half, inv_half)
         assert np.all(g == i // half) and np.all(g < G)
-        # phase 3
-        for s, H in enumerate(heads):
+        # v: chunks in output order straight to registers, then stored
+        H = heads[2]
+        if H:
+            nch = H * G * cpr
+            x_ts = H * D + x_pad
+            tsb = x_ts * es
+            in_extent = (nvalid - 1) * tsb + H * cpr * 16
+            yhs = T * D + 8 * ec if head_major else D
+            yts = D if head_major else H * D + 8 * ec
+            out_extent = ((H - 1) * yhs + (nvalid - 1) * yts + D) * es
+            inv_h = f32(f32(1.0) / f32(H))
+            for j in range(STAGE_V):
+                k = tid + j * BLOCK
+                kk = np.where(k < nch, k, 0)
+                o = div_small(kk, cpr, inv_cpr)
+                c = kk - o * cpr
+                if head_major:
+                    h, g = o // G, o % G
+                else:
+                    g = div_small(o, H, inv_h)
+                    h = o - g * H
+                ok = (k < nch) & (g < nvalid)
+                assert np.all(g[ok] * tsb + (h[ok] * cpr + c[ok]) * 16 + 16 <= in_extent)
+                yo = (h * yhs + g * yts) * es + c * 16
+                assert np.all(yo[ok] + 16 <= out_extent)
+                for qq in np.nonzero(ok)[0]:
+                    writes[2][t0 + g[qq], h[qq], c[qq] * ec:c[qq] * ec + ec] += 1
+        # phase 3 (q and k from LDS)
+        for s, H in enumerate(heads[:2]):
             if H == 0:
                 continue
             nch = H * G * cpr
@@ -414,13 +443,13 @@ def simulate_stage(T, heads, D, rd, es, G, head_major, x_pad=0):
 
 
 @pytest.mark.parametrize("T,heads,D,rd,es,G", [
-    (20, (16, 16, 16), 72, 72, 2, 8),      # vision qkv bf16 planes
-    (9, (16, 16, 16), 72, 72, 4, 4),       # vision qkv fp32 planes
-    (11, (16, 16, 0), 72, 72, 4, 4),       # vision_2d fp32
+    (22, (16, 16, 16), 72, 72, 2, 4),      # vision qkv bf16 planes
+    (9, (16, 16, 16), 72, 72, 4, 2),       # vision qkv fp32 planes
+    (11, (16, 16, 0), 72, 72, 4, 4),       # vision_2d fp32 (no v)
     (5, (28, 4, 0), 128, 128, 2, 2),
     (7, (5, 3, 2), 80, 48, 4, 4),          # partial rotary
-    (3, (10, 2, 0), 384, 384, 4, 2),
-    (37, (3, 1, 0), 8, 4, 2, 16),          # the smallest even half            # the smallest even half
+    (3, (10, 2, 3), 384, 384, 4, 2),
+    (37, (3, 1, 2), 8, 4, 2, 16),          # the smallest even half
 ])
 @pytest.mark.parametrize("head_major", [False, True])
 @pytest.mark.parametrize("x_pad", [0, 8])

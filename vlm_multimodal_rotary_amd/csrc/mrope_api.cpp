@@ -495,8 +495,12 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   // budget: five or more resident blocks per compute unit keep enough bytes
   // in flight (a block holds its LDS from its first load to its last store).
   const int budget = env_int("MROPE_STAGE_G", 0) > 0 ? kStageLdsMax : kStageLdsTarget;
-  while (G > 1 && mrope::stage_lds_bytes(a.dtype, G, p) > budget) G /= 2;
-  if (G > 0 && mrope::stage_lds_bytes(a.dtype, G, p) > budget) G = 0;
+  auto fits = [&](int g) {
+    return mrope::stage_lds_bytes(a.dtype, g, p) <= budget &&
+           (int64_t)g * a.heads[2] * (a.D * es / 16) <= mrope::stage_max_v_chunks();
+  };
+  while (G > 1 && !fits(G)) G /= 2;
+  if (G > 0 && !fits(G)) G = 0;
   if (G > 0) {
     p.stage_hm = head_major ? 1 : 0;
     p.inv_cpr = 1.0f / (float)(a.D * es / 16);

@@ -156,6 +156,8 @@ int launch_flat(int dtype, int vec, int prec, const QKParams& p, const ColTable&
 int launch_stage(int dtype, int prec, int G, const QKParams& p, const ColTable& tab,
                  void* stream);
 int stage_lds_bytes(int dtype, int G, const QKParams& p);
+// 16-byte chunks of the copied tensor (v) a staged block holds in registers.
+int stage_max_v_chunks();
 // cos/sin cache by position: cache[(p * n_freq + i) * 2 + {0, 1}] = (cos, sin)
 // of fl32(float(p) * tab.inv[i]) for p < rows, i < n_freq.
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream);

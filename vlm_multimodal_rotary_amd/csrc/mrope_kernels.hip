@@ -810,16 +810,19 @@ int launch_flat_v(int prec, const QKParams& p, const ColTable& tab, hipStream_t 
 
 // ---------------------------------------------------------------------------
 // The staged q/k kernel (no RMSNorm, cos/sin from positions).  A block owns G
-// consecutive tokens.  It first copies their rows of every tensor into LDS
-// with direct buffer-to-LDS loads (one wavefront instruction moves 64 chunks
-// of 16 bytes, consecutive in LDS) while it forms the G tokens' cos/sin,
-// then writes the output 16 bytes per lane: in head-major order the G rows
-// of a head go out back to back, one contiguous run per plane, and in
-// token-major order a token's heads do.  This is the layout transposition of
-// the vision tower's packed qkv into per-head planes; rows whose width is not
-// a whole number of cache lines also gain from writing whole runs.
+// consecutive tokens.  It copies their q and k rows into LDS with direct
+// buffer-to-LDS loads (one wavefront instruction moves 64 chunks of 16 bytes,
+// consecutive in LDS) and forms the G tokens' cos/sin; the copied tensor (v)
+// skips LDS, each lane loading its 16-byte chunks in output order straight
+// into registers.  After one barrier it writes v, then q and k rotated, 16
+// bytes per lane in output order: in head-major order the G rows of a head go
+// out back to back, one contiguous run per plane, and in token-major order a
+// token's heads do.  This is the layout transposition of the vision tower's
+// packed qkv into per-head planes.  Keeping v out of LDS lets eight blocks
+// share a compute unit instead of five.
 // Requirements (checked by the host): 16-byte aligned bases, strides and row
-// widths (D * ES), an even rotary half.
+// widths (D * ES), an even rotary half, at most kStageV * 256 chunks of v per
+// block.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -840,6 +843,34 @@ __host__ __device__ __forceinline__ int stage_slot_bytes(int G, int heads, int D
   return ((chunks + kWaveSize - 1) / kWaveSize) * kWaveSize * 16;
 }
 
+// The copied tensor (v) skips LDS: each lane loads its 16-byte chunks in
+// output order straight into registers, kStageV of them at most.
+constexpr int kStageV = 3;
+constexpr int kStageLdsSlots = 2;     // q and k go through LDS
+// s_waitcnt immediate for vmcnt(kStageV) expcnt(0) lgkmcnt(0) (gfx9 fields:
+// vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8, vmcnt high bits 15:14 zero)
+constexpr int kWaitVmcntStageV = kStageV;
+static_assert(kStageV < 16, "vmcnt field");
+
+// Output chunk k (k >= 0) of a tensor with H heads in a group: head h, token
+// g, chunk c; head-major order runs over (h, g, c), token-major over (g, h, c).
+struct StageChunk {
+  int h, g, c;
+};
+
+template <int G>
+__device__ __forceinline__ StageChunk stage_split(int k, int cpr, float inv_cpr, int H,
+                                                  float inv_h, bool head_major) {
+  const int o = div_small(k, cpr, inv_cpr);
+  const int hh = (int)((uint32_t)o / (uint32_t)G);
+  const int gt = div_small(o, H, inv_h);
+  StageChunk r;
+  r.c = k - o * cpr;
+  r.h = head_major ? hh : o - gt * H;
+  r.g = head_major ? o - hh * G : gt;
+  return r;
+}
+
 template <bool BF16, int PREC, int G>
 __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -854,18 +885,19 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
   const int D = p.D, half = p.half, rd = p.rd;
   const int cpr = D * ES / 16;         // chunks per head row
 
-  int lds_off[kSlots];
+  int lds_off[kStageLdsSlots];
   int off = 0;
 #pragma unroll
-  for (int s = 0; s < kSlots; ++s) {
+  for (int s = 0; s < kStageLdsSlots; ++s) {
     lds_off[s] = off;
     if (p.heads[s] > 0) off += stage_slot_bytes(G, p.heads[s], D, ES);
   }
   float2* cs = reinterpret_cast<float2*>(smem + off);   // [G][half]
+  const float inv_cpr = p.inv_cpr;
 
-  // 1. token rows of each tensor to LDS, in memory order [g][head][D]
+  // 1. token rows of q and k to LDS, in memory order [g][head][D]
 #pragma unroll 1
-  for (int s = 0; s < kSlots; ++s) {
+  for (int s = 0; s < kStageLdsSlots; ++s) {
     const int H = p.heads[s];
     if (H == 0) continue;
     const int rcs = H * cpr;                            // chunks per token
@@ -907,16 +939,58 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
       cs[i] = make_float2(c, sn);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  // 2b. v chunks in output order to registers, issued last: the wait below
+  // leaves them in flight through step 3
+  Words<16> rv[kStageV];
+  {
+    const int H = p.heads[2];
+    const int nch = H * G * cpr;
+    const uint32_t tsb = (uint32_t)(p.x_ts[2] * ES);
+    const __amdgpu_buffer_rsrc_t rx = buffer_of(
+        static_cast<const char*>(p.x[2]) + t0 * p.x_ts[2] * ES,
+        H > 0 ? (uint32_t)(nvalid - 1) * tsb + (uint32_t)(H * cpr) * 16u : 0u);
+#pragma unroll
+    for (int j = 0; j < kStageV; ++j) {
+      const int k = tid + j * kBlockThreads;
+      const StageChunk q = stage_split<G>(k < nch ? k : 0, cpr, inv_cpr, H > 0 ? H : 1,
+                                          p.inv_heads[2], p.stage_hm != 0);
+      const bool ok = k < nch && q.g < nvalid;
+      buf_load<16>(rx, ok ? (uint32_t)q.g * tsb + (uint32_t)(q.h * cpr + q.c) * 16u : kOutOfRange,
+                   rv[j]);
+    }
+  }
+
+  // every load but the last kStageV (the v chunks) has landed; LDS writes too
+  __builtin_amdgcn_s_waitcnt(kWaitVmcntStageV);
   __syncthreads();
 
-  // 3. rotate (q, k) or copy (v) 16 bytes per lane; write in output order
-  const float inv_cpr = p.inv_cpr;
+  // 3. v from registers (its loads have had the barrier's wait to land)
+  {
+    const int H = p.heads[2];
+    const int nch = H * G * cpr;
+    const __amdgpu_buffer_rsrc_t ry = buffer_of(
+        static_cast<char*>(p.y[2]) + t0 * p.y_ts[2] * ES,
+        H > 0 ? (uint32_t)(((int64_t)(H - 1) * p.y_hs[2] + (int64_t)(nvalid - 1) * p.y_ts[2] + D)
+                           * ES) : 0u);
+#pragma unroll
+    for (int j = 0; j < kStageV; ++j) {
+      const int k = tid + j * kBlockThreads;
+      const StageChunk q = stage_split<G>(k < nch ? k : 0, cpr, inv_cpr, H > 0 ? H : 1,
+                                          p.inv_heads[2], p.stage_hm != 0);
+      const uint32_t yo = k < nch && q.g < nvalid
+          ? (uint32_t)(((int64_t)q.h * p.y_hs[2] + (int64_t)q.g * p.y_ts[2]) * ES) +
+                (uint32_t)q.c * 16u
+          : kOutOfRange;
+      buf_store<BF16, 16>(ry, yo, rv[j]);
+    }
+  }
+
+  // 4. rotate q and k 16 bytes per lane; write in output order
 #pragma unroll 1
-  for (int s = 0; s < kSlots; ++s) {
+  for (int s = 0; s < kStageLdsSlots; ++s) {
     const int H = p.heads[s];
     if (H == 0) continue;
-    const bool rotate = s < 2;
+    const bool rotate = true;
     const int nch = H * G * cpr;
     const __amdgpu_buffer_rsrc_t ry = buffer_of(
         static_cast<char*>(p.y[s]) + t0 * p.y_ts[s] * ES,
@@ -925,16 +999,8 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
     const float inv_h = p.inv_heads[s];
 #pragma unroll 1
     for (int k = tid; k < nch; k += kBlockThreads) {
-      const int o = div_small(k, cpr, inv_cpr);
-      const int c = k - o * cpr;
-      int h, g;
-      if (p.stage_hm) {
-        h = o / G;
-        g = o - h * G;
-      } else {
-        g = div_small(o, H, inv_h);
-        h = o - g * H;
-      }
+      const StageChunk q = stage_split<G>(k, cpr, inv_cpr, H, inv_h, p.stage_hm != 0);
+      const int h = q.h, g = q.g, c = q.c;
       const unsigned char* row = src + (g * H + h) * (D * ES);
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c * 16);
       Words<16> own;
@@ -998,6 +1064,7 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
       buf_store<BF16, 16>(ry, yo, out);
     }
   }
+
 }
 
 template <bool BF16, int PREC, int G>
@@ -1005,7 +1072,7 @@ int launch_stage_t(const QKParams& p, const ColTable& tab, hipStream_t st) {
   constexpr int ES = BF16 ? 2 : 4;
   const int64_t blocks = (p.T + G - 1) / G;
   int lds = G * p.half * (int)sizeof(float2);
-  for (int s = 0; s < kSlots; ++s)
+  for (int s = 0; s < kStageLdsSlots; ++s)
     if (p.heads[s] > 0) lds += stage_slot_bytes(G, p.heads[s], p.D, ES);
   if (lds > kLdsPerCu) return (int)hipErrorInvalidValue;
   if (p.waves_cap > 0) {
@@ -1212,10 +1279,12 @@ int launch_stage(int dtype, int prec, int G, const QKParams& p, const ColTable& 
 int stage_lds_bytes(int dtype, int G, const QKParams& p) {
   const int es = dtype == MROPE_DTYPE_BF16 ? 2 : 4;
   int lds = G * p.half * 8;
-  for (int s = 0; s < kSlots; ++s)
+  for (int s = 0; s < kStageLdsSlots; ++s)
     if (p.heads[s] > 0) lds += stage_slot_bytes(G, p.heads[s], p.D, es);
   return lds;
 }
+
+int stage_max_v_chunks() { return kStageV * kBlockThreads; }
 
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream) {
   const int64_t n = (int64_t)rows * n_freq;
