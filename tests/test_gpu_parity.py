@@ -398,3 +398,26 @@ def test_flat_kernel_geometries(M, dtype, D, rd, heads, layout, section):
         assert_close(from_dev(ko)[rows], ok, dtype, "flat k")
     if rd < D:
         assert np.array_equal(from_dev(qo)[..., rd:], q[..., rd:])
+
+
+@pytest.mark.parametrize("heads", [(16, 16), (32, 8)], ids=["one-batch", "rows-across-batches"])
+def test_in_place_long_launch_matches_out_of_place(M, heads):
+    """In place on 2048+ tokens of 72-wide fp32 rows (the flat kernel's
+    shapes): bit-identical to the out-of-place call, also where a token's
+    rows span more than one of the flat kernel's load batches."""
+    import torch
+    T = 2100
+    rng = np.random.default_rng(91)
+    q, k = W.random_qk(rng, T, heads[0], heads[1], 72, "f32")
+    pos = rng.integers(0, 5000, (2, T)).astype(np.int32)
+    note(f"in place, long launch, heads {heads}")
+    qd, kd, pd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(pos, "i32")
+    qo, ko = M.rmsnorm_mrope_qk(qd, kd, pd, 72, 1e4, None, "vision_2d")
+    qi, ki = qd.clone(), kd.clone()
+    M.rmsnorm_mrope_qk(qi, ki, pd, 72, 1e4, None, "vision_2d", q_out=qi, k_out=ki)
+    torch.cuda.synchronize()
+    assert torch.equal(qi, qo) and torch.equal(ki, ko)
+    oq, ok = O.rmsnorm_mrope_qk(q[:64], k[:64], pos[:, :64], rotary_dim=72, theta=1e4,
+                                section=None, layout="vision_2d", dtype="f32")
+    assert_close(from_dev(qi)[:64], oq, "f32", "in place q")
+    assert_close(from_dev(ki)[:64], ok, "f32", "in place k")

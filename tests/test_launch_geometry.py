@@ -458,3 +458,35 @@ def test_stage_every_output_written_once(T, heads, D, rd, es, G, head_major, x_p
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))
+
+
+FLAT_BATCH = WAVE * FLAT_STEPS
+
+
+def flat_in_place_hazard(H, D, rd, v):
+    """True if a rotary chunk of the flat kernel reads its partner from a
+    batch that was stored before (which breaks in-place calls)."""
+    cpr, hc, rc = D // v, (rd // 2) // v, rd // v
+    for f in range(H * cpr):
+        c = f % cpr
+        if c < rc:
+            fp = f + hc if c < hc else f - hc
+            if fp // FLAT_BATCH < f // FLAT_BATCH:
+                return True
+    return False
+
+
+def test_flat_in_place_rule_covers_every_hazard():
+    """The host keeps in-place tensors off the flat kernel when a token's
+    rows exceed one batch; every geometry with a hazard is such a case."""
+    seen = 0
+    for D in (8, 16, 24, 40, 48, 72, 80, 96, 128, 144, 200, 256):
+        for v in (1, 2, 4, 8):
+            for rd in range(2 * v, D + 1, 2 * v):
+                if D % (2 * v) or (rd // 2) % v or (D - rd) % (2 * v):
+                    continue
+                for H in (1, 3, 5, 16, 21, 32, 40):
+                    if flat_in_place_hazard(H, D, rd, v):
+                        seen += 1
+                        assert H * (D // v) > FLAT_BATCH, (H, D, rd, v)
+    assert seen > 0

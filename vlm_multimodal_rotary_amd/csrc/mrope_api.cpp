@@ -327,13 +327,19 @@ int env_int(const char* name, int fallback) {
 // The flat kernel (chunks of the token's block lane after lane) serves the
 // positions path without RMSNorm for launches of at least one wavefront per
 // token over the whole chip.  It is chosen where the per-row mapping leaves
-// rows straddling cache lines (row bytes not a multiple of 256).
-// MROPE_FLAT=0/1 in the environment forces the choice (tuning).
+// rows straddling cache lines (row bytes not a multiple of 256).  An
+// in-place tensor qualifies only if a token's rows fit one load batch (the
+// kernel stores a batch before it loads the next, and a rotary partner may
+// sit in the next batch).  MROPE_FLAT=0/1 in the environment forces the
+// choice where it is allowed (tuning).
 bool use_flat(const QKArgs& a, int cs_mode, bool norm, int v, int es) {
   if (cs_mode != mrope::kCsFromPositions || norm || a.T < kFlatMinTokens) return false;
+  for (int s = 0; s < kSlots; ++s)
+    if (a.heads[s] > 0 && a.x[s] == a.y[s] &&
+        (int64_t)a.heads[s] * (a.D / v) > mrope::kFlatBatchChunks)
+      return false;
   static const int env = env_int("MROPE_FLAT", -1);
   if (env >= 0) return env != 0;
-  (void)v;
   return (a.D * es) % 256 != 0;
 }
 
@@ -346,13 +352,15 @@ int waves_per_simd_flat() {
   return 4;
 }
 
-// The staged kernel (rows copied to LDS G tokens at a time, written back in
-// output order) serves the positions path without RMSNorm when every base,
-// stride and row is 16-byte aligned and the rotary half is even.  It is
-// chosen for bfloat16 head-major outputs (per-head planes), where it writes
-// each head's G rows as one run: 69% of HBM peak on 16 x 72 bf16 planes
-// against 51% for the flat kernel.  For binary32 planes and token-major rows
-// the flat kernel measured faster (65% and 72% against 60% and 61%).
+// The staged kernel (q/k rows copied to LDS G tokens at a time, written back
+// in output order; v through registers) serves the positions path without
+// RMSNorm when every base, stride and row is 16-byte aligned and the rotary
+// half is even.  It is chosen for bfloat16 head-major outputs (per-head
+// planes), where it writes each head's G rows as one run: 74% of HBM peak on
+// 16 x 72 bf16 planes against 51% for the flat kernel.  For binary32 planes
+// and token-major rows the flat kernel measured faster (64% and 72% against
+// 58% and 61%).  Every read of a block lands before its first write, so
+// in-place calls are safe.
 // Returns the largest G to try (the caller shrinks it to the LDS budget), or
 // 0 for another kernel.  MROPE_STAGE=0/1 and MROPE_STAGE_G in the
 // environment force the choice.

@@ -11,6 +11,10 @@ constexpr int kMaxHalf = MROPE_MAX_ROTARY_DIM / 2;
 constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
+// Chunks the flat kernel loads before it stores any (six per lane).  A row
+// whose halves fall in different batches reads its partner after the first
+// batch's stores, so an in-place tensor must fit one batch per token.
+constexpr int kFlatBatchChunks = 6 * kWaveSize;
 
 // Per frequency column j < half: the binary32 inverse frequency it multiplies
 // and the position axis it reads.  Passed by value as a kernel argument; the

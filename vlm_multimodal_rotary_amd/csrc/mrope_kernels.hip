@@ -663,6 +663,7 @@ qk_kernel(const QKParams p, const ColTable tab) {
 // ---------------------------------------------------------------------------
 
 constexpr int kFlatSteps = 6;
+static_assert(kFlatSteps * kWaveSize == kFlatBatchChunks, "one batch of the flat kernel");
 
 template <bool BF16, int V, int PREC>
 __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, const ColTable tab) {
