@@ -131,7 +131,7 @@ def carry_parallel(summaries, B, C, threads):
     per = -(-n // threads) if n else 0
     rng = [(min(n, t * per), min(n, t * per + per)) for t in range(threads)]
     S = [list(x) for x in summaries]
-    # round 1
+    # pass 1
     t_nv = [sum(S[c][0] for c in range(a, b)) for a, b in rng]
     t_nt = [sum(S[c][1] for c in range(a, b)) for a, b in rng]
     t_lt = []
@@ -144,7 +144,7 @@ def carry_parallel(summaries, B, C, threads):
     gF_ex, _ = _excl_sum(t_nv)
     gA_ex, _ = _excl_sum(t_nt)
     lt_ex, _ = _excl_max(t_lt, -1)
-    # round 2
+    # pass 2
     t_ni, t_nvd, t_st = [], [], []
     for t, (a, b) in enumerate(rng):
         gF, gA, lt = gF_ex[t], gA_ex[t], lt_ex[t]

@@ -326,10 +326,10 @@ __device__ __forceinline__ int64_t video_adv_before(const Tables& tb, int k) {
 // The carry of chunk c is a scan over the chunks before it.  Per-sample
 // quantities restart at each sample's first chunk b*C; they are taken as the
 // batch-wide prefix at c minus the prefix at b*C.  Each thread owns a
-// contiguous range of chunks; block scans combine the ranges in three rounds
+// contiguous range of chunks; block scans combine the ranges in three passes
 // (valid/text counts and the latest valid type; segment starts by type and
 // the latest start; the sample bases), with provisional per-chunk records in
-// the summary slots between rounds.  Batch-wide filtered indices are below
+// the summary slots between passes.  Batch-wide filtered indices are below
 // 2^29 (checked on the host), so (index << 2 | type) fits an int.
 // ---------------------------------------------------------------------------
 
@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
   const int c0 = min(n, (int)threadIdx.x * per);
   const int c1 = min(n, c0 + per);
   const int C = p.C > 0 ? p.C : 1;
-  // The rounds below re-read the per-chunk records several times: keep them
+  // The passes below re-read the per-chunk records several times: keep them
   // in LDS when they fit (the provisional records never go back to memory).
   __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
   int* const rec = n <= kPosCarryLds ? rec_lds : p.ws_sum;
@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
     __syncthreads();
   }
 
-  // Round 1: valid / text counts, the latest valid type, summary flags.
+  // Pass 1: valid / text counts, the latest valid type, summary flags.
   int t_nv = 0, t_nt = 0, t_lt = -1, t_flags = 0;
   for (int c = c0; c < c1; ++c) {
     const int* s = rec + (int64_t)c * kPosSumInts;
@@ -406,7 +406,7 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
   int lt = block_excl_max(t_lt, -1, &tot, sh);
   const int flags = block_or(t_flags, sh);
 
-  // Round 2: segment starts (the first valid token of a chunk starts a
+  // Pass 2: segment starts (the first valid token of a chunk starts a
   // segment when the latest valid type before it in its sample differs).
   int t_ni = 0, t_nvd = 0, t_st = -1;
   {
@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
   int vid = block_excl_sum(t_nvd, &vid_total, sh);
   int st = block_excl_max(t_st, -1, &tot, sh);
 
-  // Round 3a: grid counters per chunk.
+  // Pass 3a: grid counters per chunk.
   for (int c = c0; c < c1; ++c) {
     int* s = rec + (int64_t)c * kPosSumInts;
     s[6] = img;
@@ -456,7 +456,7 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
   __threadfence_block();
   __syncthreads();
 
-  // Round 3b: carries relative to each sample's first chunk.
+  // Pass 3b: carries relative to each sample's first chunk.
   {
     int b = c0 / C, first = b * C;
     for (int c = c0; c < c1; ++c) {
