@@ -26,7 +26,7 @@ def pick_vec(es, D, rd, aligned_bytes=16, strides=()):
     return 0
 
 
-WAVE_TOKENS = 1   # tokens per wavefront at most (MROPE_WAVE_TOKENS)
+WAVE_TOKENS = 1   # tokens per wavefront without RMSNorm (the host takes 1, 2 or 4 with it)
 OUT_OF_RANGE = 0x80000000
 
 

@@ -493,6 +493,32 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
       return fail(MROPE_EUNSUPPORTED, "one token's rows of %s span 2^31 bytes or more",
                   s == 0 ? "q" : (s == 1 ? "k" : "v"));
   }
+  // Tokens per wavefront.  With RMSNorm on the positions path: the fewest
+  // tokens (1, 2 or 4) whose rows fill whole row-steps of every tensor, so
+  // no lane group runs the norm's arithmetic on a masked row -- 4 k heads at
+  // 8 rows per step take 2 tokens.  Measured on the 32 + 4 head bf16 prefill:
+  // 107.2 -> 103.0 us; launches without the norm, whose rows already fill
+  // their steps or that are bound by memory alone, ran slower with more
+  // tokens per wavefront.  MROPE_WAVE_TOKENS in the environment forces the
+  // count (tuning).
+  {
+    static const int env = env_int("MROPE_WAVE_TOKENS", 0);
+    int wave_tokens = 1;
+    if (env > 0) {
+      wave_tokens = env;
+    } else if (norm && cs_mode == mrope::kCsFromPositions) {
+      for (int n = 1; n <= 4; n *= 2) {
+        bool whole = true;
+        for (int s = 0; s < kSlots; ++s)
+          if (a.heads[s] > 0 && (n * a.heads[s]) % p.rpw != 0) whole = false;
+        if (whole) {
+          wave_tokens = n;
+          break;
+        }
+      }
+    }
+    if (nt_cap > wave_tokens) nt_cap = wave_tokens;
+  }
   // For binary32 tensors the cast of cos/sin to the dtype is the identity.
   const int prec = (a.dtype == MROPE_DTYPE_F32 && a.precision == MROPE_PRECISION_FP32)
                        ? MROPE_PRECISION_DTYPE : a.precision;

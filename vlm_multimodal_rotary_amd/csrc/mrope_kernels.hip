@@ -53,10 +53,6 @@
 #ifndef MROPE_MIN_WAVES
 #define MROPE_MIN_WAVES 2048
 #endif
-// Tokens per wavefront (at most; fewer when a token's cos/sin is large).
-#ifndef MROPE_WAVE_TOKENS
-#define MROPE_WAVE_TOKENS 1
-#endif
 
 namespace mrope {
 namespace {
@@ -1144,7 +1140,7 @@ __global__ void __launch_bounds__(256) cos_sin_cache_kernel(const ColTable tab, 
 template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
-  p.nt = nt_cap < MROPE_WAVE_TOKENS ? nt_cap : MROPE_WAVE_TOKENS;
+  p.nt = nt_cap;   // tokens per wavefront, chosen by the host
   if (p.nt < 1 || CS == kCsDecode) p.nt = 1;
   for (int s = 0; s < kSlots; ++s) {
     const int H = p.heads[s] > 0 ? p.heads[s] : 1;
