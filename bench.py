@@ -446,7 +446,7 @@ def main():
                   "precision": args.precision}
     line = {
         "metric": ("decode tokens/s, mrope_decode_qk" if decode else
-                   "Q+K tokens/s, fused RMSNorm+MRoPE (rmsnorm_mrope_qk)"),
+                   "Q+K tokens/s and achieved HBM GB/s (% of peak), fused RMSNorm+MRoPE"),
         "value": wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
