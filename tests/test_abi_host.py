@@ -327,3 +327,62 @@ def test_cache_arguments_are_checked():
     assert fused(FAKE + 0x30000004, 10) == _lib.MROPE_EINVAL    # misaligned cache
     assert fused(FAKE + 0x30000000, -1) == _lib.MROPE_EINVAL
     assert fused(FAKE + 0x20000000, 10) == _lib.MROPE_EINVAL    # cache overlaps q_out
+
+
+@fake_ptr_test
+def test_vision_qkv_rejects_bad_arguments():
+    lib = _lib.load()
+    n, H, D = 64, 4, 72
+
+    def call(**kw):
+        a = dict(qkv=FAKE, ts=3 * H * D, n=n, H=H, D=D, rd=72, pos=FAKE + 0x100000, ps=n,
+                 theta=1e4, dtype=_lib.DTYPE_F32, prec=_lib.PRECISION_EXACT,
+                 qo=FAKE + 0x200000, ko=FAKE + 0x300000, vo=FAKE + 0x400000, hs=n * D, ots=D,
+                 cache=None, rows=0)
+        a.update(kw)
+        return lib.mrope_vision_qkv(a["qkv"], a["ts"], a["n"], a["H"], a["D"], a["rd"], a["pos"],
+                                    a["ps"], a["theta"], a["dtype"], a["prec"], a["qo"], a["ko"],
+                                    a["vo"], a["hs"], a["ots"], a["cache"], a["rows"], None)
+
+    assert call(n=0) == _lib.MROPE_OK                         # nothing to do, nothing launched
+    for kw, code in [
+            (dict(H=-1), _lib.MROPE_EINVAL),
+            (dict(ts=3 * H * D - 1), _lib.MROPE_EINVAL),         # token stride below the rows
+            (dict(hs=0), _lib.MROPE_EINVAL),
+            (dict(ots=-D), _lib.MROPE_EINVAL),
+            (dict(hs=D, ots=D), _lib.MROPE_EINVAL),              # rows of two heads coincide
+            (dict(rd=74), _lib.MROPE_EINVAL),                    # rotary_dim > D
+            (dict(rd=70), _lib.MROPE_EINVAL),                    # odd vision half (35)
+            (dict(theta=0.0), _lib.MROPE_EINVAL),
+            (dict(pos=0), _lib.MROPE_EINVAL),
+            (dict(qkv=0), _lib.MROPE_EINVAL),
+            (dict(qo=0), _lib.MROPE_EINVAL),
+            (dict(prec=5), _lib.MROPE_EINVAL),
+            (dict(dtype=7), _lib.MROPE_EUNSUPPORTED),
+            (dict(qo=FAKE + 64), _lib.MROPE_EINVAL),             # q planes overlap the input
+            (dict(ko=FAKE + 0x200000 + 256), _lib.MROPE_EINVAL),  # k planes overlap q planes
+            (dict(vo=FAKE + 0x100000), _lib.MROPE_EINVAL),       # v planes overlap positions
+            (dict(cache=FAKE + 0x500004, rows=10), _lib.MROPE_EINVAL),   # misaligned cache
+    ]:
+        rc = call(**kw)
+        assert rc == code, (kw, rc, lib.mrope_last_error())
+        assert lib.mrope_last_error()
+
+
+@fake_ptr_test
+def test_buffers_beyond_32_bit_offsets_are_refused():
+    """A kernel addresses one token's rows (or one block's planes) through a
+    buffer descriptor with 32-bit byte offsets: a token whose rows span 2^31
+    bytes or more is refused before anything is enqueued."""
+    lib = _lib.load()
+    big = 1 << 23                      # heads of 128 bf16: one token's q rows = 2^31 bytes
+    rc = _fused(hq=big, q_ts=big * 128, qo_ts=big * 128, T=1, pos_stride=1,
+                k=FAKE + (1 << 36), qo=FAKE + (1 << 37), ko=FAKE + (1 << 38),
+                pos=FAKE + (1 << 39), wq=FAKE + (1 << 40), wk=FAKE + (1 << 40) + 4096)
+    assert rc == _lib.MROPE_EUNSUPPORTED, lib.mrope_last_error()
+    n, H, D = 1 << 20, 16, 72          # fp32 planes: (H - 1) * n * D * 4 bytes > 2^31
+    rc = lib.mrope_vision_qkv(FAKE, 3 * H * D, n, H, D, 72, FAKE + (1 << 39), n, 1e4,
+                              _lib.DTYPE_F32, _lib.PRECISION_EXACT, FAKE + (1 << 36),
+                              FAKE + (1 << 37), FAKE + (1 << 38), n * D, D, None, 0, None)
+    assert rc == _lib.MROPE_EUNSUPPORTED, lib.mrope_last_error()
+    assert b"2^31" in lib.mrope_last_error()
