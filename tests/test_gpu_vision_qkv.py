@@ -176,3 +176,20 @@ def test_kernel_choice_by_shape(M):
         M.vision_qkv(qkv, pos, 72, 1e4, head_major=head_major)
         torch.cuda.synchronize()
         assert M.last_kernel() == want, (dtype, n, head_major, M.last_kernel())
+
+
+def test_many_heads_fall_back_to_the_flat_kernel(M):
+    """bf16 planes whose v rows of one token exceed the staged kernel's
+    registers (96 heads of 72) take the flat kernel, with the same results."""
+    rng = np.random.default_rng(76)
+    n, H = 2048, 96
+    qkv = W._store(rng.standard_normal((n, 3, H, 72)).astype(np.float32), "bf16")
+    pos = rng.integers(0, 4096, (2, n)).astype(np.int32)
+    note("vision_qkv bf16 96 heads (flat fallback)")
+    gq, gk, gv = _run(M, qkv, pos, "bf16", 72, 1e4)
+    assert M.last_kernel() == "flat_kernel"
+    rows = np.array([0, 1, 777, n - 1])
+    oq, ok, ov = O.vision_qkv(qkv[rows], pos[:, rows], rotary_dim=72, theta=1e4, dtype="bf16")
+    assert_close(gq[:, rows], oq, "bf16", "fallback q")
+    assert_close(gk[:, rows], ok, "bf16", "fallback k")
+    assert np.array_equal(gv[:, rows].view(np.uint8), ov.view(np.uint8))
