@@ -403,42 +403,39 @@ def simulate_stage(T, heads, D, rd, es, G, head_major, x_pad=0):
                 assert np.all(yo[ok] + 16 <= out_extent)
                 for qq in np.nonzero(ok)[0]:
                     writes[2][t0 + g[qq], h[qq], c[qq] * ec:c[qq] * ec + ec] += 1
-        # phase 3 (q and k from LDS)
+        # phase 3 (q and k from LDS): thread t owns chunk position t % (G * cpr)
+        # and walks heads t // (G * cpr) + k * hl
+        gc = G * cpr
+        assert gc <= BLOCK
+        hl = BLOCK // gc
+        h0 = tid // gc
+        pos = tid - h0 * gc
+        g = pos // cpr
+        c = pos - g * cpr
+        row_bytes = D * es
         for s, H in enumerate(heads[:2]):
             if H == 0:
                 continue
-            nch = H * G * cpr
             yhs = T * D + 8 * ec if head_major else D
             yts = D if head_major else H * D + 8 * ec
             extent = ((H - 1) * yhs + (nvalid - 1) * yts + D) * es
-            inv_h = f32(f32(1.0) / f32(H))
-            row_bytes = D * es
-            for kb in range(0, nch, BLOCK):
-                k = kb + tid
-                live = k < nch
-                o = div_small(k, cpr, inv_cpr)
-                c = k - o * cpr
-                if head_major:
-                    h, g = o // G, o % G
-                else:
-                    g = div_small(o, H, inv_h)
-                    h = o - g * H
-                assert np.all(o[live] == k[live] // cpr)
-                row = (g * H + h) * row_bytes
-                assert np.all(row[live] + c[live] * 16 + 16 <= stage_slot_bytes(G, H, D, es))
-                for m in range(ec // 2):
-                    col = c * ec + 2 * m
-                    rot = live & (s < 2) & (col < rd)
-                    first = col < half
-                    pcol = np.where(first, col + half, col - half)
-                    j = np.where(first, col, col - half)
-                    assert np.all(pcol[rot] * es + 2 * es <= row_bytes)
-                    assert np.all(j[rot] % 2 == 0) and np.all(g[rot] * half + j[rot] + 2 <= G * half)
-                st = live & (g < nvalid)
-                yo = (h * yhs + g * yts) * es + c * 16
-                assert np.all(yo[st] + 16 <= extent)
-                for q in np.nonzero(st)[0]:
-                    writes[s][t0 + g[q], h[q], c[q] * ec:c[q] * ec + ec] += 1
+            for m in range(ec // 2):
+                col = c * ec + 2 * m
+                rot = col < rd
+                first = col < half
+                pcol = np.where(~rot, col, np.where(first, col + half, col - half))
+                j = np.where(~rot, 0, np.where(first, col, col - half))
+                assert np.all(pcol * es + 2 * es <= row_bytes)
+                assert np.all(j % 2 == 0) and np.all(g * half + j + 2 <= G * half)
+            for h in range(H):
+                t = np.nonzero((h0 < hl) & (h0 <= h) & ((h - h0) % np.maximum(hl, 1) == 0))[0]
+                row = (g[t] * H + h) * row_bytes
+                assert np.all(row + c[t] * 16 + 16 <= G * H * cpr * 16)
+                live = g[t] < nvalid
+                yo = (h * yhs + g[t] * yts) * es + c[t] * 16
+                assert np.all(yo[live] + 16 <= extent)
+                for q in t[live]:
+                    writes[s][t0 + g[q], h, c[q] * ec:c[q] * ec + ec] += 1
     return writes
 
 

@@ -530,8 +530,10 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
   // in flight (a block holds its LDS from its first load to its last store).
   const int budget = env_int("MROPE_STAGE_G", 0) > 0 ? kStageLdsMax : kStageLdsTarget;
   auto fits = [&](int g) {
+    // LDS, v's registers, and one thread per chunk position of a group
     return mrope::stage_lds_bytes(a.dtype, g, p) <= budget &&
-           (int64_t)g * a.heads[2] * (a.D * es / 16) <= mrope::stage_max_v_chunks();
+           (int64_t)g * a.heads[2] * (a.D * es / 16) <= mrope::stage_max_v_chunks() &&
+           g * (a.D * es / 16) <= mrope::kBlockThreads;
   };
   while (G > 1 && !fits(G)) G /= 2;
   if (G > 0 && !fits(G)) G = 0;

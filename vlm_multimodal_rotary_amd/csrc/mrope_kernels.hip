@@ -982,86 +982,109 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
     }
   }
 
-  // 4. rotate q and k 16 bytes per lane; write in output order
+  // 4. rotate q and k.  Thread t owns one 16-byte chunk position (token g,
+  // chunk c) of the group's rows, pos = t % (G * cpr), and walks the heads
+  // h = t / (G * cpr), + hl, + 2 hl, ... (hl = 256 / (G * cpr) threads per
+  // position; the host keeps G * cpr <= 256).  Its columns, partner offsets
+  // and cos/sin are fixed, so they are formed once; per chunk there remain
+  // the LDS reads, the rotation and the store, and for each head the
+  // positions of a group go out as one contiguous run.
+  {
+    const int gc = G * cpr;
+    const int hl = kBlockThreads / gc;
+    const int h0 = tid / gc;
+    const int pos = tid - h0 * gc;
+    const int g = pos / cpr;
+    const int c = pos - g * cpr;
+    constexpr int NP = EC / 2;           // element pairs per chunk
+    constexpr int WP = BF16 ? 1 : 2;     // 32-bit words per pair
+    bool rot[NP];
+    int poff[NP];                        // byte offset of the partner pair in the row
+    double cd[EC], sd[EC];               // cos, and sin with the half's sign
+    float cf[EC], sf[EC];
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int col = c * EC + 2 * m;
+      rot[m] = col < rd;
+      const bool first = col < half;
+      const int pcol = !rot[m] ? col : (first ? col + half : col - half);
+      const int j = !rot[m] ? 0 : (first ? col : col - half);
+      poff[m] = pcol * ES;
+      const float4 cc = *reinterpret_cast<const float4*>(cs + g * half + j);
+      const float cv[2] = {cc.x, cc.z};
+      const float sv[2] = {cc.y, cc.w};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float cfe = cv[e], sfe = sv[e];
+        if constexpr (BF16 && PREC == MROPE_PRECISION_DTYPE) {
+          cfe = round_bf16(cfe);
+          sfe = round_bf16(sfe);
+        }
+        // first half: y c - partner s = y c + partner (-s); negating is exact
+        cf[2 * m + e] = cfe;
+        sf[2 * m + e] = first ? -sfe : sfe;
+        cd[2 * m + e] = (double)cv[e];
+        sd[2 * m + e] = first ? -(double)sv[e] : (double)sv[e];
+      }
+    }
 #pragma unroll 1
-  for (int s = 0; s < kStageLdsSlots; ++s) {
-    const int H = p.heads[s];
-    if (H == 0) continue;
-    const bool rotate = true;
-    const int nch = H * G * cpr;
-    const __amdgpu_buffer_rsrc_t ry = buffer_of(
-        static_cast<char*>(p.y[s]) + t0 * p.y_ts[s] * ES,
-        (uint32_t)(((int64_t)(H - 1) * p.y_hs[s] + (int64_t)(nvalid - 1) * p.y_ts[s] + D) * ES));
-    const unsigned char* src = smem + lds_off[s];
-    const float inv_h = p.inv_heads[s];
+    for (int s = 0; s < kStageLdsSlots; ++s) {
+      const int H = p.heads[s];
+      if (H == 0 || h0 >= hl) continue;
+      const __amdgpu_buffer_rsrc_t ry = buffer_of(
+          static_cast<char*>(p.y[s]) + t0 * p.y_ts[s] * ES,
+          (uint32_t)(((int64_t)(H - 1) * p.y_hs[s] + (int64_t)(nvalid - 1) * p.y_ts[s] + D) * ES));
+      const unsigned char* row = smem + lds_off[s] + (g * H + h0) * (D * ES);
+      const int row_step = hl * D * ES;
+      uint32_t yo = (uint32_t)(((int64_t)h0 * p.y_hs[s] + (int64_t)g * p.y_ts[s]) * ES) +
+                    (uint32_t)c * 16u;
+      const uint32_t y_step = (uint32_t)((int64_t)hl * p.y_hs[s] * ES);
+      const bool live = g < nvalid;
 #pragma unroll 1
-    for (int k = tid; k < nch; k += kBlockThreads) {
-      const StageChunk q = stage_split<G>(k, cpr, inv_cpr, H, inv_h, p.stage_hm != 0);
-      const int h = q.h, g = q.g, c = q.c;
-      const unsigned char* row = src + (g * H + h) * (D * ES);
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c * 16);
-      Words<16> own;
-      own.w[0] = v.x; own.w[1] = v.y; own.w[2] = v.z; own.w[3] = v.w;
-      Words<16> out = own;
-      if (rotate && c * EC < rd) {
-        float a[EC];
+      for (int h = h0; h < H; h += hl, row += row_step, yo += y_step) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c * 16);
+        Words<16> own;
+        own.w[0] = v.x; own.w[1] = v.y; own.w[2] = v.z; own.w[3] = v.w;
+        float a[EC], b[EC];
         unpack<BF16, EC>(own, a);
 #pragma unroll
-        for (int m = 0; m < EC / 2; ++m) {
-          const int col = c * EC + 2 * m;
-          if (col < rd) {
-            const bool first = col < half;
-            const int pcol = first ? col + half : col - half;
-            const int j = first ? col : col - half;
-            float b0, b1;
-            if constexpr (BF16) {
-              const uint32_t w = *reinterpret_cast<const uint32_t*>(row + pcol * 2);
-              b0 = bf_lo(w);
-              b1 = bf_hi(w);
-            } else {
-              const float2 w = *reinterpret_cast<const float2*>(row + pcol * 4);
-              b0 = w.x;
-              b1 = w.y;
-            }
-            const float4 cc = *reinterpret_cast<const float4*>(cs + g * half + j);
-            const float bb[2] = {b0, b1};
-            const float cv[2] = {cc.x, cc.z};
-            const float sv[2] = {cc.y, cc.w};
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const float y = a[2 * m + e];
-              if constexpr (PREC == MROPE_PRECISION_EXACT) {
-                const double sg = first ? -1.0 : 1.0;
-                a[2 * m + e] = (float)__builtin_fma((double)y, (double)cv[e],
-                                                    sg * ((double)bb[e] * (double)sv[e]));
-              } else {
-#pragma clang fp contract(off)
-                constexpr bool CAST = BF16 && PREC == MROPE_PRECISION_DTYPE;
-                float cf = cv[e], sf = sv[e];
-                if constexpr (CAST) {
-                  cf = round_bf16(cf);
-                  sf = round_bf16(sf);
-                }
-                float po = y * cf;
-                float pq = bb[e] * sf;
-                if constexpr (CAST) {
-                  po = round_bf16(po);
-                  pq = round_bf16(pq);
-                }
-                a[2 * m + e] = first ? po - pq : po + pq;
-              }
-            }
+        for (int m = 0; m < NP; ++m) {
+          if constexpr (BF16) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(row + poff[m]);
+            b[2 * m] = bf_lo(w);
+            b[2 * m + 1] = bf_hi(w);
+          } else {
+            const float2 w = *reinterpret_cast<const float2*>(row + poff[m]);
+            b[2 * m] = w.x;
+            b[2 * m + 1] = w.y;
           }
         }
+#pragma unroll
+        for (int i = 0; i < EC; ++i) {
+          if constexpr (PREC == MROPE_PRECISION_EXACT) {
+            a[i] = (float)__builtin_fma((double)a[i], cd[i], (double)b[i] * sd[i]);
+          } else {
+#pragma clang fp contract(off)
+            float po = a[i] * cf[i];
+            float pq = b[i] * sf[i];
+            if constexpr (BF16 && PREC == MROPE_PRECISION_DTYPE) {
+              po = round_bf16(po);
+              pq = round_bf16(pq);
+            }
+            a[i] = po + pq;
+          }
+        }
+        Words<16> out;
         pack<BF16, EC>(a, out);
+#pragma unroll
+        for (int m = 0; m < NP; ++m)
+#pragma unroll
+          for (int w = 0; w < WP; ++w)
+            out.w[m * WP + w] = rot[m] ? out.w[m * WP + w] : own.w[m * WP + w];
+        buf_store<BF16, 16>(ry, live ? yo : kOutOfRange, out);
       }
-      const uint32_t yo = g < nvalid
-          ? (uint32_t)(((int64_t)h * p.y_hs[s] + (int64_t)g * p.y_ts[s]) * ES) + (uint32_t)c * 16u
-          : kOutOfRange;
-      buf_store<BF16, 16>(ry, yo, out);
     }
   }
-
 }
 
 template <bool BF16, int PREC, int G>
