@@ -27,8 +27,12 @@
  *    elements; 0 broadcasts one 1-D position row to every axis).  |p| must
  *    be below 2^24 so float(p) is exact.
  *  - Device buffers are owned by the caller.  The library allocates nothing
- *    and keeps no state between calls; small tables (section, inv_freq) are
- *    host pointers copied into kernel arguments.
+ *    and keeps no state between calls beyond two thread-local diagnostics
+ *    (mrope_last_error, mrope_last_kernel); small tables (section, inv_freq)
+ *    are host pointers copied into kernel arguments.
+ *  - Kernels address a token's rows of a tensor (or, for per-head planes, the
+ *    rows of a few tokens across all planes) with 32-bit byte offsets: a
+ *    span of 2^31 bytes or more is MROPE_EUNSUPPORTED.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
  *  - Outputs may alias their own input exactly (in place).  Any other overlap
