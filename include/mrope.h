@@ -32,7 +32,8 @@
  *    are host pointers copied into kernel arguments.
  *  - Kernels address a token's rows of a tensor (or, for per-head planes, the
  *    rows of a few tokens across all planes) with 32-bit byte offsets: a
- *    span of 2^31 bytes or more is MROPE_EUNSUPPORTED.
+ *    span of 2^31 bytes or more is MROPE_EUNSUPPORTED, and so are more than
+ *    2^20 heads in one tensor.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
  *  - Outputs may alias their own input exactly (in place).  Any other overlap

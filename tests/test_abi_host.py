@@ -375,14 +375,28 @@ def test_buffers_beyond_32_bit_offsets_are_refused():
     buffer descriptor with 32-bit byte offsets: a token whose rows span 2^31
     bytes or more is refused before anything is enqueued."""
     lib = _lib.load()
-    big = 1 << 23                      # heads of 128 bf16: one token's q rows = 2^31 bytes
-    rc = _fused(hq=big, q_ts=big * 128, qo_ts=big * 128, T=1, pos_stride=1,
+    big = 1 << 20                      # heads of 1024 bf16: one token's q rows = 2^31 bytes
+    rc = _fused(hq=big, D=1024, q_ts=big * 1024, qo_ts=big * 1024, hk=4, k_ts=4 * 1024,
+                ko_ts=4 * 1024, T=1, pos_stride=1,
                 k=FAKE + (1 << 36), qo=FAKE + (1 << 37), ko=FAKE + (1 << 38),
                 pos=FAKE + (1 << 39), wq=FAKE + (1 << 40), wk=FAKE + (1 << 40) + 4096)
     assert rc == _lib.MROPE_EUNSUPPORTED, lib.mrope_last_error()
+    assert b"2^31" in lib.mrope_last_error()
     n, H, D = 1 << 20, 16, 72          # fp32 planes: (H - 1) * n * D * 4 bytes > 2^31
     rc = lib.mrope_vision_qkv(FAKE, 3 * H * D, n, H, D, 72, FAKE + (1 << 39), n, 1e4,
                               _lib.DTYPE_F32, _lib.PRECISION_EXACT, FAKE + (1 << 36),
                               FAKE + (1 << 37), FAKE + (1 << 38), n * D, D, None, 0, None)
     assert rc == _lib.MROPE_EUNSUPPORTED, lib.mrope_last_error()
     assert b"2^31" in lib.mrope_last_error()
+
+
+@fake_ptr_test
+def test_head_counts_are_bounded():
+    """More than 2^20 heads per tensor is refused (row indices are split
+    through binary32 reciprocals, exact within that bound)."""
+    lib = _lib.load()
+    big = (1 << 20) + 1
+    rc = _fused(hq=big, q_ts=big * 128, qo_ts=big * 128, T=1, pos_stride=1,
+                k=FAKE + (1 << 36), qo=FAKE + (1 << 37), ko=FAKE + (1 << 38),
+                pos=FAKE + (1 << 39), wq=FAKE + (1 << 40), wk=FAKE + (1 << 40) + 4096)
+    assert rc == _lib.MROPE_EUNSUPPORTED and b"heads" in lib.mrope_last_error()

@@ -178,6 +178,8 @@ int pick_vec(int dtype, int D, int rd, const void* const* ptrs, int nptrs,
 // (0 = D, token-major rows).
 constexpr int kSlots = mrope::kSlots;
 constexpr int64_t kFlatMinTokens = 2048;   // one wavefront per token fills the chip
+constexpr int kMaxHeads = 1 << 20;          // heads per tensor
+constexpr int64_t kFlatMaxChunks = 1 << 22; // chunks of one token's rows in the flat kernel
 constexpr int kStageLdsTarget = 32 * 1024;  // LDS of a staged block: five or more per CU
 constexpr int kStageLdsMax = 64 * 1024;     // ... at most (two per CU), with G forced
 
@@ -224,6 +226,10 @@ int check_qk_tensors(const QKArgs& a, bool need_rd) {
   const char* nm[kSlots] = {"q", "k", "v"};
   for (int s = 0; s < kSlots; ++s) {
     if (a.heads[s] < 0) return fail(MROPE_EINVAL, "%s heads = %d is negative", nm[s], a.heads[s]);
+    // the kernels split row indices through binary32 reciprocals, exact for
+    // the index ranges this bound keeps
+    if (a.heads[s] > kMaxHeads)
+      return fail(MROPE_EUNSUPPORTED, "%s heads = %d exceed %d", nm[s], a.heads[s], kMaxHeads);
     if (a.heads[s] == 0 || a.T == 0) continue;
     if (a.x[s] == nullptr) return fail(MROPE_EINVAL, "%s input is NULL", nm[s]);
     if (a.y[s] == nullptr) return fail(MROPE_EINVAL, "%s output is NULL", nm[s]);
@@ -334,10 +340,12 @@ int env_int(const char* name, int fallback) {
 // choice where it is allowed (tuning).
 bool use_flat(const QKArgs& a, int cs_mode, bool norm, int v, int es) {
   if (cs_mode != mrope::kCsFromPositions || norm || a.T < kFlatMinTokens) return false;
-  for (int s = 0; s < kSlots; ++s)
-    if (a.heads[s] > 0 && a.x[s] == a.y[s] &&
-        (int64_t)a.heads[s] * (a.D / v) > mrope::kFlatBatchChunks)
-      return false;
+  for (int s = 0; s < kSlots; ++s) {
+    const int64_t chunks = (int64_t)a.heads[s] * (a.D / v);
+    // the row of a chunk comes from a binary32 reciprocal: exact below 2^22
+    if (chunks >= kFlatMaxChunks) return false;
+    if (a.heads[s] > 0 && a.x[s] == a.y[s] && chunks > mrope::kFlatBatchChunks) return false;
+  }
   static const int env = env_int("MROPE_FLAT", -1);
   if (env >= 0) return env != 0;
   return (a.D * es) % 256 != 0;
