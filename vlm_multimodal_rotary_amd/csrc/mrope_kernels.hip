@@ -844,10 +844,6 @@ __host__ __device__ __forceinline__ int stage_slot_bytes(int G, int heads, int D
 // output order straight into registers, kStageV of them at most.
 constexpr int kStageV = 3;
 constexpr int kStageLdsSlots = 2;     // q and k go through LDS
-// s_waitcnt immediate for vmcnt(kStageV) expcnt(0) lgkmcnt(0) (gfx9 fields:
-// vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8, vmcnt high bits 15:14 zero)
-constexpr int kWaitVmcntStageV = kStageV;
-static_assert(kStageV < 16, "vmcnt field");
 
 // Output chunk k (k >= 0) of a tensor with H heads in a group: head h, token
 // g, chunk c; head-major order runs over (h, g, c), token-major over (g, h, c).
@@ -936,8 +932,7 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
       cs[i] = make_float2(c, sn);
     }
   }
-  // 2b. v chunks in output order to registers, issued last: the wait below
-  // leaves them in flight through step 3
+  // 2b. v chunks in output order to registers
   Words<16> rv[kStageV];
   {
     const int H = p.heads[2];
@@ -957,11 +952,12 @@ __global__ void __launch_bounds__(kBlockThreads) stage_kernel(const QKParams p, 
     }
   }
 
-  // every load but the last kStageV (the v chunks) has landed; LDS writes too
-  __builtin_amdgcn_s_waitcnt(kWaitVmcntStageV);
+  // every load has landed (the LDS transfers among them), and the LDS
+  // writes of the cos/sin; waiting for the v chunks too costs nothing measurable
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // 3. v from registers (its loads have had the barrier's wait to land)
+  // 3. v from registers
   {
     const int H = p.heads[2];
     const int nch = H * G * cpr;
