@@ -337,31 +337,27 @@ struct SlotState {
   int H, nrows;
 };
 
-// Loads UU row-steps (two chunks per lane each), then finishes them in order:
-// RMSNorm, rotation, stores.  Rows past the tile read and write through the
-// out-of-range offset, so the memory operations per call are static.
-template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC, int UU, typename CsT>
-__device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st, int r0,
-                                              const QKParams& p, int grp, int rpw, int lpr,
-                                              bool lane_on, bool rot, uint32_t ca, uint32_t cb,
-                                              int col_a, const float (&wa)[V],
-                                              const float (&wb)[V], const CsT* lc,
-                                              const CsT* ls, int64_t t0) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int CB = ES * V;
+template <int CB, int UU>
+struct StepLoads {
   Words<CB> ra[UU], rb[UU];
   int tlu[UU];
   bool ok[UU];
   uint32_t you[UU];
+};
+
+template <int CB, int UU>
+__device__ __forceinline__ void load_steps(SlotState<CB>& st, int r0, int grp, int rpw,
+                                           bool lane_on, uint32_t ca, uint32_t cb,
+                                           StepLoads<CB, UU>& L) {
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
     const int r = r0 + u * rpw + grp;
-    ok[u] = lane_on && r < st.nrows;
-    tlu[u] = st.tl;
-    you[u] = ok[u] ? st.yo : kOutOfRange;
-    const uint32_t xoff = ok[u] ? st.xo : kOutOfRange;
-    buf_load<CB>(st.rx, xoff + ca, ra[u]);
-    buf_load<CB>(st.rx, xoff + cb, rb[u]);
+    L.ok[u] = lane_on && r < st.nrows;
+    L.tlu[u] = st.tl;
+    L.you[u] = L.ok[u] ? st.yo : kOutOfRange;
+    const uint32_t xoff = L.ok[u] ? st.xo : kOutOfRange;
+    buf_load<CB>(st.rx, xoff + ca, L.ra[u]);
+    buf_load<CB>(st.rx, xoff + cb, L.rb[u]);
     st.xo += st.xinc;
     st.yo += st.yinc;
     st.h += st.dr;
@@ -373,6 +369,22 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
       st.yo += st.ywrap;
     }
   }
+}
+
+template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC, int UU, typename CsT>
+__device__ __forceinline__ void finish_steps(const SlotState<(BF16 ? 2 : 4) * V>& st,
+                                             const StepLoads<(BF16 ? 2 : 4) * V, UU>& L,
+                                             const QKParams& p, int lpr, bool rot, uint32_t ca,
+                                             uint32_t cb, int col_a, const float (&wa)[V],
+                                             const float (&wb)[V], const CsT* lc,
+                                             const CsT* ls, int64_t t0) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int CB = ES * V;
+  const Words<CB>(&ra)[UU] = L.ra;
+  const Words<CB>(&rb)[UU] = L.rb;
+  const int(&tlu)[UU] = L.tlu;
+  const bool(&ok)[UU] = L.ok;
+  const uint32_t(&you)[UU] = L.you;
 #pragma unroll
   for (int u = 0; u < UU; ++u) {
     if constexpr (CS == kCsNone && !NORM) {
@@ -458,6 +470,19 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
   }
 }
 
+template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC, int UU, typename CsT>
+__device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st, int r0,
+                                              const QKParams& p, int grp, int rpw, int lpr,
+                                              bool lane_on, bool rot, uint32_t ca, uint32_t cb,
+                                              int col_a, const float (&wa)[V],
+                                              const float (&wb)[V], const CsT* lc,
+                                              const CsT* ls, int64_t t0) {
+  StepLoads<(BF16 ? 2 : 4) * V, UU> L;
+  load_steps<(BF16 ? 2 : 4) * V, UU>(st, r0, grp, rpw, lane_on, ca, cb, L);
+  finish_steps<BF16, V, CS, NORM, LPR, PREC, UU>(st, L, p, lpr, rot, ca, cb, col_a, wa, wb, lc, ls,
+                                                t0);
+}
+
 // Wavefront w owns the tile of tokens [w*nt, w*nt + nt): first the tile's
 // cos/sin (in its LDS slice), then the tile's q rows and k rows, U row-steps
 // per batch of loads.  Wavefronts are short-lived and many; the hardware
@@ -515,6 +540,79 @@ qk_kernel(const QKParams p, const ColTable tab) {
   const int steps_all = pre[kSlots];
   const int step_begin = split ? steps_all * part / p.parts : 0;
   const int step_end = split ? steps_all * (part + 1) / p.parts : steps_all;
+  // Walking state of tensor s from step lo on.
+  auto make_state = [&](int s, int lo) {
+    const int H = p.heads[s];
+    const int64_t xts = p.x_ts[s];
+    const int64_t yts = p.y_ts[s];
+    const int64_t yhs = p.y_hs[s];
+    SlotState<CB> st;
+    // Tile-local buffers: byte offsets below stay within 32 bits.
+    st.rx = buffer_of(static_cast<const char*>(p.x[s]) + t0 * xts * ES,
+                      (uint32_t)(((int64_t)(ntok - 1) * xts + (int64_t)H * p.D) * ES));
+    st.ry = buffer_of(static_cast<const char*>(p.y[s]) + t0 * yts * ES,
+                      (uint32_t)(((int64_t)(ntok - 1) * yts + (int64_t)(H - 1) * yhs + p.D) * ES));
+    st.H = H;
+    st.nrows = ntok * H;
+    st.dq = p.dq[s];
+    st.dr = p.dr[s];
+    // First row of this lane: r = lo * rpw + grp; r / H through a binary32
+    // reciprocal (r < 2^23, so the estimate is off by at most one), corrected.
+    const int r_first = lo * rpw + grp;
+    st.tl = (int)((float)r_first * p.inv_heads[s]);
+    if (st.tl * H > r_first) --st.tl;
+    if ((st.tl + 1) * H <= r_first) ++st.tl;
+    st.h = r_first - st.tl * H;
+    st.xo = (uint32_t)(((int64_t)st.tl * xts + (int64_t)st.h * p.D) * ES);
+    st.yo = (uint32_t)(((int64_t)st.tl * yts + (int64_t)st.h * yhs) * ES);
+    st.xinc = (uint32_t)(((int64_t)st.dq * xts + (int64_t)st.dr * p.D) * ES);
+    st.yinc = (uint32_t)(((int64_t)st.dq * yts + (int64_t)st.dr * yhs) * ES);
+    st.xwrap = (uint32_t)((xts - (int64_t)H * p.D) * ES);
+    st.ywrap = (uint32_t)((yts - (int64_t)H * yhs) * ES);
+    return st;
+  };
+  // Decode: rotated k goes to its cache row; a row outside [0, capacity) gets
+  // an empty buffer, so its stores are dropped.
+  auto k_cache_buffer = [&](int64_t seq, int32_t slot) {
+    const bool in_cache = slot >= 0 && slot < p.kc_cap;
+    return buffer_of(static_cast<const char*>(p.y[1]) +
+                         (seq * p.kc_seq + (int64_t)(in_cache ? slot : 0) * p.kc_tok) * ES,
+                     in_cache ? (uint32_t)((int64_t)p.heads[1] * p.D * ES) : 0u);
+  };
+  // Decode: the part's first row-step (and its norm weights) is loaded before
+  // the token's cache length is read and its cos/sin formed, and finished
+  // right after.  Vector memory waits count loads in issue order, so the one
+  // inv_freq value the cos/sin needs is loaded first and the loads are issued
+  // on every path (out of range where there is no work): the cos/sin then
+  // waits for that value alone.
+  [[maybe_unused]] int s_pre = -1;
+  [[maybe_unused]] SlotState<CB> st_pre;
+  [[maybe_unused]] StepLoads<CB, 1> L_pre;
+  [[maybe_unused]] float inv_first = 0.f;
+  [[maybe_unused]] Words<CB> w_pre_a, w_pre_b;
+  if constexpr (CS == kCsDecode) {
+    if (lane < half) inv_first = tab.inv[lane];
+    const int lo0 = (step_begin > pre[0] ? step_begin : pre[0]) - pre[0];
+    const int hi0 = (step_end < pre[1] ? step_end : pre[1]) - pre[0];
+    const int lo1 = (step_begin > pre[1] ? step_begin : pre[1]) - pre[1];
+    const int hi1 = (step_end < pre[2] ? step_end : pre[2]) - pre[1];
+    int lo_pre = 0;
+    if (p.heads[0] > 0 && lo0 < hi0) {
+      s_pre = 0;
+      lo_pre = lo0;
+    } else if (p.heads[1] > 0 && lo1 < hi1) {
+      s_pre = 1;
+      lo_pre = lo1;
+    }
+    st_pre = make_state(s_pre >= 0 ? s_pre : 0, lo_pre);
+    if constexpr (NORM) {
+      const __amdgpu_buffer_rsrc_t rw =
+          buffer_of(p.w[s_pre >= 0 ? s_pre : 0], s_pre >= 0 ? (uint32_t)(p.D * ES) : 0u);
+      buf_load<CB>(rw, ca, w_pre_a);
+      buf_load<CB>(rw, cb, w_pre_b);
+    }
+    load_steps<CB, 1>(st_pre, lo_pre * rpw, grp, rpw, lane_on && s_pre >= 0, ca, cb, L_pre);
+  }
   {
     // Decode: token t0 is token i of sequence b; its text position (the same
     // on every axis) continues the sequence's cache.
@@ -525,7 +623,13 @@ qk_kernel(const QKParams p, const ColTable tab) {
       const int i = (int)(t0 - dec_seq * p.new_tokens);
       dec_slot = p.cache_len[dec_seq] + i;
       const int32_t pp = dec_slot + (p.rope_delta != nullptr ? p.rope_delta[dec_seq] : 0);
-      for (int j = lane; j < half; j += kWaveSize) {
+      if (lane < half) {
+        float c, s;
+        angle_cos_sin(pp, inv_first, c, s);
+        lc[lane] = (cs_t)c;
+        ls[lane] = (cs_t)s;
+      }
+      for (int j = lane + kWaveSize; j < half; j += kWaveSize) {
         float c, s;
         angle_cos_sin(pp, tab.inv[j], c, s);
         lc[j] = (cs_t)c;
@@ -561,50 +665,31 @@ qk_kernel(const QKParams p, const ColTable tab) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
+    if constexpr (CS == kCsDecode) {
+      if (s_pre >= 0) {
+        if (s_pre == 1) st_pre.ry = k_cache_buffer(dec_seq, dec_slot);
+        float wa[V], wb[V];
+        if constexpr (NORM) {
+          unpack<BF16, V>(w_pre_a, wa);
+          unpack<BF16, V>(w_pre_b, wb);
+        }
+        finish_steps<BF16, V, CS, NORM, LPR, PREC, 1>(st_pre, L_pre, p, lpr, rot, ca, cb, col_a,
+                                                      wa, wb, lc, ls, t0);
+      }
+    }
 #pragma unroll 1
     for (int s = 0; s < kSlots; ++s) {
       const int H = p.heads[s];
       if (H == 0) continue;
       // This part's steps of tensor s.
-      const int lo = (step_begin > pre[s] ? step_begin : pre[s]) - pre[s];
+      int lo = (step_begin > pre[s] ? step_begin : pre[s]) - pre[s];
       const int hi = (step_end < pre[s + 1] ? step_end : pre[s + 1]) - pre[s];
+      if (s == s_pre) ++lo;     // loaded and finished around the prologue
       if (lo >= hi) continue;
-      const int64_t xts = p.x_ts[s];
-      const int64_t yts = p.y_ts[s];
-      const int64_t yhs = p.y_hs[s];
-      SlotState<CB> st;
-      // Tile-local buffers: byte offsets below stay within 32 bits.
-      st.rx = buffer_of(static_cast<const char*>(p.x[s]) + t0 * xts * ES,
-                        (uint32_t)(((int64_t)(ntok - 1) * xts + (int64_t)H * p.D) * ES));
-      st.ry = buffer_of(static_cast<const char*>(p.y[s]) + t0 * yts * ES,
-                        (uint32_t)(((int64_t)(ntok - 1) * yts + (int64_t)(H - 1) * yhs + p.D) * ES));
+      SlotState<CB> st = make_state(s, lo);
       if constexpr (CS == kCsDecode) {
-        if (s == 1) {
-          // Rotated k goes to its cache row; a row outside [0, capacity) gets
-          // an empty buffer, so its stores are dropped.
-          const bool in_cache = dec_slot >= 0 && dec_slot < p.kc_cap;
-          st.ry = buffer_of(static_cast<const char*>(p.y[1]) +
-                                (dec_seq * p.kc_seq + (int64_t)(in_cache ? dec_slot : 0) * p.kc_tok) * ES,
-                            in_cache ? (uint32_t)((int64_t)H * p.D * ES) : 0u);
-        }
+        if (s == 1) st.ry = k_cache_buffer(dec_seq, dec_slot);
       }
-      st.H = H;
-      st.nrows = ntok * H;
-      st.dq = p.dq[s];
-      st.dr = p.dr[s];
-      // First row of this lane: r = lo * rpw + grp; r / H through a binary32
-      // reciprocal (r < 2^23, so the estimate is off by at most one), corrected.
-      const int r_first = lo * rpw + grp;
-      st.tl = (int)((float)r_first * p.inv_heads[s]);
-      if (st.tl * H > r_first) --st.tl;
-      if ((st.tl + 1) * H <= r_first) ++st.tl;
-      st.h = r_first - st.tl * H;
-      st.xo = (uint32_t)(((int64_t)st.tl * xts + (int64_t)st.h * p.D) * ES);
-      st.yo = (uint32_t)(((int64_t)st.tl * yts + (int64_t)st.h * yhs) * ES);
-      st.xinc = (uint32_t)(((int64_t)st.dq * xts + (int64_t)st.dr * p.D) * ES);
-      st.yinc = (uint32_t)(((int64_t)st.dq * yts + (int64_t)st.dr * yhs) * ES);
-      st.xwrap = (uint32_t)((xts - (int64_t)H * p.D) * ES);
-      st.ywrap = (uint32_t)((yts - (int64_t)H * yhs) * ES);
 
       // The third tensor (v of a packed qkv) is copied: no norm, no rotation.
       if constexpr (CS == kCsFromPositions) {
