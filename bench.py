@@ -8,7 +8,8 @@ k[32768,4,128] bf16, interleaved [24,20,20], theta 1e6, RMSNorm eps 1e-6.
 
 Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
 kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
-bounded sample of the same workload (cpu_baseline).
+bounded sample of the same workload (cpu_baseline: one thread, then one
+process per core).
 
 Warmup is at least W steps and at least --min-warmup-s seconds: the first
 tens of milliseconds of sustained HBM traffic run at a different clock state,
@@ -17,6 +18,7 @@ kernel launch on torch's current stream, timed with HIP events on that stream.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                   [--graph G] [--cold] [--cs-cache] [--precision exact|dtype|fp32]
+                  [--cpu-procs P]
   python bench.py --copy-calib BYTES   # plain device copy, for counter scaling
 
 Other workloads time the other entry points the same way: the decode step
@@ -63,30 +65,85 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, wl, budget_s: float = 12.0, precision: str = "exact"):
-    """The oracle as it stands, on consecutive 64-token windows of the same
-    workload, until about budget_s of CPU time; single thread."""
+def _oracle_fused_windows(q, k, pos, wl, wq, wk, precision, chunk):
     from oracle import mrope_oracle as O
+    for i in range(q.shape[0] // chunk):
+        sl = slice(i * chunk, (i + 1) * chunk)
+        O.rmsnorm_mrope_qk(q[sl], k[sl], pos[:, sl], rotary_dim=wl.rotary_dim, theta=wl.theta,
+                           section=wl.section, layout=wl.layout, wq=wq, wk=wk, eps=wl.eps,
+                           dtype=wl.dtype, precision=precision)
+
+
+def _oracle_worker(job):
+    """One process of the multi-process oracle sample: from a common start
+    time, repeats the oracle over its own token windows until the deadline.
+    Returns (tokens done, seconds)."""
+    q, k, pos, wl, wq, wk, precision, chunk, t_start, budget_s = job
+    now = time.time()
+    if now < t_start:
+        time.sleep(t_start - now)
+    start = time.perf_counter()
+    done = 0
+    while True:
+        _oracle_fused_windows(q, k, pos, wl, wq, wk, precision, chunk)
+        done += q.shape[0]
+        el = time.perf_counter() - start
+        if el >= budget_s:
+            return done, el
+
+
+def cpu_baseline(inp, wl, budget_s: float = 12.0, precision: str = "exact", procs: int = 1):
+    """The oracle as it stands, on consecutive 64-token windows of the same
+    workload: one thread for about budget_s, then (procs > 1) one process per
+    core, each on its own 8 windows, for about 30 s of CPU time in all.  The
+    reported value is the aggregate rate of the processes."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
     T = wl.T
-    chunk = 64
+    chunk = min(64, T)
+    wq = inp["wq"] if wl.norm else None
+    wk = inp["wk"] if wl.norm else None
     done = 0
     start = time.perf_counter()
     t0 = 0
     while True:
         sl = slice(t0, t0 + chunk)
-        O.rmsnorm_mrope_qk(inp["q"][sl], inp["k"][sl], inp["pos"][:, sl],
-                           rotary_dim=wl.rotary_dim, theta=wl.theta, section=wl.section,
-                           layout=wl.layout, wq=inp["wq"] if wl.norm else None,
-                           wk=inp["wk"] if wl.norm else None, eps=wl.eps, dtype=wl.dtype,
-                           precision=precision)
+        _oracle_fused_windows(inp["q"][sl], inp["k"][sl], inp["pos"][:, sl], wl, wq, wk,
+                              precision, chunk)
         done += chunk
         t0 = (t0 + chunk) % (T - chunk + 1)
         elapsed = time.perf_counter() - start
         if elapsed >= budget_s:
             break
-    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} tokens ({done // chunk} windows of {chunk} consecutive tokens, "
-                      f"all {wl.hq}+{wl.hk} heads) of {wl.name}, {elapsed:.1f} s, one thread"}
+    one = done / elapsed
+    sample = (f"{done} tokens ({done // chunk} windows of {chunk} consecutive tokens, all "
+              f"{wl.hq}+{wl.hk} heads) of {wl.name}, {elapsed:.1f} s, one thread")
+    if procs <= 1:
+        return {"value": one, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": sample}
+    per = min(8, T // chunk) * chunk
+    stride = max(per, (T - per) // procs)
+    wall = max(2.0, 30.0 / procs)
+    t_start = time.time() + 4.0
+    jobs = []
+    for i in range(procs):
+        a = min(i * stride, T - per)
+        jobs.append((inp["q"][a:a + per], inp["k"][a:a + per], inp["pos"][:, a:a + per], wl,
+                     wq, wk, precision, chunk, t_start, wall))
+    try:
+        with ProcessPoolExecutor(procs, mp_context=mp.get_context("spawn")) as ex:
+            futs = [ex.submit(_oracle_worker, j) for j in jobs]
+            res = [f.result(timeout=wall + 120.0) for f in futs]
+    except Exception as e:  # a worker died or never started: report the one thread
+        return {"value": one, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{sample} (the {procs}-process sample failed: {type(e).__name__})"}
+    agg = sum(d / e for d, e in res)
+    toks = sum(d for d, _ in res)
+    return {"value": agg, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "one_thread": one,
+            "sample": f"{procs} processes from one start time, each repeating {per // chunk} windows of "
+                      f"{chunk} tokens for {wall:.1f} s ({toks} tokens in all; value = sum of "
+                      f"their rates); before them {sample}"}
 
 
 def time_steps(step, args, stream=None):
@@ -365,6 +422,9 @@ def main():
     ap.add_argument("--precision", default="exact", choices=["exact", "dtype", "fp32"],
                     help="rotation rounding: exact (default), dtype (cos/sin cast to the "
                          "tensor dtype, bf16 tensor ops) or fp32 (fp32 tensor ops)")
+    ap.add_argument("--cpu-procs", type=int, default=0,
+                    help="processes for the oracle's multi-process sample (default: the "
+                         "cores this process may run on, at most 16; 1 = one thread only)")
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many steps in one HIP graph and time graph replays "
@@ -474,7 +534,9 @@ def main():
         line["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = (cpu_baseline_decode(inp, wl, precision=args.precision) if decode
-                                else cpu_baseline(inp, wl, precision=args.precision))
+                                else cpu_baseline(inp, wl, precision=args.precision,
+                                                  procs=args.cpu_procs or
+                                                  min(len(os.sched_getaffinity(0)), 16)))
     print(json.dumps(line), flush=True)
 
 
