@@ -395,9 +395,12 @@ const char* mrope_last_error(void);
  * mrope_decode_qk, mrope_vision_qkv) enqueued: "qk_kernel" (rows spread over
  * lane groups, the general path), "flat_kernel" (a token's block of rows
  * lane after lane) or "stage_kernel" (rows staged through LDS, written in
- * output order); empty string before the first launch.  A diagnostic for
- * profiles and benchmarks: the choice depends on the shapes, dtype and
- * layout only, never on the values.  Static storage; no ownership.
+ * output order); after mrope_rope_index, the kernels of its passes 2 and 3:
+ * "rope_index_fused" (one kernel; up to 1024 chunks of 1024 tokens and 256
+ * grids per type) or "rope_index_carry+apply" (two kernels, any size); empty
+ * string before the first launch.  A diagnostic for profiles, benchmarks and
+ * tests: the choice depends on the shapes, dtype, layout and grid counts
+ * only, never on the values.  Static storage; no ownership.
  */
 const char* mrope_last_kernel(void);
 

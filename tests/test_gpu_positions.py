@@ -72,6 +72,33 @@ def test_random_batches(M, seed, B, L):
     _compare(M, types, images, videos, mask, f"random seed {seed}")
 
 
+@pytest.mark.parametrize("case", ["small", "many_grids", "many_chunks"])
+def test_pass_forms(M, case):
+    """Passes 2 and 3 run as one kernel when the chunk summaries and grids fit
+    LDS (up to 1024 chunks, 256 grids of a type), else as two kernels; both
+    forms give the oracle's table."""
+    rng = np.random.default_rng(900)
+    if case == "small":
+        types, mask, images, videos = W.random_mm_batch(rng, 2, 600)
+        want = "rope_index_fused"
+        assert len(images) <= 256 and len(videos) <= 256
+    elif case == "many_grids":
+        types, mask, images, videos = W.random_mm_batch(rng, 4, 4000)
+        want = "rope_index_carry+apply"
+        assert len(images) > 256 or len(videos) > 256
+    else:
+        L = 600000   # 2 x 586 chunks of 1024 tokens
+        types = np.zeros((2, L), dtype=np.int64)
+        types[0, 1000:1012] = 1
+        types[1, 5000:5006] = 1
+        mask = np.ones((2, L), dtype=np.int64)
+        mask[1, :3000] = 0
+        images, videos = [(1, 6, 8), (1, 4, 6)], []
+        want = "rope_index_carry+apply"
+    _compare(M, types, images, videos, mask, f"pass form {case}")
+    assert M.last_kernel() == want
+
+
 def test_workload_layouts_and_no_mask(M):
     """The mixed and video workloads' segment lists, without a mask; the GPU
     table equals both the oracle and the workload generator's table."""

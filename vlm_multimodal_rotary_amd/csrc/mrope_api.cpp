@@ -749,7 +749,7 @@ int mrope_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask
   p.ws_adv_i = reinterpret_cast<int64_t*>(ws + w.adv_i);
   p.ws_adv_v = reinterpret_cast<int64_t*>(ws + w.adv_v);
   p.ws_cum_t = reinterpret_cast<int32_t*>(ws + w.cum_t);
-  const int hrc = mrope::launch_rope_index(p, stream);
+  const int hrc = mrope::launch_rope_index(p, stream, &g_last_kernel);
   if (hrc != (int)hipSuccess)
     return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
   return ok();

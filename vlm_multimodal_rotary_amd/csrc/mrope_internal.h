@@ -140,7 +140,8 @@ struct VisionPosParams {
   int32_t* status;
 };
 
-int launch_rope_index(const RopeIndexParams& p, void* stream);
+// *kernel receives the name of the pass-2/3 form launched.
+int launch_rope_index(const RopeIndexParams& p, void* stream, const char** kernel);
 int launch_vision_pos_ids(const VisionPosParams& p, void* stream);
 
 // Launchers (mrope_kernels.hip).  Return a hipError_t value as int.

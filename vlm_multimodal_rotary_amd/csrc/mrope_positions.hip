@@ -17,6 +17,10 @@
 //      starts with block scans seeded by the carry, and writes the positions;
 //      rope_delta = max + 1 - valid length by one atomic max per block.
 //
+// When the chunk summaries fit LDS (up to 1024 chunks) and the grids fit the
+// LDS tables, passes 2 and 3 run as one kernel: every block of the apply pass
+// does the carry work itself, in LDS, and keeps its own chunk's carry.
+//
 // The grid iterators of the walkthrough (one image iterator and one video
 // iterator shared by the batch, videos split into single-slice grids) become
 // global counters: the k-th image segment of the batch uses image grid k, the
@@ -35,6 +39,14 @@ namespace mrope {
 namespace {
 
 constexpr int kPT = kPosThreads;
+
+// Raw buffer over `bytes` bytes at base: loads past the range return 0 and
+// touch no memory, so a lane with nothing to read needs no branch.
+__device__ __forceinline__ int32_t load_in_range(const int32_t* base, uint32_t count, int i) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(base), 0, (int)(count * sizeof(int32_t)), 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)i * (uint32_t)sizeof(int32_t), 0, 0);
+}
 constexpr int kPer = kPosPerThread;
 constexpr int kWaves = kPT / kWaveSize;
 
@@ -42,26 +54,51 @@ constexpr int kWaves = kPT / kWaveSize;
 // Block scans over 256 threads (four wavefronts).
 // ---------------------------------------------------------------------------
 
-template <typename T>
-__device__ __forceinline__ T wave_incl_sum(T v) {
-  const int lane = threadIdx.x & (kWaveSize - 1);
-#pragma unroll
-  for (int d = 1; d < kWaveSize; d <<= 1) {
-    const T u = __shfl_up(v, d);
-    if (lane >= d) v += u;
+// Wavefront scans on DPP moves (register-to-register, no LDS round trip).
+// A lane whose DPP source lies outside its row, or whose row the row mask
+// leaves out, receives `id` instead.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move(int id, int v) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_move(T id, T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+  if constexpr (sizeof(T) == 4) {
+    return (T)dpp_move<CTRL, ROW_MASK>((int)id, (int)v);
+  } else {
+    const unsigned long long u = (unsigned long long)v, d = (unsigned long long)id;
+    const unsigned lo = (unsigned)dpp_move<CTRL, ROW_MASK>((int)(unsigned)d, (int)(unsigned)u);
+    const unsigned hi =
+        (unsigned)dpp_move<CTRL, ROW_MASK>((int)(unsigned)(d >> 32), (int)(unsigned)(u >> 32));
+    return (T)(((unsigned long long)hi << 32) | lo);
   }
+}
+
+// Inclusive scan over the wavefront: Hillis-Steele within each row of 16
+// lanes (row_shr 1, 2, 4, 8), then the last lane of row 0 and 2 into rows 1
+// and 3 (row_bcast 15) and the last lane of row 1 into rows 2 and 3
+// (row_bcast 31).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_incl_scan(T v, T id, Op op) {
+  v = op(v, dpp_move<0x111, 0xF>(id, v));
+  v = op(v, dpp_move<0x112, 0xF>(id, v));
+  v = op(v, dpp_move<0x114, 0xF>(id, v));
+  v = op(v, dpp_move<0x118, 0xF>(id, v));
+  v = op(v, dpp_move<0x142, 0xA>(id, v));
+  v = op(v, dpp_move<0x143, 0xC>(id, v));
   return v;
 }
 
 template <typename T>
-__device__ __forceinline__ T wave_incl_max(T v) {
-  const int lane = threadIdx.x & (kWaveSize - 1);
-#pragma unroll
-  for (int d = 1; d < kWaveSize; d <<= 1) {
-    const T u = __shfl_up(v, d);
-    if (lane >= d && u > v) v = u;
-  }
-  return v;
+__device__ __forceinline__ T wave_incl_sum(T v) {
+  return wave_incl_scan(v, (T)0, [](T a, T b) { return a + b; });
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_max(T v, T lo) {
+  return wave_incl_scan(v, lo, [](T a, T b) { return a > b ? a : b; });
 }
 
 // Exclusive sum over the block; *total receives the block sum.  `sh` holds
@@ -90,9 +127,8 @@ template <typename T>
 __device__ T block_excl_max(T v, T lo, T* total, T* sh) {
   const int w = threadIdx.x / kWaveSize;
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const T incl = wave_incl_max(v);
-  T prev = __shfl_up(incl, 1);
-  if (lane == 0) prev = lo;
+  const T incl = wave_incl_max(v, lo);
+  const T prev = dpp_move<0x138, 0xF>(lo, incl);   // wave_shr 1: the lane before
   if (lane == kWaveSize - 1) sh[w] = incl;
   __syncthreads();
   T before = lo, all = lo;
@@ -111,9 +147,8 @@ __device__ T block_excl_max(T v, T lo, T* total, T* sh) {
 __device__ int block_or(int v, int* sh) {
   const int w = threadIdx.x / kWaveSize;
   const int lane = threadIdx.x & (kWaveSize - 1);
-#pragma unroll
-  for (int d = 1; d < kWaveSize; d <<= 1) v |= __shfl_xor(v, d);
-  if (lane == 0) sh[w] = v;
+  v = wave_incl_scan(v, 0, [](int a, int b) { return a | b; });
+  if (lane == kWaveSize - 1) sh[w] = v;
   __syncthreads();
   int all = 0;
 #pragma unroll
@@ -135,25 +170,36 @@ struct Run {
   int flags;
 };
 
-__device__ __forceinline__ void read_run(const RopeIndexParams& p, int b, int64_t l0, Run& r) {
-  r.nv = r.nt = r.ni = r.nvd = 0;
-  r.ft = r.lt = r.lsF = r.lsT = -1;
-  r.flags = 0;
-  const int64_t row = (int64_t)b * p.L;
-  // Loads at clamped addresses, all issued before any is used; tokens past
-  // the row are discarded afterwards.
+// The run's token types and mask words.  Loads at clamped addresses, issued
+// together; tokens past the row are discarded by parse_run.  Without a mask
+// the type row is read in its place, so no branch surrounds a load.
+struct RunWords {
   int tv[kPer], mv[kPer];
+};
+
+__device__ __forceinline__ void load_run(const RopeIndexParams& p, int b, int64_t l0,
+                                         RunWords& w) {
+  const int64_t row = (int64_t)b * p.L;
+  const int32_t* mrow = p.mask != nullptr ? p.mask : p.types;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int64_t l = (l0 + k) < p.L ? (l0 + k) : (p.L - 1);
-    tv[k] = p.types[row + l];
-    mv[k] = p.mask != nullptr ? p.mask[row + l] : 1;
+    w.tv[k] = p.types[row + l];
+    w.mv[k] = mrow[row + l];
   }
+}
+
+__device__ __forceinline__ void parse_run(const RopeIndexParams& p, int64_t l0,
+                                          const RunWords& w, Run& r) {
+  r.nv = r.nt = r.ni = r.nvd = 0;
+  r.ft = r.lt = r.lsF = r.lsT = -1;
+  r.flags = 0;
+  const bool masked = p.mask != nullptr;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     int ty = -1;
-    if (l0 + k < p.L && mv[k] != 0) {
-      ty = tv[k];
+    if (l0 + k < p.L && (!masked || w.mv[k] != 0)) {
+      ty = w.tv[k];
       if (ty < 0 || ty > 2) {
         r.flags |= MROPE_POS_BAD_TYPE;
         ty = 0;
@@ -173,6 +219,12 @@ __device__ __forceinline__ void read_run(const RopeIndexParams& p, int b, int64_
     ++r.nv;
     r.nt += ty == 0;
   }
+}
+
+__device__ __forceinline__ void read_run(const RopeIndexParams& p, int b, int64_t l0, Run& r) {
+  RunWords w;
+  load_run(p, b, l0, w);
+  parse_run(p, l0, w, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -224,6 +276,9 @@ __global__ void __launch_bounds__(kPT) rope_index_summarize(const RopeIndexParam
   block_excl_max(r.ft >= 0 ? (int)((kPT - 1 - threadIdx.x) << 2) | r.ft : -1, -1, &first_enc, sh);
   const int fl_tot = block_or(r.flags, sh);
   if (threadIdx.x == 0) {
+    // starting values for the fused pass 2+3 (the carry pass rewrites both)
+    if (j == 0) p.rope_delta[b] = INT32_MIN;
+    if (blockIdx.x == 0) *p.status = 0;
     int* s = p.ws_sum + ((int64_t)b * p.C + j) * kPosSumInts;
     s[0] = field(tot, 0);
     s[1] = field(tot, 1);
@@ -321,7 +376,7 @@ __device__ __forceinline__ int64_t video_adv_before(const Tables& tb, int k) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: grid tables and chunk carries (one block).
+// Pass 2: grid tables and chunk carries.
 //
 // The carry of chunk c is a scan over the chunks before it.  Per-sample
 // quantities restart at each sample's first chunk b*C; they are taken as the
@@ -331,34 +386,66 @@ __device__ __forceinline__ int64_t video_adv_before(const Tables& tb, int k) {
 // the latest start; the sample bases), with provisional per-chunk records in
 // the summary slots between passes.  Batch-wide filtered indices are below
 // 2^29 (checked on the host), so (index << 2 | type) fits an int.
+//
+// This work is written once, as device functions.  rope_index_carry runs it
+// in one block and stores every chunk's carry for rope_index_apply.  When the
+// chunk records fit LDS and the grids fit the apply pass's LDS tables,
+// rope_index_fused runs it in every block of the apply pass instead and keeps
+// its own chunk's carry: one kernel fewer, the same results.
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p) {
-  __shared__ int sh[kWaves];
-  __shared__ long long shl[kWaves];
-  // Grid-advance prefix tables: adv_i[k] = sum of image advances before k;
-  // cum_t[v] = slices before video v; adv_v[v] = their advances.
+constexpr int kRecIt = (kPosCarryLds * kPosSumInts + kPT - 1) / kPT;
+constexpr int kGridIt = (3 * kPosStageGrids + kPT - 1) / kPT;
+constexpr int kAdvIt = (kPosStageGrids + 1 + kPT - 1) / kPT;
+
+// This thread's words of the n chunk summaries (loads issued together).
+__device__ __forceinline__ void load_records(const RopeIndexParams& p, int n, int (&rv)[kRecIt]) {
+#pragma unroll
+  for (int u = 0; u < kRecIt; ++u) {
+    const int i = threadIdx.x + u * kPT;
+    rv[u] = i < n * kPosSumInts ? p.ws_sum[i] : 0;
+  }
+}
+
+__device__ __forceinline__ void store_records(const int (&rv)[kRecIt], int n, int* rec) {
+#pragma unroll
+  for (int u = 0; u < kRecIt; ++u) {
+    const int i = threadIdx.x + u * kPT;
+    if (i < n * kPosSumInts) rec[i] = rv[u];
+  }
+}
+
+// Grid-advance prefix tables: adv_i[k] = sum of image advances before k;
+// cum_t[v] = slices before video v; adv_v[v] = their advances.  The grids of
+// the first tile come in as (ih, iw) and (vt, vh, vw); put(0, k, adv_i[k]),
+// put(1, v, cum_t[v]) and put(2, v, adv_v[v]) store the entries.  Returns
+// the number of video slices.
+template <typename Put>
+__device__ int grid_prefix_tables(const RopeIndexParams& p, int ih, int iw, int vt, int vh,
+                                  int vw, long long* shl, Put put) {
   long long carry = 0;
   for (int base = 0; base < p.n_images; base += kPT) {
     const int k = base + threadIdx.x;
     long long a = 0;
     if (k < p.n_images) {
-      const int h = p.image_grid[3 * k + 1], w = p.image_grid[3 * k + 2];
+      const int h = base == 0 ? ih : p.image_grid[3 * k + 1];
+      const int w = base == 0 ? iw : p.image_grid[3 * k + 2];
       a = (h > w ? h : w) / p.merge;
     }
     long long tot;
     const long long ex = block_excl_sum(a, &tot, shl);
-    if (k < p.n_images) p.ws_adv_i[k] = carry + ex;
+    if (k < p.n_images) put(0, k, carry + ex);
     carry += tot;
   }
-  if (threadIdx.x == 0) p.ws_adv_i[p.n_images] = carry;
+  if (threadIdx.x == 0) put(0, p.n_images, carry);
   long long ct = 0, ca = 0;
   for (int base = 0; base < p.n_videos; base += kPT) {
     const int v = base + threadIdx.x;
     long long t = 0, a = 0;
     if (v < p.n_videos) {
-      t = p.video_grid[3 * v];
-      const int h = p.video_grid[3 * v + 1], w = p.video_grid[3 * v + 2];
+      t = base == 0 ? vt : p.video_grid[3 * v];
+      const int h = base == 0 ? vh : p.video_grid[3 * v + 1];
+      const int w = base == 0 ? vw : p.video_grid[3 * v + 2];
       t = t > 0 ? t : 0;
       a = t * ((h > w ? h : w) / p.merge);
     }
@@ -366,30 +453,32 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
     const long long et = block_excl_sum(t, &tt, shl);
     const long long ea = block_excl_sum(a, &ta, shl);
     if (v < p.n_videos) {
-      p.ws_cum_t[v] = (int)(ct + et);
-      p.ws_adv_v[v] = ca + ea;
+      put(1, v, ct + et);
+      put(2, v, ca + ea);
     }
     ct += tt;
     ca += ta;
   }
   if (threadIdx.x == 0) {
-    p.ws_cum_t[p.n_videos] = (int)ct;
-    p.ws_adv_v[p.n_videos] = ca;
+    put(1, p.n_videos, ct);
+    put(2, p.n_videos, ca);
   }
+  return (int)ct;
+}
 
-  const int n = p.B * p.C;
+// Carries of the n chunks whose summaries rec holds (overwritten with
+// provisional records).  emit(c, o) receives chunk c's carry-in;
+// end(b, valid, open_len, open_type, open_grid) the end of sample b (its
+// valid length and the segment open there).  Returns the status bits the
+// summaries report; img_total / vid_total receive the batch's image and video
+// segment counts.
+template <typename Emit, typename End>
+__device__ int chunk_carries(const RopeIndexParams& p, int* rec, int n, int* sh, int* img_total,
+                             int* vid_total, Emit emit, End end) {
   const int per = (n + kPT - 1) / kPT;
   const int c0 = min(n, (int)threadIdx.x * per);
   const int c1 = min(n, c0 + per);
   const int C = p.C > 0 ? p.C : 1;
-  // The passes below re-read the per-chunk records several times: keep them
-  // in LDS when they fit (the provisional records never go back to memory).
-  __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
-  int* const rec = n <= kPosCarryLds ? rec_lds : p.ws_sum;
-  if (n <= kPosCarryLds) {
-    for (int i = threadIdx.x; i < n * kPosSumInts; i += kPT) rec_lds[i] = p.ws_sum[i];
-    __syncthreads();
-  }
 
   // Pass 1: valid / text counts, the latest valid type, summary flags.
   int t_nv = 0, t_nt = 0, t_lt = -1, t_flags = 0;
@@ -440,9 +529,8 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
       if (lts >= 0) lt = (c << 2) | lts;
     }
   }
-  int img_total, vid_total;
-  int img = block_excl_sum(t_ni, &img_total, sh);
-  int vid = block_excl_sum(t_nvd, &vid_total, sh);
+  int img = block_excl_sum(t_ni, img_total, sh);
+  int vid = block_excl_sum(t_nvd, vid_total, sh);
   int st = block_excl_max(t_st, -1, &tot, sh);
 
   // Pass 3a: grid counters per chunk.
@@ -469,38 +557,75 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
       const int F0 = s0[0];
       const int S_in = (st >= 0 && (st >> 2) >= F0) ? (st >> 2) - F0 : -1;
       const int segT_in = S_in >= 0 ? (st & 3) : -1;
-      int* o = p.ws_carry + (int64_t)c * kPosCarryInts;
-      o[0] = s[0] - F0;
-      o[1] = s[1] - s0[1];
-      o[2] = s[2];
-      o[3] = s[6];
-      o[4] = s[7];
-      o[5] = s0[6];
-      o[6] = s0[7];
-      o[7] = S_in;
-      o[8] = segT_in;
+      const int o[kPosCarryInts] = {s[0] - F0, s[1] - s0[1], s[2],  s[6],   s[7],
+                                    s0[6],     s0[7],       S_in, segT_in};
+      emit(c, o);
       if (s[5] > st) st = s[5];
       if (c - first == C - 1) {
-        // the sample's end: valid length, the open segment, the delta's seed
+        // the sample's end: valid length and the open segment
         const int valid = s[0] + s[8] - F0;
         const int S_end = (st >= 0 && (st >> 2) >= F0) ? (st >> 2) - F0 : -1;
         const int segT_end = S_end >= 0 ? (st & 3) : -1;
-        p.ws_valid[b] = valid;
-        p.rope_delta[b] = valid == 0 ? 0 : INT32_MIN;
-        int* e = p.ws_end + 3 * b;
-        e[0] = valid - S_end;
-        e[1] = segT_end;
-        e[2] = segT_end == 1 ? s[6] + s[3] - 1 : s[7] + s[4] - 1;
+        end(b, valid, valid - S_end, segT_end,
+            segT_end == 1 ? s[6] + s[3] - 1 : s[7] + s[4] - 1);
       }
     }
   }
+  return flags;
+}
+
+__global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p) {
+  __shared__ int sh[kWaves];
+  __shared__ long long shl[kWaves];
+  __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
+  const int n = p.B * p.C;
+  // The first tile of each grid table and the chunk records (when they fit
+  // LDS) are loaded before any of them is used: one memory round trip.
+  const bool rec_in_lds = n <= kPosCarryLds;
+  const int tg = 3 * (int)threadIdx.x;
+  const int ih = load_in_range(p.image_grid, 3u * (uint32_t)p.n_images, tg + 1);
+  const int iw = load_in_range(p.image_grid, 3u * (uint32_t)p.n_images, tg + 2);
+  const int vt = load_in_range(p.video_grid, 3u * (uint32_t)p.n_videos, tg);
+  const int vh = load_in_range(p.video_grid, 3u * (uint32_t)p.n_videos, tg + 1);
+  const int vw = load_in_range(p.video_grid, 3u * (uint32_t)p.n_videos, tg + 2);
+  int rv[kRecIt];
+  if (rec_in_lds) load_records(p, n, rv);
+  const int slices =
+      grid_prefix_tables(p, ih, iw, vt, vh, vw, shl, [&](int table, int i, long long v) {
+        if (table == 0) p.ws_adv_i[i] = v;
+        else if (table == 1) p.ws_cum_t[i] = (int)v;
+        else p.ws_adv_v[i] = v;
+      });
+  // The passes re-read the per-chunk records several times: keep them in LDS
+  // when they fit (the provisional records never go back to memory).
+  int* const rec = rec_in_lds ? rec_lds : p.ws_sum;
+  if (rec_in_lds) {
+    store_records(rv, n, rec_lds);
+    __syncthreads();
+  }
+  int img_total, vid_total;
+  const int flags = chunk_carries(
+      p, rec, n, sh, &img_total, &vid_total,
+      [&](int c, const int (&o)[kPosCarryInts]) {
+        int* d = p.ws_carry + (int64_t)c * kPosCarryInts;
+#pragma unroll
+        for (int i = 0; i < kPosCarryInts; ++i) d[i] = o[i];
+      },
+      [&](int b, int valid, int open_len, int open_type, int open_grid) {
+        p.ws_valid[b] = valid;
+        p.rope_delta[b] = valid == 0 ? 0 : INT32_MIN;
+        int* e = p.ws_end + 3 * b;
+        e[0] = open_len;
+        e[1] = open_type;
+        e[2] = open_grid;
+      });
   if (p.C == 0)   // empty sequences: every sample has delta 0
     for (int b = threadIdx.x; b < p.B; b += kPT) p.rope_delta[b] = 0;
   // (each sample's last segment is checked by the apply pass, which has
   // the grid tables at hand)
   if (threadIdx.x == 0) {
     int status = flags;
-    if (img_total > p.n_images || vid_total > (int)ct) status |= MROPE_POS_NO_GRID;
+    if (img_total > p.n_images || vid_total > slices) status |= MROPE_POS_NO_GRID;
     *p.status = status;
   }
 }
@@ -509,44 +634,22 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
 // Pass 3: positions.
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p) {
-  __shared__ int sh[kWaves];
-  __shared__ unsigned long long shu[kWaves];
-  __shared__ long long shl[kWaves];
-  // LDS copy of the grid tables when they are small (the common case): the
-  // segment starts of a chunk then look grids up without memory round trips.
-  __shared__ int32_t t_img[3 * kPosStageGrids];
-  __shared__ int64_t t_adv_i[kPosStageGrids + 1];
-  __shared__ int32_t t_vid[3 * kPosStageGrids];
-  __shared__ int32_t t_cum_t[kPosStageGrids + 1];
-  __shared__ int64_t t_adv_v[kPosStageGrids + 1];
-  Tables tb = global_tables(p);
-  if (p.n_images <= kPosStageGrids && p.n_videos <= kPosStageGrids) {
-    for (int i = threadIdx.x; i < 3 * p.n_images; i += kPT) t_img[i] = p.image_grid[i];
-    for (int i = threadIdx.x; i <= p.n_images; i += kPT) t_adv_i[i] = p.ws_adv_i[i];
-    for (int i = threadIdx.x; i < 3 * p.n_videos; i += kPT) t_vid[i] = p.video_grid[i];
-    for (int i = threadIdx.x; i <= p.n_videos; i += kPT) {
-      t_cum_t[i] = p.ws_cum_t[i];
-      t_adv_v[i] = p.ws_adv_v[i];
-    }
-    tb.img = t_img;
-    tb.adv_i = t_adv_i;
-    tb.vid = t_vid;
-    tb.cum_t = t_cum_t;
-    tb.adv_v = t_adv_v;
-    // the copies are ordered before their first use by the barriers of the
-    // block scans below
-  }
-  const int b = (int)(blockIdx.x / (unsigned)p.C);
-  const int j = (int)(blockIdx.x - (unsigned)b * (unsigned)p.C);
-  const int* cin = p.ws_carry + ((int64_t)b * p.C + j) * kPosCarryInts;
+// Positions of chunk j of sample b from its carry-in cin, the sample's valid
+// length, the segment open at the sample's end e (length, type, grid index;
+// read by the sample's last chunk), and the chunk's token words.
+// extra_flags are status bits found before; every block ORs its bits into
+// the status word and raises rope_delta[b] to its largest position + 1 -
+// valid length.
+__device__ __forceinline__ void apply_chunk(const RopeIndexParams& p, const Tables& tb, int b,
+                                            int j, const int (&cin)[kPosCarryInts],
+                                            int valid_len, const int* e, const RunWords& words,
+                                            int extra_flags, int* sh, unsigned long long* shu,
+                                            long long* shl) {
   const int F_in = cin[0], A_in = cin[1], prevT_in = cin[2], img_in = cin[3], vid_in = cin[4];
   const int img_base = cin[5], vid_base = cin[6], S_in = cin[7], segT_in = cin[8];
-  const int valid_len = p.ws_valid[b];
-
   const int64_t l0 = (int64_t)j * kPosChunk + (int64_t)threadIdx.x * kPer;
   Run r;
-  read_run(p, b, l0, r);
+  parse_run(p, l0, words, r);
   int lt_tot;
   const int pe = block_excl_max(r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1, -1, &lt_tot, sh);
   int prevT = pe >= 0 ? (pe & 3) : prevT_in;
@@ -574,7 +677,7 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
   const int64_t adv0 = image_adv_before(tb, img_base) + video_adv_before(tb, vid_base);
   int64_t badv = image_adv_before(tb, img) + video_adv_before(tb, vid) - adv0;
 
-  int flags = 0;   // bad types were reported by the summary pass
+  int flags = extra_flags;
   int64_t mx = INT64_MIN;
   const int64_t tok0 = (int64_t)b * p.L + l0;
 #pragma unroll
@@ -627,7 +730,6 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
   // the sample's last segment must be complete (checked once, by the block
   // of its last chunk)
   if (j == p.C - 1 && threadIdx.x == 0) {
-    const int* e = p.ws_end + 3 * b;
     if (e[1] == 1 || e[1] == 2) {
       const Grid ge = grid_of(tb, e[1], e[2]);
       if (ge.ok && e[0] != ge.slots) flags |= MROPE_POS_LENGTH;
@@ -640,6 +742,160 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
     if (bmax != (long long)INT64_MIN) atomicMax(&p.rope_delta[b], (int)(bmax + 1 - valid_len));
     if (f) atomicOr(p.status, f);
   }
+}
+
+__global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p) {
+  __shared__ int sh[kWaves];
+  __shared__ unsigned long long shu[kWaves];
+  __shared__ long long shl[kWaves];
+  // LDS copy of the grid tables when they are small (the common case): the
+  // segment starts of a chunk then look grids up without memory round trips.
+  __shared__ int32_t t_img[3 * kPosStageGrids];
+  __shared__ int64_t t_adv_i[kPosStageGrids + 1];
+  __shared__ int32_t t_vid[3 * kPosStageGrids];
+  __shared__ int32_t t_cum_t[kPosStageGrids + 1];
+  __shared__ int64_t t_adv_v[kPosStageGrids + 1];
+  // Every global load of the block (the tables, the chunk's carry, its
+  // tokens) is issued before the first wait, so the block pays one memory
+  // round trip before its scans.
+  Tables tb = global_tables(p);
+  const bool stage = p.n_images <= kPosStageGrids && p.n_videos <= kPosStageGrids;
+  int32_t gi[kGridIt], gv[kGridIt], gc[kAdvIt];
+  int64_t ga[kAdvIt], gw[kAdvIt];
+  if (stage) {
+#pragma unroll
+    for (int u = 0; u < kGridIt; ++u) {
+      const int i = threadIdx.x + u * kPT;
+      gi[u] = i < 3 * p.n_images ? p.image_grid[i] : 0;
+      gv[u] = i < 3 * p.n_videos ? p.video_grid[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kAdvIt; ++u) {
+      const int i = threadIdx.x + u * kPT;
+      ga[u] = i <= p.n_images ? p.ws_adv_i[i] : 0;
+      gc[u] = i <= p.n_videos ? p.ws_cum_t[i] : 0;
+      gw[u] = i <= p.n_videos ? p.ws_adv_v[i] : 0;
+    }
+  }
+  const int b = (int)(blockIdx.x / (unsigned)p.C);
+  const int j = (int)(blockIdx.x - (unsigned)b * (unsigned)p.C);
+  int cin[kPosCarryInts];
+  const int* cg = p.ws_carry + ((int64_t)b * p.C + j) * kPosCarryInts;
+#pragma unroll
+  for (int i = 0; i < kPosCarryInts; ++i) cin[i] = cg[i];
+  const int valid_len = p.ws_valid[b];
+
+  const int64_t l0 = (int64_t)j * kPosChunk + (int64_t)threadIdx.x * kPer;
+  RunWords words;
+  load_run(p, b, l0, words);
+  if (stage) {
+#pragma unroll
+    for (int u = 0; u < kGridIt; ++u) {
+      const int i = threadIdx.x + u * kPT;
+      if (i < 3 * p.n_images) t_img[i] = gi[u];
+      if (i < 3 * p.n_videos) t_vid[i] = gv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kAdvIt; ++u) {
+      const int i = threadIdx.x + u * kPT;
+      if (i <= p.n_images) t_adv_i[i] = ga[u];
+      if (i <= p.n_videos) {
+        t_cum_t[i] = gc[u];
+        t_adv_v[i] = gw[u];
+      }
+    }
+    tb.img = t_img;
+    tb.adv_i = t_adv_i;
+    tb.vid = t_vid;
+    tb.cum_t = t_cum_t;
+    tb.adv_v = t_adv_v;
+    // the copies are ordered before their first use by the barriers of the
+    // block scans in apply_chunk
+  }
+  // bad types were reported by the summary pass, through the carry pass
+  apply_chunk(p, tb, b, j, cin, valid_len, p.ws_end + 3 * b, words, 0, sh, shu, shl);
+}
+
+// Passes 2 and 3 in one kernel (the chunk records fit LDS, the grids fit the
+// LDS tables): each block runs the carry work on the whole batch in LDS and
+// then writes its own chunk's positions.  The summary pass has set the
+// status word to 0 and every rope_delta to INT32_MIN.
+__global__ void __launch_bounds__(kPT) rope_index_fused(const RopeIndexParams p) {
+  __shared__ int sh[kWaves];
+  __shared__ unsigned long long shu[kWaves];
+  __shared__ long long shl[kWaves];
+  __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
+  __shared__ int32_t t_img[3 * kPosStageGrids];
+  __shared__ int64_t t_adv_i[kPosStageGrids + 1];
+  __shared__ int32_t t_vid[3 * kPosStageGrids];
+  __shared__ int32_t t_cum_t[kPosStageGrids + 1];
+  __shared__ int64_t t_adv_v[kPosStageGrids + 1];
+  __shared__ int own_carry[kPosCarryInts];
+  __shared__ int own_end[4];   // valid length, open length, open type, open grid
+  const int n = p.B * p.C;
+  const int b = (int)(blockIdx.x / (unsigned)p.C);
+  const int j = (int)(blockIdx.x - (unsigned)b * (unsigned)p.C);
+  const int c_self = (int)blockIdx.x;
+  // every global load first: grids, chunk summaries, this chunk's tokens
+  int32_t gi[kGridIt], gv[kGridIt];
+#pragma unroll
+  for (int u = 0; u < kGridIt; ++u) {
+    const int i = threadIdx.x + u * kPT;
+    gi[u] = load_in_range(p.image_grid, 3u * (uint32_t)p.n_images, i);
+    gv[u] = load_in_range(p.video_grid, 3u * (uint32_t)p.n_videos, i);
+  }
+  int rv[kRecIt];
+  load_records(p, n, rv);
+  const int64_t l0 = (int64_t)j * kPosChunk + (int64_t)threadIdx.x * kPer;
+  RunWords words;
+  load_run(p, b, l0, words);
+#pragma unroll
+  for (int u = 0; u < kGridIt; ++u) {
+    const int i = threadIdx.x + u * kPT;
+    if (i < 3 * p.n_images) t_img[i] = gi[u];
+    if (i < 3 * p.n_videos) t_vid[i] = gv[u];
+  }
+  store_records(rv, n, rec_lds);
+  __syncthreads();
+  const int k = threadIdx.x;
+  const int ih = k < p.n_images ? t_img[3 * k + 1] : 0;
+  const int iw = k < p.n_images ? t_img[3 * k + 2] : 0;
+  const int vt = k < p.n_videos ? t_vid[3 * k] : 0;
+  const int vh = k < p.n_videos ? t_vid[3 * k + 1] : 0;
+  const int vw = k < p.n_videos ? t_vid[3 * k + 2] : 0;
+  const int slices =
+      grid_prefix_tables(p, ih, iw, vt, vh, vw, shl, [&](int table, int i, long long v) {
+        if (table == 0) t_adv_i[i] = v;
+        else if (table == 1) t_cum_t[i] = (int)v;
+        else t_adv_v[i] = v;
+      });
+  int img_total, vid_total;
+  int flags = chunk_carries(
+      p, rec_lds, n, sh, &img_total, &vid_total,
+      [&](int c, const int (&o)[kPosCarryInts]) {
+        if (c == c_self) {
+#pragma unroll
+          for (int i = 0; i < kPosCarryInts; ++i) own_carry[i] = o[i];
+        }
+      },
+      [&](int bb, int valid, int open_len, int open_type, int open_grid) {
+        if (bb == b) {
+          own_end[0] = valid;
+          own_end[1] = open_len;
+          own_end[2] = open_type;
+          own_end[3] = open_grid;
+        }
+      });
+  if (img_total > p.n_images || vid_total > slices) flags |= MROPE_POS_NO_GRID;
+  __syncthreads();
+  int cin[kPosCarryInts];
+#pragma unroll
+  for (int i = 0; i < kPosCarryInts; ++i) cin[i] = own_carry[i];
+  const int valid_len = own_end[0];
+  // a sample without valid tokens raises no rope_delta: its delta is 0
+  if (valid_len == 0 && j == p.C - 1 && threadIdx.x == 0) p.rope_delta[b] = 0;
+  const Tables tb{t_img, t_adv_i, t_vid, t_cum_t, t_adv_v, p.n_images, p.n_videos, p.merge};
+  apply_chunk(p, tb, b, j, cin, valid_len, own_end + 1, words, flags, sh, shu, shl);
 }
 
 // ---------------------------------------------------------------------------
@@ -702,14 +958,21 @@ __global__ void __launch_bounds__(kPT) vision_pos_ids_kernel(const VisionPosPara
 
 }  // namespace
 
-int launch_rope_index(const RopeIndexParams& p, void* stream) {
+int launch_rope_index(const RopeIndexParams& p, void* stream, const char** kernel) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t chunks = (int64_t)p.B * p.C;
   if (chunks > 0)
     hipLaunchKernelGGL(rope_index_summarize, dim3((unsigned)chunks), dim3(kPT), 0, st, p);
-  hipLaunchKernelGGL(rope_index_carry, dim3(1), dim3(kPT), 0, st, p);
-  if (chunks > 0)
-    hipLaunchKernelGGL(rope_index_apply, dim3((unsigned)chunks), dim3(kPT), 0, st, p);
+  const bool fused = chunks > 0 && chunks <= kPosCarryLds && p.n_images <= kPosStageGrids &&
+                     p.n_videos <= kPosStageGrids;
+  *kernel = fused ? "rope_index_fused" : "rope_index_carry+apply";
+  if (fused) {
+    hipLaunchKernelGGL(rope_index_fused, dim3((unsigned)chunks), dim3(kPT), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(rope_index_carry, dim3(1), dim3(kPT), 0, st, p);
+    if (chunks > 0)
+      hipLaunchKernelGGL(rope_index_apply, dim3((unsigned)chunks), dim3(kPT), 0, st, p);
+  }
   return (int)hipGetLastError();
 }
 
