@@ -59,11 +59,24 @@ def first_row_split(r, H):
     return tl, r - tl * H
 
 
+def first_row_split_lanes(r, H):
+    """first_row_split over an array of rows (the same binary32 arithmetic)."""
+    r = np.asarray(r, dtype=np.int64)
+    inv = np.float32(np.float32(1.0) / np.float32(H))
+    tl = (r.astype(np.float32) * inv).astype(np.float32).astype(np.int64)
+    tl = np.where(tl * H > r, tl - 1, tl)
+    tl = np.where((tl + 1) * H <= r, tl + 1, tl)
+    return tl, r - tl * H
+
+
 def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_waves=MIN_WAVES,
-             head_major=False):
+             head_major=False, pre_steps=0):
     """Returns per-slot write counts of the outputs (q, k and, with three
     head counts, the copied v of a packed qkv); asserts read and write
-    bounds.  head_major puts the outputs in per-head planes."""
+    bounds.  head_major puts the outputs in per-head planes.  pre_steps
+    row-steps are issued ahead of the rest (the decode and RMSNorm forms
+    preload 1 and 2).  U (steps per batch of loads) orders the steps within a
+    run but not which rows they cover, so the model takes them one by one."""
     p = plan(T, D, rd, es, fused=fused, wave_tokens=wave_tokens, heads=heads,
              min_waves=min_waves)
     v, half, lpr, rpw, lrot, nt = p["v"], p["half"], p["lpr"], p["rpw"], p["lrot"], p["nt"]
@@ -95,20 +108,15 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
             pre.append(pre[-1] + -(-ntok * H // rpw))
         steps_all = pre[-1]
         sb, se = steps_all * part // parts, steps_all * (part + 1) // parts
-        for s, H in enumerate(heads):
-            if H == 0:
-                continue
-            lo = max(sb, pre[s]) - pre[s]
-            hi = min(se, pre[s + 1]) - pre[s]
-            if lo >= hi:
-                continue
+        def run(s, lo, enabled):
+            """Row-steps lo, lo + 1, ... of tensor s, one per entry of
+            `enabled` (False: the step is issued with every lane masked)."""
+            H = heads[s]
             extent = ((ntok - 1) * xts[s] + H * D) * es   # tile buffer size in bytes
             out_extent = ((ntok - 1) * yts[s] + (H - 1) * yhs[s] + D) * es
             assert extent < OUT_OF_RANGE and out_extent < OUT_OF_RANGE
             nrows = ntok * H
-            split = [first_row_split(int(lo * rpw + g), H) for g in grp]
-            tl = np.array([a for a, _ in split])
-            h = np.array([b for _, b in split])
+            tl, h = first_row_split_lanes(lo * rpw + grp, H)
             dq, dr = rpw // H, rpw % H
             xo = (tl * xts[s] + h * D) * es
             xinc = (dq * xts[s] + dr * D) * es
@@ -116,42 +124,66 @@ def simulate(T, heads, D, rd, es, fused=True, U=2, wave_tokens=WAVE_TOKENS, min_
             yo = (tl * yts[s] + h * yhs[s]) * es
             yinc = (dq * yts[s] + dr * yhs[s]) * es
             ywrap = (yts[s] - H * yhs[s]) * es
-            full = (hi - lo) // U
-            batches = [U] * full + [1] * ((hi - lo) - full * U)
             r0 = lo * rpw
-            for uu in batches:
-                for u in range(uu):
-                    r = r0 + u * rpw + grp
-                    ok = lane_on & (r < nrows)
+            for on in enabled:
+                r = r0 + grp
+                ok = lane_on & (r < nrows) & on
+                if on:
                     assert np.all(tl[ok] == r[ok] // H) and np.all(h[ok] == r[ok] % H)
-                    off = np.where(ok, xo, OUT_OF_RANGE)
-                    # live rows stay inside the tile buffer, masked ones outside it
-                    assert np.all(off[ok] + col_b[ok] * es + v * es <= extent)
-                    assert np.all(off[~ok] >= extent)
-                    yoff = np.where(ok, yo, OUT_OF_RANGE)
-                    assert np.all(yoff[ok] + col_b[ok] * es + v * es <= out_extent)
-                    assert np.all(yoff[ok] >= 0)
-                    assert np.all(yoff[~ok] >= out_extent)
-                    # the store address is the element (t, h, col) of the view
-                    assert np.all(yoff[ok] == (tl[ok] * yts[s] + h[ok] * yhs[s]) * es)
-                    tlr = np.where(ok, tl, 0)
-                    if fused:
-                        o = tlr * half + col_a
-                        assert np.all(o[l < lrot] + v <= nt * half)
-                    for i in np.nonzero(ok)[0]:
-                        tok = t0 + tl[i]
-                        writes[s][tok, h[i], col_a[i]:col_a[i] + v] += 1
-                        writes[s][tok, h[i], col_b[i]:col_b[i] + v] += 1
-                    xo = xo + xinc
-                    yo = yo + yinc
-                    h = h + dr
-                    tl = tl + dq
-                    wrap = h >= H
-                    h = np.where(wrap, h - H, h)
-                    tl = np.where(wrap, tl + 1, tl)
-                    xo = np.where(wrap, xo + xwrap, xo)
-                    yo = np.where(wrap, yo + ywrap, yo)
-                r0 += uu * rpw
+                off = np.where(ok, xo, OUT_OF_RANGE)
+                # live rows stay inside the tile buffer, masked ones outside it
+                assert np.all(off[ok] + col_b[ok] * es + v * es <= extent)
+                assert np.all(off[~ok] >= extent)
+                yoff = np.where(ok, yo, OUT_OF_RANGE)
+                assert np.all(yoff[ok] + col_b[ok] * es + v * es <= out_extent)
+                assert np.all(yoff[ok] >= 0)
+                assert np.all(yoff[~ok] >= out_extent)
+                # the store address is the element (t, h, col) of the view
+                assert np.all(yoff[ok] == (tl[ok] * yts[s] + h[ok] * yhs[s]) * es)
+                tlr = np.where(ok, tl, 0)
+                if fused:
+                    o = tlr * half + col_a
+                    assert np.all(o[l < lrot] + v <= nt * half)
+                tok = (t0 + tl[ok])[:, None]
+                hh = h[ok][:, None]
+                span_v = np.arange(v)[None, :]
+                np.add.at(writes[s], (tok, hh, col_a[ok][:, None] + span_v), 1)
+                np.add.at(writes[s], (tok, hh, col_b[ok][:, None] + span_v), 1)
+                xo = xo + xinc
+                yo = yo + yinc
+                h = h + dr
+                tl = tl + dq
+                wrap = h >= H
+                h = np.where(wrap, h - H, h)
+                tl = np.where(wrap, tl + 1, tl)
+                xo = np.where(wrap, xo + xwrap, xo)
+                yo = np.where(wrap, yo + ywrap, yo)
+                r0 += rpw
+
+        def span(s):
+            return max(sb, pre[s]) - pre[s], min(se, pre[s + 1]) - pre[s]
+
+        # the first pre_steps row-steps of the part's first q or k work,
+        # issued before the cos/sin prologue (masked past the available ones)
+        s_pre, n_pre = None, 0
+        if pre_steps:
+            for s in (0, 1):
+                if s < len(heads) and heads[s] > 0 and span(s)[0] < span(s)[1]:
+                    s_pre = s
+                    break
+            if s_pre is not None:
+                lo, hi = span(s_pre)
+                n_pre = min(pre_steps, hi - lo)
+                run(s_pre, lo, [u < n_pre for u in range(pre_steps)])
+        for s, H in enumerate(heads):
+            if H == 0:
+                continue
+            lo, hi = span(s)
+            if s == s_pre:
+                lo += n_pre
+            if lo >= hi:
+                continue
+            run(s, lo, [True] * (hi - lo))
     return writes, p
 
 
@@ -159,6 +191,12 @@ def test_first_row_split_exact():
     for H in range(1, 4097):
         for g in range(64):
             assert first_row_split(g, H) == (g // H, g % H), (g, H)
+    rng = np.random.default_rng(1)
+    for H in list(range(1, 200)) + [int(x) for x in rng.integers(1, 100000, 200)]:
+        r = rng.integers(0, 2 ** 23, 64)
+        tl, h = first_row_split_lanes(r, H)
+        assert np.array_equal(tl, r // H) and np.array_equal(h, r % H)
+        assert [first_row_split(int(x), H) for x in r] == list(zip(tl.tolist(), h.tolist()))
     rng = np.random.default_rng(0)
     for _ in range(20000):
         H = int(rng.integers(1, 100000))
@@ -185,12 +223,16 @@ GEOMS = [
 ]
 
 
-@pytest.mark.parametrize("U,wave_tokens,min_waves", [(1, 1, 1), (2, 1, 2048), (4, 2, 2048),
-                                                      (2, 16, 64), (2, 1, 1 << 20)])
+@pytest.mark.parametrize("U,wave_tokens,min_waves,pre_steps", [
+    (1, 1, 1, 0), (2, 1, 2048, 0), (4, 2, 2048, 0), (2, 16, 64, 0), (2, 1, 1 << 20, 0),
+    (2, 1, 2048, 1),                                                 # decode's preload
+    (1, 1, 1, 2), (2, 1, 2048, 2), (4, 2, 2048, 2), (2, 16, 64, 2), (2, 1, 1 << 20, 2),
+])
 @pytest.mark.parametrize("T,heads,D,rd,es", GEOMS)
 def test_every_output_written_once_and_reads_in_bounds(T, heads, D, rd, es, U, wave_tokens,
-                                                         min_waves):
-    writes, p = simulate(T, heads, D, rd, es, U=U, wave_tokens=wave_tokens, min_waves=min_waves)
+                                                         min_waves, pre_steps):
+    writes, p = simulate(T, heads, D, rd, es, U=U, wave_tokens=wave_tokens, min_waves=min_waves,
+                         pre_steps=pre_steps)
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))
@@ -207,8 +249,9 @@ def test_rms_norm_only_geometry():
 def test_decode_sized_launch_splits_tiles():
     p = plan(512, 128, 128, 2, heads=(32, 4))
     assert p["parts"] == 4 and p["nwaves"] == 2048
-    writes, p = simulate(512, (32, 4), 128, 128, 2)
-    assert np.all(writes[0] == 1) and np.all(writes[1] == 1)
+    for pre_steps in (0, 1):
+        writes, p = simulate(512, (32, 4), 128, 128, 2, pre_steps=pre_steps)
+        assert np.all(writes[0] == 1) and np.all(writes[1] == 1)
 
 
 def test_full_size_plans():
@@ -231,7 +274,8 @@ def test_full_size_plans():
     (50, (16, 16, 0), 72, 72, 4, 2048),      # without v
 ])
 def test_three_slot_packed_qkv(T, heads, D, rd, es, min_waves, head_major):
-    writes, p = simulate(T, heads, D, rd, es, min_waves=min_waves, head_major=head_major)
+    writes, p = simulate(T, heads, D, rd, es, min_waves=min_waves, head_major=head_major,
+                         pre_steps=2)
     for s, H in enumerate(heads):
         if H:
             assert np.all(writes[s] == 1), (s, np.unique(writes[s]))

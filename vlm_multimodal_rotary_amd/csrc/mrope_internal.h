@@ -65,6 +65,10 @@ struct QKParams {
   float inv_heads[kSlots];      // 1 / heads, per tensor (launcher)
   const int32_t* pos;
   int64_t pos_stride;
+  // axis of frequency column j as a rule (set by the launcher from the
+  // column table): ax_mode 0: (j >= ax_a) + (j >= ax_b); 1: 1 if j % 3 == 1
+  // and j < ax_a, 2 if j % 3 == 2 and j < ax_b, else 0; -1: read the table
+  int ax_mode, ax_a, ax_b;
   const float* cos;
   const float* sin;
   int64_t cs_ts;

@@ -579,19 +579,50 @@ qk_kernel(const QKParams p, const ColTable tab) {
                          (seq * p.kc_seq + (int64_t)(in_cache ? slot : 0) * p.kc_tok) * ES,
                      in_cache ? (uint32_t)((int64_t)p.heads[1] * p.D * ES) : 0u);
   };
-  // Decode: the part's first row-step (and its norm weights) is loaded before
-  // the token's cache length is read and its cos/sin formed, and finished
-  // right after.  Vector memory waits count loads in issue order, so the one
-  // inv_freq value the cos/sin needs is loaded first and the loads are issued
-  // on every path (out of range where there is no work): the cos/sin then
-  // waits for that value alone.
+  // Decode and the fused RMSNorm path: the part's first row-steps (and their
+  // norm weights) are loaded before the tile's cos/sin are formed, and
+  // finished right after, so the sincos overlaps their memory latency.
+  // Decode preloads one step, the positions path two (three or four measured
+  // slower: more registers, or no gain).  Vector memory waits count loads in
+  // issue order, so what the cos/sin needs (inv_freq values, and on the
+  // positions path the positions, addressed through the axis rule rather
+  // than a table load) is loaded first, and the row loads are issued on
+  // every path (out of range where there is no work): the cos/sin then waits
+  // for its own inputs alone.
   [[maybe_unused]] int s_pre = -1;
   [[maybe_unused]] SlotState<CB> st_pre;
-  [[maybe_unused]] StepLoads<CB, 1> L_pre;
+  constexpr int kPreSteps = 2;   // row-steps preloaded on the positions path (decode: 1)
+  [[maybe_unused]] StepLoads<CB, 1> L_pre, L_more[kPreSteps - 1];
+  [[maybe_unused]] int n_pre_steps = 0;
   [[maybe_unused]] float inv_first = 0.f;
   [[maybe_unused]] Words<CB> w_pre_a, w_pre_b;
-  if constexpr (CS == kCsDecode) {
-    if (lane < half) inv_first = tab.inv[lane];
+  // Positions path: the cos/sin inputs of the prologue's first kPrePos
+  // iterations (tiles up to 128 (token, column) pairs) are loaded up front.
+  // Without RMSNorm the preload measured no faster, so it is off there.
+  constexpr int kPrePos = 2;
+  constexpr bool kPrePosPath = CS == kCsFromPositions && NORM;
+  [[maybe_unused]] int32_t pos_pre[kPrePos];
+  [[maybe_unused]] float inv_pre[kPrePos];
+  if constexpr (kPrePosPath) {
+    const int n_cs = ntok * half;
+#pragma unroll
+    for (int m = 0; m < kPrePos; ++m) {
+      const int idx = lane + m * kWaveSize;
+      const int id = idx < n_cs ? idx : 0;
+      const int tl = id / half;
+      const int j = id - tl * half;
+      int ax;
+      if (p.ax_mode == 0) ax = (j >= p.ax_a) + (j >= p.ax_b);
+      else if (p.ax_mode == 1) ax = (j % 3 == 1 && j < p.ax_a) ? 1 : (j % 3 == 2 && j < p.ax_b) ? 2 : 0;
+      else ax = tab.axis[j];
+      pos_pre[m] = p.pos[(int64_t)ax * p.pos_stride + t0 + tl];
+      inv_pre[m] = tab.inv[j];
+    }
+  }
+  if constexpr (CS == kCsDecode || kPrePosPath) {
+    if constexpr (CS == kCsDecode) {
+      if (lane < half) inv_first = tab.inv[lane];
+    }
     const int lo0 = (step_begin > pre[0] ? step_begin : pre[0]) - pre[0];
     const int hi0 = (step_end < pre[1] ? step_end : pre[1]) - pre[0];
     const int lo1 = (step_begin > pre[1] ? step_begin : pre[1]) - pre[1];
@@ -612,6 +643,17 @@ qk_kernel(const QKParams p, const ColTable tab) {
       buf_load<CB>(rw, cb, w_pre_b);
     }
     load_steps<CB, 1>(st_pre, lo_pre * rpw, grp, rpw, lane_on && s_pre >= 0, ca, cb, L_pre);
+    if constexpr (kPrePosPath) {
+      const int hi_pre = s_pre == 0 ? hi0 : hi1;
+      const int avail = s_pre < 0 ? 0 : hi_pre - lo_pre;
+      n_pre_steps = avail < kPreSteps ? avail : kPreSteps;
+#pragma unroll
+      for (int u = 0; u < kPreSteps - 1; ++u)
+        load_steps<CB, 1>(st_pre, (lo_pre + 1 + u) * rpw, grp, rpw, lane_on && u + 1 < n_pre_steps,
+                          ca, cb, L_more[u]);
+    } else {
+      n_pre_steps = s_pre >= 0 ? 1 : 0;
+    }
   }
   {
     // Decode: token t0 is token i of sequence b; its text position (the same
@@ -641,7 +683,28 @@ qk_kernel(const QKParams p, const ColTable tab) {
     }
     if constexpr (CS == kCsFromPositions) {
       const int n = ntok * half;
-      for (int idx = lane; idx < n; idx += kWaveSize) {
+      const int n_pre = kPrePosPath ? kPrePos : 0;
+#pragma unroll
+      for (int m = 0; m < n_pre; ++m) {
+        const int idx = lane + m * kWaveSize;
+        if (idx < n) {
+          const int tl = idx / half;
+          const int j = idx - tl * half;
+          const int32_t pp = pos_pre[m];
+          float c, s;
+          if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
+            const float2 cs = *reinterpret_cast<const float2*>(
+                p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
+            c = cs.x;
+            s = cs.y;
+          } else {
+            angle_cos_sin(pp, inv_pre[m], c, s);
+          }
+          lc[idx] = (cs_t)c;
+          ls[idx] = (cs_t)s;
+        }
+      }
+      for (int idx = lane + n_pre * kWaveSize; idx < n; idx += kWaveSize) {
         const int tl = idx / half;
         const int j = idx - tl * half;
         const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t0 + tl];
@@ -665,9 +728,11 @@ qk_kernel(const QKParams p, const ColTable tab) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    if constexpr (CS == kCsDecode) {
+    if constexpr (CS == kCsDecode || kPrePosPath) {
       if (s_pre >= 0) {
-        if (s_pre == 1) st_pre.ry = k_cache_buffer(dec_seq, dec_slot);
+        if constexpr (CS == kCsDecode) {
+          if (s_pre == 1) st_pre.ry = k_cache_buffer(dec_seq, dec_slot);
+        }
         float wa[V], wb[V];
         if constexpr (NORM) {
           unpack<BF16, V>(w_pre_a, wa);
@@ -675,6 +740,12 @@ qk_kernel(const QKParams p, const ColTable tab) {
         }
         finish_steps<BF16, V, CS, NORM, LPR, PREC, 1>(st_pre, L_pre, p, lpr, rot, ca, cb, col_a,
                                                       wa, wb, lc, ls, t0);
+        if constexpr (kPrePosPath) {
+#pragma unroll
+          for (int u = 0; u < kPreSteps - 1; ++u)
+            finish_steps<BF16, V, CS, NORM, LPR, PREC, 1>(st_pre, L_more[u], p, lpr, rot, ca, cb,
+                                                          col_a, wa, wb, lc, ls, t0);
+        }
       }
     }
 #pragma unroll 1
@@ -684,7 +755,7 @@ qk_kernel(const QKParams p, const ColTable tab) {
       // This part's steps of tensor s.
       int lo = (step_begin > pre[s] ? step_begin : pre[s]) - pre[s];
       const int hi = (step_end < pre[s + 1] ? step_end : pre[s + 1]) - pre[s];
-      if (s == s_pre) ++lo;     // loaded and finished around the prologue
+      if (s == s_pre) lo += n_pre_steps;   // loaded and finished around the prologue
       if (lo >= hi) continue;
       SlotState<CB> st = make_state(s, lo);
       if constexpr (CS == kCsDecode) {
@@ -1241,9 +1312,41 @@ __global__ void __launch_bounds__(256) cos_sin_cache_kernel(const ColTable tab, 
   *reinterpret_cast<float2*>(cache + 2 * idx) = v;
 }
 
+// The axis table as one of the kernel's two rules (ax_mode 0 or 1), or -1.
+void fit_axis_rule(const ColTable& tab, int half, QKParams& p) {
+  int n0 = 0, n1 = 0, n2 = 0;
+  bool sorted = true;
+  for (int j = 0; j < half; ++j) {
+    n0 += tab.axis[j] == 0;
+    n1 += tab.axis[j] == 1;
+    n2 += tab.axis[j] == 2;
+    if (j > 0 && tab.axis[j] < tab.axis[j - 1]) sorted = false;
+  }
+  for (int mode = 0; mode < 2; ++mode) {
+    const int a = mode == 0 ? n0 : 3 * n1;
+    const int b = mode == 0 ? n0 + n1 : 3 * n2;
+    if (mode == 0 && !sorted) continue;
+    bool ok = true;
+    for (int j = 0; j < half && ok; ++j) {
+      const int ax = mode == 0 ? (j >= a) + (j >= b)
+                              : (j % 3 == 1 && j < a) ? 1 : (j % 3 == 2 && j < b) ? 2 : 0;
+      ok = ax == tab.axis[j];
+    }
+    if (ok) {
+      p.ax_mode = mode;
+      p.ax_a = a;
+      p.ax_b = b;
+      return;
+    }
+  }
+  p.ax_mode = -1;
+  p.ax_a = p.ax_b = 0;
+}
+
 template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
+  if (CS == kCsFromPositions) fit_axis_rule(tab, p.half, p);
   p.nt = nt_cap;   // tokens per wavefront, chosen by the host
   if (p.nt < 1 || CS == kCsDecode) p.nt = 1;
   for (int s = 0; s < kSlots; ++s) {
