@@ -143,6 +143,47 @@ __device__ T block_excl_max(T v, T lo, T* total, T* sh) {
   return prev > before ? prev : before;
 }
 
+// Several independent exclusive scans in one LDS round (two barriers in all).
+// kind[k]: 0 sum, 1 max, 2 bitwise or; id[k] is the identity of the k-th
+// scan; excl[k] receives the scan before this thread, total[k] the block's.
+// `sh` holds K * kWaves entries.  Contains barriers: every thread calls it.
+enum ScanKind : int { kScanSum = 0, kScanMax = 1, kScanOr = 2 };
+
+template <typename T>
+__device__ __forceinline__ T scan_op(int kind, T a, T b) {
+  return kind == kScanSum ? a + b : kind == kScanMax ? (a > b ? a : b) : (a | b);
+}
+
+template <int K, typename T>
+__device__ __forceinline__ void block_scan_multi(const T (&v)[K], const T (&id)[K],
+                                                 const int (&kind)[K], T (&excl)[K],
+                                                 T (&total)[K], T* sh) {
+  const int w = threadIdx.x / kWaveSize;
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  T prev[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int kd = kind[k];
+    const T incl = wave_incl_scan(v[k], id[k], [kd](T a, T b) { return scan_op(kd, a, b); });
+    prev[k] = dpp_move<0x138, 0xF>(id[k], incl);   // wave_shr 1: the lane before
+    if (lane == kWaveSize - 1) sh[k * kWaves + w] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    T before = id[k], all = id[k];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const T x = sh[k * kWaves + i];
+      if (i < w) before = scan_op(kind[k], before, x);
+      all = scan_op(kind[k], all, x);
+    }
+    excl[k] = scan_op(kind[k], before, prev[k]);
+    total[k] = all;
+  }
+  __syncthreads();
+}
+
 // Bitwise OR over the block.
 __device__ int block_or(int v, int* sh) {
   const int w = threadIdx.x / kWaveSize;
@@ -244,6 +285,7 @@ __device__ __forceinline__ int field(unsigned long long v, int i) {
 
 __global__ void __launch_bounds__(kPT) rope_index_summarize(const RopeIndexParams p) {
   __shared__ int sh[kWaves];
+  __shared__ int shm[3 * kWaves];
   __shared__ unsigned long long shu[kWaves];
   const int b = (int)(blockIdx.x / (unsigned)p.C);
   const int j = (int)(blockIdx.x - (unsigned)b * (unsigned)p.C);
@@ -252,9 +294,16 @@ __global__ void __launch_bounds__(kPT) rope_index_summarize(const RopeIndexParam
   read_run(p, b, l0, r);
   // latest valid type before this run in the chunk; the block total is the
   // chunk's last valid type
-  int last_enc;
-  const int enc = r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1;
-  const int pe = block_excl_max(enc, -1, &last_enc, sh);
+  // One round: the latest valid type before this run in the chunk (its block
+  // total is the chunk's last valid type), the chunk's first valid type (the
+  // smallest thread with a valid token), and the bad-type flags.
+  const int v1[3] = {r.lt >= 0 ? (int)(threadIdx.x << 2) | r.lt : -1,
+                     r.ft >= 0 ? (int)((kPT - 1 - threadIdx.x) << 2) | r.ft : -1, r.flags};
+  const int id1[3] = {-1, -1, 0};
+  const int kd1[3] = {kScanMax, kScanMax, kScanOr};
+  int ex1[3], tot1[3];
+  block_scan_multi(v1, id1, kd1, ex1, tot1, shm);
+  const int pe = ex1[0], last_enc = tot1[0], first_enc = tot1[1], fl_tot = tot1[2];
   const int pt = pe >= 0 ? (pe & 3) : -1;
   // The run's first valid token starts a segment when a valid token earlier
   // in the chunk has another type; the chunk's first valid token is decided
@@ -271,10 +320,6 @@ __global__ void __launch_bounds__(kPT) rope_index_summarize(const RopeIndexParam
   else if (fs) cand = (nv_ex << 2) | r.ft;
   int last_start;
   block_excl_max(cand, -1, &last_start, sh);
-  // first valid type of the chunk (the smallest thread with a valid token)
-  int first_enc;
-  block_excl_max(r.ft >= 0 ? (int)((kPT - 1 - threadIdx.x) << 2) | r.ft : -1, -1, &first_enc, sh);
-  const int fl_tot = block_or(r.flags, sh);
   if (threadIdx.x == 0) {
     // starting values for the fused pass 2+3 (the carry pass rewrites both)
     if (j == 0) p.rope_delta[b] = INT32_MIN;
@@ -420,6 +465,7 @@ __device__ __forceinline__ void store_records(const int (&rv)[kRecIt], int n, in
 // the first tile come in as (ih, iw) and (vt, vh, vw); put(0, k, adv_i[k]),
 // put(1, v, cum_t[v]) and put(2, v, adv_v[v]) store the entries.  Returns
 // the number of video slices.
+// `shl` holds 2 * kWaves entries.
 template <typename Put>
 __device__ int grid_prefix_tables(const RopeIndexParams& p, int ih, int iw, int vt, int vh,
                                   int vw, long long* shl, Put put) {
@@ -449,9 +495,12 @@ __device__ int grid_prefix_tables(const RopeIndexParams& p, int ih, int iw, int 
       t = t > 0 ? t : 0;
       a = t * ((h > w ? h : w) / p.merge);
     }
-    long long tt, ta;
-    const long long et = block_excl_sum(t, &tt, shl);
-    const long long ea = block_excl_sum(a, &ta, shl);
+    const long long v2[2] = {t, a};
+    const long long id2[2] = {0, 0};
+    const int kd2[2] = {kScanSum, kScanSum};
+    long long ex2[2], tot2[2];
+    block_scan_multi(v2, id2, kd2, ex2, tot2, shl);
+    const long long et = ex2[0], ea = ex2[1], tt = tot2[0], ta = tot2[1];
     if (v < p.n_videos) {
       put(1, v, ct + et);
       put(2, v, ca + ea);
@@ -467,7 +516,7 @@ __device__ int grid_prefix_tables(const RopeIndexParams& p, int ih, int iw, int 
 }
 
 // Carries of the n chunks whose summaries rec holds (overwritten with
-// provisional records).  emit(c, o) receives chunk c's carry-in;
+// provisional records); `sh` holds 4 * kWaves ints.  emit(c, o) receives chunk c's carry-in;
 // end(b, valid, open_len, open_type, open_grid) the end of sample b (its
 // valid length and the segment open there).  Returns the status bits the
 // summaries report; img_total / vid_total receive the batch's image and video
@@ -489,11 +538,13 @@ __device__ int chunk_carries(const RopeIndexParams& p, int* rec, int n, int* sh,
     if (s[5] >= 0) t_lt = (c << 2) | s[5];
     t_flags |= s[8];
   }
-  int tot;
-  int gF = block_excl_sum(t_nv, &tot, sh);
-  int gA = block_excl_sum(t_nt, &tot, sh);
-  int lt = block_excl_max(t_lt, -1, &tot, sh);
-  const int flags = block_or(t_flags, sh);
+  const int v1[4] = {t_nv, t_nt, t_lt, t_flags};
+  const int id1[4] = {0, 0, -1, 0};
+  const int kd1[4] = {kScanSum, kScanSum, kScanMax, kScanOr};
+  int ex1[4], tot1[4];
+  block_scan_multi(v1, id1, kd1, ex1, tot1, sh);
+  int gF = ex1[0], gA = ex1[1], lt = ex1[2];
+  const int flags = tot1[3];
 
   // Pass 2: segment starts (the first valid token of a chunk starts a
   // segment when the latest valid type before it in its sample differs).
@@ -529,9 +580,14 @@ __device__ int chunk_carries(const RopeIndexParams& p, int* rec, int n, int* sh,
       if (lts >= 0) lt = (c << 2) | lts;
     }
   }
-  int img = block_excl_sum(t_ni, img_total, sh);
-  int vid = block_excl_sum(t_nvd, vid_total, sh);
-  int st = block_excl_max(t_st, -1, &tot, sh);
+  const int v2[3] = {t_ni, t_nvd, t_st};
+  const int id2[3] = {0, 0, -1};
+  const int kd2[3] = {kScanSum, kScanSum, kScanMax};
+  int ex2[3], tot2[3];
+  block_scan_multi(v2, id2, kd2, ex2, tot2, sh);
+  int img = ex2[0], vid = ex2[1], st = ex2[2];
+  *img_total = tot2[0];
+  *vid_total = tot2[1];
 
   // Pass 3a: grid counters per chunk.
   for (int c = c0; c < c1; ++c) {
@@ -575,8 +631,8 @@ __device__ int chunk_carries(const RopeIndexParams& p, int* rec, int n, int* sh,
 }
 
 __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p) {
-  __shared__ int sh[kWaves];
-  __shared__ long long shl[kWaves];
+  __shared__ int sh[4 * kWaves];
+  __shared__ long long shl[2 * kWaves];
   __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
   const int n = p.B * p.C;
   // The first tile of each grid table and the chunk records (when they fit
@@ -639,7 +695,7 @@ __global__ void __launch_bounds__(kPT) rope_index_carry(const RopeIndexParams p)
 // read by the sample's last chunk), and the chunk's token words.
 // extra_flags are status bits found before; every block ORs its bits into
 // the status word and raises rope_delta[b] to its largest position + 1 -
-// valid length.
+// valid length.  `sh` and `shu` hold kWaves entries, `shl` 2 * kWaves.
 __device__ __forceinline__ void apply_chunk(const RopeIndexParams& p, const Tables& tb, int b,
                                             int j, const int (&cin)[kPosCarryInts],
                                             int valid_len, const int* e, const RunWords& words,
@@ -735,9 +791,13 @@ __device__ __forceinline__ void apply_chunk(const RopeIndexParams& p, const Tabl
       if (ge.ok && e[0] != ge.slots) flags |= MROPE_POS_LENGTH;
     }
   }
-  long long bmax;
-  block_excl_max((long long)mx, (long long)INT64_MIN, &bmax, shl);
-  const int f = block_or(flags, sh);
+  const long long v3[2] = {(long long)mx, (long long)flags};
+  const long long id3[2] = {(long long)INT64_MIN, 0};
+  const int kd3[2] = {kScanMax, kScanOr};
+  long long ex3[2], tot3[2];
+  block_scan_multi(v3, id3, kd3, ex3, tot3, shl);
+  const long long bmax = tot3[0];
+  const int f = (int)tot3[1];
   if (threadIdx.x == 0) {
     if (bmax != (long long)INT64_MIN) atomicMax(&p.rope_delta[b], (int)(bmax + 1 - valid_len));
     if (f) atomicOr(p.status, f);
@@ -747,7 +807,7 @@ __device__ __forceinline__ void apply_chunk(const RopeIndexParams& p, const Tabl
 __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p) {
   __shared__ int sh[kWaves];
   __shared__ unsigned long long shu[kWaves];
-  __shared__ long long shl[kWaves];
+  __shared__ long long shl[2 * kWaves];
   // LDS copy of the grid tables when they are small (the common case): the
   // segment starts of a chunk then look grids up without memory round trips.
   __shared__ int32_t t_img[3 * kPosStageGrids];
@@ -821,9 +881,9 @@ __global__ void __launch_bounds__(kPT) rope_index_apply(const RopeIndexParams p)
 // then writes its own chunk's positions.  The summary pass has set the
 // status word to 0 and every rope_delta to INT32_MIN.
 __global__ void __launch_bounds__(kPT) rope_index_fused(const RopeIndexParams p) {
-  __shared__ int sh[kWaves];
+  __shared__ int sh[4 * kWaves];
   __shared__ unsigned long long shu[kWaves];
-  __shared__ long long shl[kWaves];
+  __shared__ long long shl[2 * kWaves];
   __shared__ int rec_lds[kPosCarryLds * kPosSumInts];
   __shared__ int32_t t_img[3 * kPosStageGrids];
   __shared__ int64_t t_adv_i[kPosStageGrids + 1];
