@@ -307,11 +307,12 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t rs, uint32_t off
   }
 }
 
-template <bool BF16, int CB>
+// NT: non-temporal (streaming) store, aux 2.  The default is measured per
+// dtype for qk_kernel and stage_kernel; flat_kernel chooses by output layout.
+template <bool BF16, int CB, bool NT = (BF16 ? MROPE_NT_STORES_BF16 : MROPE_NT_STORES_F32)>
 __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, uint32_t off,
                                           const Words<CB>& r) {
-  // aux 2: non-temporal (streaming) store
-  constexpr int aux = (BF16 ? MROPE_NT_STORES_BF16 : MROPE_NT_STORES_F32) ? 2 : 0;
+  constexpr int aux = NT ? 2 : 0;
   if constexpr (CB == 16) {
     const u32x4_t v = {r.w[0], r.w[1], r.w[2], r.w[3]};
     __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, aux);
@@ -817,7 +818,7 @@ qk_kernel(const QKParams p, const ColTable tab) {
 constexpr int kFlatSteps = 6;
 static_assert(kFlatSteps * kWaveSize == kFlatBatchChunks, "one batch of the flat kernel");
 
-template <bool BF16, int V, int PREC>
+template <bool BF16, int V, int PREC, bool NTS>
 __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int CB = ES * V;
@@ -930,7 +931,7 @@ __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, c
           }
           pack<BF16, V>(a, out);
         }
-        buf_store<BF16, CB>(ry, yoff[u], out);
+        buf_store<BF16, CB, NTS>(ry, yoff[u], out);
       }
     }
   }
@@ -944,8 +945,20 @@ int launch_flat_t(const QKParams& p, const ColTable& tab, hipStream_t st) {
     const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
     if (cap_lds > lds) lds = cap_lds;
   }
-  hipLaunchKernelGGL((flat_kernel<BF16, V, PREC>), dim3((unsigned)blocks), dim3(kBlockThreads),
-                     lds, st, p, tab);
+  // Store policy.  bf16: non-temporal.  fp32: non-temporal when every output
+  // is token-major (a wavefront's stores then cover whole lines: vision_2d
+  // 105.4 -> 98.6 us), cached for per-head planes (a 288-byte row starts
+  // mid-line on every other token, and non-temporal partial lines cost:
+  // 175 -> 208 us).
+  bool token_major = true;
+  for (int s = 0; s < kSlots; ++s)
+    if (p.heads[s] > 0 && p.y_hs[s] != p.D) token_major = false;
+  if (BF16 ? MROPE_NT_STORES_BF16 : token_major)
+    hipLaunchKernelGGL((flat_kernel<BF16, V, PREC, true>), dim3((unsigned)blocks),
+                       dim3(kBlockThreads), lds, st, p, tab);
+  else
+    hipLaunchKernelGGL((flat_kernel<BF16, V, PREC, false>), dim3((unsigned)blocks),
+                       dim3(kBlockThreads), lds, st, p, tab);
   return (int)hipGetLastError();
 }
 
