@@ -72,13 +72,33 @@ def test_random_batches(M, seed, B, L):
     _compare(M, types, images, videos, mask, f"random seed {seed}")
 
 
-@pytest.mark.parametrize("case", ["small", "many_grids", "many_chunks"])
+def _image_run_batch(n_images, L):
+    """One sample: n_images 4x4 images (four merged slots each, advance 2)
+    each after a text token, then text to length L."""
+    types = np.zeros((1, L), dtype=np.int64)
+    for k in range(n_images):
+        types[0, 5 * k + 1:5 * k + 5] = 1
+    return types, [(1, 4, 4)] * n_images
+
+
+@pytest.mark.parametrize("case", ["small", "many_grids", "many_chunks", "grids_at_limit",
+                                  "grids_past_limit", "chunks_at_limit", "chunks_past_limit"])
 def test_pass_forms(M, case):
     """Passes 2 and 3 run as one kernel when the chunk summaries and grids fit
     LDS (up to 1024 chunks, 256 grids of a type), else as two kernels; both
-    forms give the oracle's table."""
+    forms give the oracle's table, on both sides of each limit."""
     rng = np.random.default_rng(900)
-    if case == "small":
+    if case in ("grids_at_limit", "grids_past_limit"):
+        n = 256 if case == "grids_at_limit" else 257
+        types, images = _image_run_batch(n, 3000)
+        mask, videos = None, []
+        want = "rope_index_fused" if n == 256 else "rope_index_carry+apply"
+    elif case in ("chunks_at_limit", "chunks_past_limit"):
+        L = 1024 * 1024 + (0 if case == "chunks_at_limit" else 1)
+        types, images = _image_run_batch(3, L)
+        mask, videos = None, []
+        want = "rope_index_fused" if case == "chunks_at_limit" else "rope_index_carry+apply"
+    elif case == "small":
         types, mask, images, videos = W.random_mm_batch(rng, 2, 600)
         want = "rope_index_fused"
         assert len(images) <= 256 and len(videos) <= 256
