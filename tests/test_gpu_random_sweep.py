@@ -3,7 +3,7 @@ head dims from 2 to 512, partial rotary, every layout with a random valid
 section, token strides wider than the rows (so the chunk width drops below
 16 bytes when the stride is not a multiple of it), with and without the
 norm, all three precisions, in place and out of place, wide position
-ranges.  A second sweep runs 2048+ tokens without the norm (the flat and
+ranges; eight of them at 2048-4096 tokens with the norm.  A second sweep runs 2048+ tokens without the norm (the flat and
 staged kernels), token-major and as the vision tower's per-head planes,
 checked on sampled tokens.
 
@@ -53,8 +53,23 @@ def _random_case(rng):
                     inplace=bool(rng.integers(2)), seed=int(rng.integers(1 << 30)))
 
 
+def _random_large_norm_case(rng):
+    """2048-4096 tokens with the norm: one part per tile, tiles of one or two
+    tokens, and the row-steps preloaded ahead of the cos/sin prologue."""
+    c = _random_case(rng)
+    c["T"] = int(rng.integers(2048, 4097))
+    c["norm"] = True
+    cap = 6_000_000 // (c["T"] * c["D"])
+    if c["hq"] + c["hk"] > cap:
+        c["hk"] = min(c["hk"], max(cap - 1, 0))
+        c["hq"] = max(1, cap - c["hk"])
+    return c
+
+
 _RNG = np.random.default_rng(2024)
 CASES = [_random_case(_RNG) for _ in range(48)]
+_NRNG = np.random.default_rng(4096)
+CASES += [_random_large_norm_case(_NRNG) for _ in range(8)]
 
 
 @pytest.fixture(scope="module")
