@@ -37,12 +37,13 @@
 #ifndef MROPE_ROWS_IN_FLIGHT_F32
 #define MROPE_ROWS_IN_FLIGHT_F32 4
 #endif
-// Non-temporal (streaming) hint on the row stores, by element type.
 // Row-steps in flight for chunks narrower than 16 bytes (e.g. bf16 with a
 // half head of 36: 8-byte chunks).
 #ifndef MROPE_ROWS_IN_FLIGHT_NARROW
 #define MROPE_ROWS_IN_FLIGHT_NARROW 2
 #endif
+// Non-temporal (streaming) hint on the row stores of qk_kernel and
+// stage_kernel, by element type (flat_kernel chooses by output layout).
 #ifndef MROPE_NT_STORES_BF16
 #define MROPE_NT_STORES_BF16 1
 #endif
