@@ -92,10 +92,10 @@ def _oracle_worker(job):
             return done, el
 
 
-def cpu_baseline(inp, wl, budget_s: float = 12.0, precision: str = "exact", procs: int = 1):
+def cpu_baseline(inp, wl, budget_s: float = 8.0, precision: str = "exact", procs: int = 1):
     """The oracle as it stands, on consecutive 64-token windows of the same
     workload: one thread for about budget_s, then (procs > 1) one process per
-    core, each on its own 8 windows, for about 30 s of CPU time in all.  The
+    core, each on its own 8 windows, for about 20 s of CPU time in all.  The
     reported value is the aggregate rate of the processes."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
@@ -123,7 +123,7 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0, precision: str = "exact", proc
                 "sample": sample}
     per = min(8, T // chunk) * chunk
     stride = max(per, (T - per) // procs)
-    wall = max(2.0, 30.0 / procs)
+    wall = max(1.0, 20.0 / procs)
     t_start = time.time() + 4.0
     jobs = []
     for i in range(procs):
