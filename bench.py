@@ -240,7 +240,8 @@ def build_cache(M, dim: int, theta: float, rows: int):
 
 
 def bench_positions(args):
-    """One step = one mrope_rope_index call (three kernels) over the batch."""
+    """One step = one mrope_rope_index call (two kernels at this size, three past the
+    fused pass's limits) over the batch."""
     import numpy as np
     import torch
     import workloads as W
