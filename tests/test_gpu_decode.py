@@ -143,3 +143,58 @@ def test_decode_and_prefill_replay_in_a_hip_graph(M):
         assert torch.equal(cache_g.view(torch.int16), cache_eager.view(torch.int16)), rep
         assert torch.equal(pq_g.view(torch.int16), pq_eager.view(torch.int16)), rep
         assert torch.equal(pk_g.view(torch.int16), pk_eager.view(torch.int16)), rep
+
+
+def test_position_builder_and_vision_fusion_replay_in_a_hip_graph(M):
+    """The position builder (both forms of passes 2 and 3) and the vision
+    fusion (staged bf16 planes, flat fp32 planes and fp32 token-major rows)
+    captured in one graph: every replay, with the outputs cleared and eager
+    work between replays, equals the eager result."""
+    import torch
+    rng = np.random.default_rng(31)
+    batches = [W.random_mm_batch(rng, 2, 600), W.random_mm_batch(rng, 4, 4000)]
+    assert len(batches[1][2]) > 256            # the second one takes the two-kernel form
+    dev_batches = []
+    for types, mask, images, videos in batches:
+        g = lambda x: None if not x else to_dev(np.asarray(x, dtype=np.int32).reshape(-1, 3), "i32")
+        dev_batches.append((to_dev(types.astype(np.int32), "i32"), g(images), g(videos),
+                            to_dev(mask.astype(np.int32), "i32")))
+    eager_pos = [M.rope_index(t, i, v, m)[:2] for t, i, v, m in dev_batches]
+    vis = []
+    for name, head_major in (("vision_qkv_planes_bf16", True), ("vision_qkv_planes", True),
+                             ("vision_qkv_planes", False)):
+        wl = W.VISION_QKV_WORKLOADS[name]
+        inp = W.make_vision_qkv_inputs(wl, n=4096)
+        qkv = to_dev(inp["qkv"].reshape(4096, -1), wl.dtype).reshape(4096, 3, wl.heads, wl.D)
+        pos = to_dev(inp["pos"], "i32")
+        outs = M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta, head_major=head_major)
+        vis.append((qkv, pos, wl, head_major, [o.clone() for o in outs]))
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):            # warm the allocator outside the capture
+        for t, i, v, m in dev_batches:
+            M.rope_index(t, i, v, m, check=False)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        g_pos = [M.rope_index(t, i, v, m, check=False)[:2] for t, i, v, m in dev_batches]
+        g_vis = [M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta, head_major=hm)
+                 for qkv, pos, wl, hm, _ in vis]
+    for rep in range(3):
+        for pair in g_pos:
+            for x in pair:
+                x.zero_()
+        for outs in g_vis:
+            for x in outs:
+                x.zero_()
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for (gp, gd), (ep, ed) in zip(g_pos, eager_pos):
+            assert torch.equal(gp, ep) and torch.equal(gd, ed), rep
+        for outs, (_, _, _, _, want) in zip(g_vis, vis):
+            for a, b in zip(outs, want):
+                assert torch.equal(a.view(torch.int8), b.view(torch.int8)), rep
