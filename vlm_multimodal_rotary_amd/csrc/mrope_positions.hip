@@ -5,11 +5,11 @@
 // Rotary Position Embedding", get_rope_index walkthrough).  Every position is
 // a prefix quantity of the token sequence, so the builder is three scans:
 //
-//   1. summarize: one block per 4096-token chunk of a sample reduces the
+//   1. summarize: one block per 1024-token chunk of a sample reduces the
 //      chunk (valid and text token counts, first/last valid type, segment
 //      starts by type, the last start) -- tokens are read once.
-//   2. carry:     one block walks the chunk summaries in order (in LDS tiles)
-//      and writes each chunk's carry-in: filtered index, text count, the
+//   2. carry:     one block scans the chunk summaries (held in LDS when they
+//      fit) and writes each chunk's carry-in: filtered index, text count, the
 //      previous valid type, the global image / video grid counters, the open
 //      segment; it also builds the grid-advance prefix tables and the
 //      per-sample valid length.
