@@ -15,7 +15,12 @@
 //    lane with no redundancy, into its own LDS slice; every q and k head of a
 //    token then reuses them (the pages compute cos/sin once per forward and
 //    share them over heads).  Rows of the tile are walked with 64/lpr rows per
-//    instruction and U rows in flight per lane.
+//    instruction and U rows in flight per lane.  With RMSNorm (and in decode)
+//    the first row-steps are loaded before the sincos and finished after it,
+//    so that the sincos overlaps their memory latency.
+//  * flat_kernel (rows that are not whole 256-byte line pairs) and
+//    stage_kernel (bf16 per-head planes, through LDS) serve the positions
+//    path without RMSNorm; the host picks the kernel by shape.
 //  * The RMS reduction of a row runs over its lpr lanes with DPP
 //    (quad_perm, row_half_mirror, row_mirror) on float64 partial sums.
 //  * Numerics follow the pages' conventions with the rounding points made
@@ -485,10 +490,12 @@ __device__ __forceinline__ void process_steps(SlotState<(BF16 ? 2 : 4) * V>& st,
                                                 t0);
 }
 
-// Wavefront w owns the tile of tokens [w*nt, w*nt + nt): first the tile's
-// cos/sin (in its LDS slice), then the tile's q rows and k rows, U row-steps
-// per batch of loads.  Wavefronts are short-lived and many; the hardware
-// overlaps them, and the chip's active window of rows stays contiguous.
+// Wavefront w owns part w % parts of the tile of tokens [t0, t0 + nt),
+// t0 = (w / parts) * nt (parts = 1 on large launches): first the tile's
+// cos/sin (in its LDS slice), then its part of the tile's row-steps -- q, k
+// and a packed qkv's copied v, in that order -- U per batch of loads.
+// Wavefronts are short-lived and many; the hardware overlaps them, and the
+// chip's active window of rows stays contiguous.
 template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 __global__ void __launch_bounds__(kBlockThreads)
 qk_kernel(const QKParams p, const ColTable tab) {
