@@ -503,13 +503,16 @@ qk_kernel(const QKParams p, const ColTable tab) {
   constexpr int CB = ES * V;
   constexpr int U = CB < 16 ? MROPE_ROWS_IN_FLIGHT_NARROW
                             : (BF16 ? MROPE_ROWS_IN_FLIGHT_BF16 : MROPE_ROWS_IN_FLIGHT_F32);
-  typedef double cs_t;
+  // cos/sin are binary32 values: LDS holds them as float (half the bytes of
+  // double; measured 0.9% faster on the headline, 1.4% on chunked video) and
+  // the rotation widens them exactly.
+  typedef float cs_t;
   extern __shared__ double lds[];
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int half = p.half;
-  cs_t* lc = lds + wib * (2 * p.nt * half);
+  cs_t* lc = reinterpret_cast<cs_t*>(lds) + wib * (2 * p.nt * half);
   cs_t* ls = lc + p.nt * half;
 
   const int lpr = LPR > 0 ? LPR : p.lpr;
@@ -852,8 +855,8 @@ __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, c
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   const int half = p.half;
-  double* lc = lds + wib * 2 * half;
-  double* ls = lc + half;
+  float* lc = reinterpret_cast<float*>(lds) + wib * 2 * half;   // binary32 cos/sin
+  float* ls = lc + half;
   const int64_t t0 = (int64_t)blockIdx.x * kWavesPerBlock + wib;
   if (t0 >= p.T) return;
 
@@ -929,13 +932,14 @@ __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, c
           float a[V], b[V];
           unpack<BF16, V>(own[u], a);
           unpack<BF16, V>(par[u], b);
-          const double* cc = lc + col[u];
-          const double* sc = ls + col[u];
+          const float* cc = lc + col[u];
+          const float* sc = ls + col[u];
           if constexpr (PREC == MROPE_PRECISION_EXACT) {
             const double sg = kind[u] == 0 ? -1.0 : 1.0;
 #pragma unroll
             for (int i = 0; i < V; ++i)
-              a[i] = (float)__builtin_fma((double)a[i], cc[i], sg * ((double)b[i] * sc[i]));
+              a[i] = (float)__builtin_fma((double)a[i], (double)cc[i],
+                                          sg * ((double)b[i] * (double)sc[i]));
           } else {
 #pragma clang fp contract(off)
             constexpr bool CAST = BF16 && PREC == MROPE_PRECISION_DTYPE;
@@ -966,7 +970,7 @@ __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, c
 template <bool BF16, int V, int PREC>
 int launch_flat_t(const QKParams& p, const ColTable& tab, hipStream_t st) {
   const int64_t blocks = (p.T + kWavesPerBlock - 1) / kWavesPerBlock;
-  int lds = kWavesPerBlock * 2 * p.half * (int)sizeof(double);
+  int lds = kWavesPerBlock * 2 * p.half * (int)sizeof(float);
   if (p.waves_cap > 0) {
     const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
     if (cap_lds > lds) lds = cap_lds;
@@ -1405,7 +1409,7 @@ int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   p.parts = (int)parts;
   const int64_t waves = tiles * parts;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(double) : 0;
+  int lds = cs_lds ? kWavesPerBlock * 2 * p.nt * p.half * (int)sizeof(float) : 0;
   if (p.waves_cap > 0) {
     // Bound the resident wavefronts per SIMD: a block asks for enough LDS
     // that at most waves_cap blocks of four wavefronts share a compute unit.
