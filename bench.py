@@ -6,28 +6,44 @@ positions, per-head RMSNorm, rotation of every q and k head), inputs resident
 in HBM.  Default workload: Omni-like text prefill, q[32768,32,128] and
 k[32768,4,128] bf16, interleaved [24,20,20], theta 1e6, RMSNorm eps 1e-6.
 
+Measures (HIP events on the stream the kernels are launched on):
+
+* rotating (the reported value): step i works on buffer set i mod S (S = 3
+  by default: 3 x 604 MB for the headline), launched back to back, so no
+  step reads a line that the previous step left in the 256 MB memory-side
+  cache (MALL); the steady state of a stream of layers whose q/k come from
+  HBM.
+* same_buffers: every step on one set, back to back (what the previous
+  measure of this benchmark reported); workloads whose bytes fit the MALL
+  are partly served from it here.
+* copy_ceiling: mrope_stream_copy of the workload's bytes (the q/k bytes read
+  are copied into as many bytes written), rotating over S sets the same way:
+  the rate a plain copy of this size reaches under the same measure.
+
+Order on the GPU: the copy ceiling (W warmup + K timed steps), then the
+kernel rotating (W + K), then the kernel on one buffer set (W + K); the
+profile summaries pick their dispatches by this order (--trace-summary).
+
 Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
 kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
-bounded sample of the same workload (cpu_baseline: one thread, then one
-process per core).
-
-Warmup is at least W steps and at least --min-warmup-s seconds: the first
-tens of milliseconds of sustained HBM traffic run at a different clock state,
-and the timed K steps are meant to see the steady state.  Each step is one
-kernel launch on torch's current stream, timed with HIP events on that stream.
+bounded sample of the same workload (cpu_baseline).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--graph G] [--cold] [--cs-cache] [--precision exact|dtype|fp32]
-                  [--cpu-procs P]
+                  [--rotate S] [--graph G] [--cold] [--cs-cache]
+                  [--precision exact|dtype|fp32] [--cpu-procs P]
   python bench.py --copy-calib BYTES   # plain device copy, for counter scaling
+  python bench.py --trace-summary DIR --workload NAME --steps K --warmup W
+                  # per-phase kernel durations from a rocprofv3 kernel trace
 
-Other workloads time the other entry points the same way: the decode step
-(omni_decode), the vision packed-qkv fusion (vision_qkv_planes[_bf16]) and
-the position builder (mm_prompt_positions).
+Other workloads time the other entry points: the decode step (omni_decode),
+the vision packed-qkv fusion (vision_qkv_planes[_bf16]) and the position
+builder (mm_prompt_positions).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -42,6 +58,10 @@ DEFAULT_WORKLOAD = "omni_text_prefill"
 KERNEL_SOURCES = ["vlm_multimodal_rotary_amd/csrc/mrope_kernels.hip",
                   "vlm_multimodal_rotary_amd/csrc/mrope_api.cpp",
                   "vlm_multimodal_rotary_amd/csrc/mrope_internal.h"]
+# The machine's CPU share for one GPU: oracle worker pools stay within it
+# whatever the affinity mask shows.
+HOST_CORE_SHARE = 16
+ORACLE_CHUNK = 1024           # tokens per oracle call (bounds its memory)
 
 
 def kernel_source_hash() -> str:
@@ -53,163 +73,189 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """(bytes per launch, source note) from the committed rocprofv3 counter
+    summary, or (None, reason) when there is none or the kernel sources
+    changed since it was taken.  The counters (FETCH_SIZE + WRITE_SIZE) count
+    bytes between L2 and the memory fabric; lines served by the MALL are
+    included."""
+    rel = os.path.join("profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
-        return None
+        return None, f"no {rel}"
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    h = kernel_source_hash()
+    if rec.get("kernel_source_hash") != h:
+        return None, f"{rel} was taken on other kernel sources"
+    return rec.get("hbm_bytes_per_launch"), (
+        f"L2<->fabric bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy) from "
+        f"{rel}, kernel source hash {h}; not measured in this run")
 
 
-def _oracle_fused_windows(q, k, pos, wl, wq, wk, precision, chunk):
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def _oracle_chunks(q, k, pos, wl, wq, wk, precision, chunk):
+    """Runs the oracle over consecutive chunks of the given tokens; returns
+    the token count."""
     from oracle import mrope_oracle as O
-    for i in range(q.shape[0] // chunk):
-        sl = slice(i * chunk, (i + 1) * chunk)
+    n = q.shape[0]
+    for a in range(0, n, chunk):
+        sl = slice(a, min(n, a + chunk))
         O.rmsnorm_mrope_qk(q[sl], k[sl], pos[:, sl], rotary_dim=wl.rotary_dim, theta=wl.theta,
                            section=wl.section, layout=wl.layout, wq=wq, wk=wk, eps=wl.eps,
                            dtype=wl.dtype, precision=precision)
+    return n
 
 
 def _oracle_worker(job):
     """One process of the multi-process oracle sample: from a common start
-    time, repeats the oracle over its own token windows until the deadline.
-    Returns (tokens done, seconds)."""
+    time, walks its share of the workload chunk after chunk (starting over
+    if time remains) until the deadline.  Returns (tokens done, seconds)."""
     q, k, pos, wl, wq, wk, precision, chunk, t_start, budget_s = job
     now = time.time()
     if now < t_start:
         time.sleep(t_start - now)
     start = time.perf_counter()
-    done = 0
+    done, a, n = 0, 0, q.shape[0]
     while True:
-        _oracle_fused_windows(q, k, pos, wl, wq, wk, precision, chunk)
-        done += q.shape[0]
+        sl = slice(a, min(n, a + chunk))
+        done += _oracle_chunks(q[sl], k[sl], pos[:, sl], wl, wq, wk, precision, chunk)
+        a = a + chunk if a + chunk < n else 0
         el = time.perf_counter() - start
         if el >= budget_s:
             return done, el
 
 
-def cpu_baseline(inp, wl, budget_s: float = 8.0, precision: str = "exact", procs: int = 1):
-    """The oracle as it stands, on consecutive 64-token windows of the same
-    workload: one thread for about budget_s, then (procs > 1) one process per
-    core, each on its own 8 windows, for about 20 s of CPU time in all.  The
-    reported value is the aggregate rate of the processes."""
+def host_cores():
+    """(cores the pool uses, cores this process may run on)."""
+    visible = len(os.sched_getaffinity(0))
+    return min(visible, HOST_CORE_SHARE), visible
+
+
+def cpu_baseline(inp, wl, budget_s: float = 6.0, precision: str = "exact", procs: int = 1):
+    """The oracle as it stands on the same workload, 1024-token chunks
+    streaming through it: one thread from the first token for about budget_s,
+    then (procs > 1) one process per core, process i on the i-th contiguous
+    share of the tokens, for about 20 s of CPU time in all.  The reported
+    value is the aggregate rate of the processes."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
     T = wl.T
-    chunk = min(64, T)
+    chunk = min(ORACLE_CHUNK, T)
     wq = inp["wq"] if wl.norm else None
     wk = inp["wk"] if wl.norm else None
-    done = 0
+    done, a = 0, 0
     start = time.perf_counter()
-    t0 = 0
     while True:
-        sl = slice(t0, t0 + chunk)
-        _oracle_fused_windows(inp["q"][sl], inp["k"][sl], inp["pos"][:, sl], wl, wq, wk,
-                              precision, chunk)
-        done += chunk
-        t0 = (t0 + chunk) % (T - chunk + 1)
+        sl = slice(a, min(T, a + chunk))
+        done += _oracle_chunks(inp["q"][sl], inp["k"][sl], inp["pos"][:, sl], wl, wq, wk,
+                               precision, chunk)
+        a = a + chunk if a + chunk < T else 0
         elapsed = time.perf_counter() - start
         if elapsed >= budget_s:
             break
     one = done / elapsed
-    sample = (f"{done} tokens ({done // chunk} windows of {chunk} consecutive tokens, all "
-              f"{wl.hq}+{wl.hk} heads) of {wl.name}, {elapsed:.1f} s, one thread")
+    sample = (f"{done} tokens of {wl.name} in {chunk}-token chunks from token 0 on (all "
+              f"{wl.hq}+{wl.hk} heads), {elapsed:.1f} s, one thread")
+    used, visible = host_cores()
     if procs <= 1:
-        return {"value": one, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": sample}
-    per = min(8, T // chunk) * chunk
-    stride = max(per, (T - per) // procs)
+        return {"value": one, "unit": "tokens/s", "cores": 1, "cores_visible": visible,
+                "kind": "oracle", "sample": sample}
+    share = max(chunk, -(-T // procs))
     wall = max(1.0, 20.0 / procs)
     t_start = time.time() + 4.0
     jobs = []
     for i in range(procs):
-        a = min(i * stride, T - per)
-        jobs.append((inp["q"][a:a + per], inp["k"][a:a + per], inp["pos"][:, a:a + per], wl,
-                     wq, wk, precision, chunk, t_start, wall))
+        a = min(i * share, max(0, T - share))
+        sl = slice(a, a + share)
+        jobs.append((inp["q"][sl], inp["k"][sl], inp["pos"][:, sl], wl, wq, wk, precision, chunk,
+                     t_start, wall))
     try:
         with ProcessPoolExecutor(procs, mp_context=mp.get_context("spawn")) as ex:
             futs = [ex.submit(_oracle_worker, j) for j in jobs]
-            res = [f.result(timeout=wall + 120.0) for f in futs]
+            res = [f.result(timeout=wall + 180.0) for f in futs]
     except Exception as e:  # a worker died or never started: report the one thread
-        return {"value": one, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": one, "unit": "tokens/s", "cores": 1, "cores_visible": visible,
+                "kind": "oracle",
                 "sample": f"{sample} (the {procs}-process sample failed: {type(e).__name__})"}
     agg = sum(d / e for d, e in res)
     toks = sum(d for d, _ in res)
-    return {"value": agg, "unit": "tokens/s", "cores": procs, "kind": "oracle",
-            "one_thread": one,
-            "sample": f"{procs} processes from one start time, each repeating {per // chunk} windows of "
-                      f"{chunk} tokens for {wall:.1f} s ({toks} tokens in all; value = sum of "
-                      f"their rates); before them {sample}"}
+    return {"value": agg, "unit": "tokens/s", "cores": procs, "cores_visible": visible,
+            "kind": "oracle", "one_thread": one,
+            "sample": f"{procs} processes from one start time, process i on the i-th share of "
+                      f"{share} consecutive tokens, {chunk}-token chunks, for {wall:.2f} s each "
+                      f"({toks} tokens in all; value = sum of their rates); {visible} cores "
+                      f"visible, the pool kept to the box's share of {HOST_CORE_SHARE} per GPU; "
+                      f"before them {sample}"}
 
 
-def time_steps(step, args, stream=None):
-    """Warm up (at least W steps and --min-warmup-s), optionally capture
-    --graph steps in one HIP graph, then time K steps with HIP events on the
-    launching stream.  Returns (ms per step, steps timed, warmup steps, wall
-    ms per step)."""
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def time_region(fns, warmup: int, steps: int):
+    """W untimed steps, then exactly K timed ones; step i calls fns[i % len].
+    HIP events on torch's current stream (the stream every call here
+    launches on) bracket the K steps.  Returns (ms per step, wall ms per
+    step)."""
     import torch
-    t_warm = time.perf_counter()
-    done = 0
-    while done < args.warmup or time.perf_counter() - t_warm < args.min_warmup_s:
-        for _ in range(50):
-            step()
-        done += 50
-        torch.cuda.synchronize()
-    runner = step
-    per_run = 1
-    if args.graph > 0:
-        # Capture G steps once; each replay launches them back to back without
-        # host overhead.  The captured launches are plain kernel launches.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.graph):
-                step()
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-        runner = graph.replay
-        per_run = args.graph
-    runs = max(1, args.steps // per_run)
+    S = len(fns)
+    for i in range(warmup):
+        fns[i % S]()
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(runs):
-        runner()
+    for i in range(steps):
+        fns[i % S]()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    n = runs * per_run
-    return ev0.elapsed_time(ev1) / n, n, done, wall * 1e3 / n
+    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
 
 
-def time_steps_cold(step, args):
-    """Each timed step starts with no line of its inputs in L2 or the 256 MB
-    MALL: a 1 GiB scratch read (outside the timed interval; a read, so that
-    no dirty line of the flush is written back inside the step) precedes
-    it, and the step alone is bracketed by HIP events.  Returns the mean
-    step time.  The step's own writes may then stay in the MALL past the
-    end of the step, which back-to-back timing does not allow."""
+def time_graph(step, graph_steps: int, warmup: int, steps: int):
+    """Capture graph_steps steps in one HIP graph and time replays of it
+    (launch-bound workloads).  W untimed steps first; then ceil(K / G)
+    replays.  Returns (ms per step, steps timed, wall ms per step)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(graph_steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    runs = max(1, -(-steps // graph_steps))
+    ms, wall = time_region([graph.replay], 0, runs)
+    return ms / graph_steps, runs * graph_steps, wall / graph_steps
+
+
+def time_steps_cold(step, warmup: int, steps: int):
+    """Each timed step starts with no line of its inputs in L2 or the MALL:
+    a 1 GiB scratch buffer is read (outside the timed interval; a read, so
+    that no dirty line of the flush is written back inside the step) before
+    it, and the step alone is bracketed by HIP events.  Returns the mean step
+    time.  Per-step timing includes the launch's ramp-up and drain, which
+    back-to-back timing overlaps."""
     import torch
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    for _ in range(max(3, args.warmup // 50)):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    n = max(1, min(args.steps, 500))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
+           for _ in range(steps)]
     wall0 = time.perf_counter()
     for e0, e1 in evs:
         torch.sum(scratch, dim=0, out=sink)
@@ -218,9 +264,94 @@ def time_steps_cold(step, args):
         e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total = sum(e0.elapsed_time(e1) for e0, e1 in evs)
-    return total / n, n, 0, wall * 1e3 / n
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps, wall * 1e3 / steps
 
+
+def copy_ceiling(M, nbytes: int, sets: int, warmup: int, steps: int):
+    """mrope_stream_copy of nbytes (read) into nbytes (written), rotating over
+    `sets` source/destination pairs, back to back: the same measure as the
+    kernel's rotating figure.  Returns the record for the JSON line."""
+    import torch
+    nbytes = (nbytes + 15) // 16 * 16
+    pairs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
+              torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+    fns = [lambda s=s, d=d: M.stream_copy(s, d) for s, d in pairs]
+    ms, _ = time_region(fns, warmup, steps)
+    del pairs
+    torch.cuda.empty_cache()
+    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "stream_copy_kernel (mrope_stream_copy)", "bytes_read": nbytes,
+            "bytes_written": nbytes, "sets": sets, "ms_per_copy": ms, "gbps": gbps,
+            "frac_of_peak": gbps / HBM_PEAK_GBPS}
+
+
+def measures(M, fns_sets, copy_bytes, args):
+    """Copy ceiling, rotating and same-buffer figures of a step, in the order
+    the trace summary expects.  fns_sets[i] runs the step on buffer set i."""
+    out = {}
+    out["copy"] = copy_ceiling(M, copy_bytes, len(fns_sets), args.warmup, args.steps)
+    out["rotating"] = time_region(fns_sets, args.warmup, args.steps)
+    out["same"] = time_region(fns_sets[:1], args.warmup, args.steps)
+    return out
+
+
+def dispatch_plan(warmup: int, steps: int):
+    """(kernel family, phase, dispatch count) in launch order, as measures()
+    issues them."""
+    return [("copy", "warmup", warmup), ("copy", "timed_rotating", steps),
+            ("kernel", "warmup_rotating", warmup), ("kernel", "timed_rotating", steps),
+            ("kernel", "warmup_same_buffers", warmup), ("kernel", "timed_same_buffers", steps)]
+
+
+def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
+    """Per-phase durations of the kernels in a rocprofv3 kernel trace of a
+    bench.py run (--no-cpu-baseline, same --steps/--warmup): dispatches of the
+    copy kernel and of the rotary kernel, split by dispatch_plan()."""
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
+    rows = []
+    for p in paths:
+        with open(p) as f:
+            rows.extend(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def family(name):
+        if "stream_copy_kernel" in name:
+            return "copy"
+        for k in ("qk_kernel", "qk_pipe_kernel", "flat_kernel", "stage_kernel"):
+            if k in name:
+                return "kernel"
+        return None
+
+    seq = {"copy": [], "kernel": []}
+    names = {}
+    for r in rows:
+        fam = family(r["Kernel_Name"])
+        if fam is None:
+            continue
+        seq[fam].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        names.setdefault(fam, r["Kernel_Name"])
+    out = {"trace_files": [os.path.relpath(p, trace_dir) for p in paths], "phases": []}
+    pos = {"copy": 0, "kernel": 0}
+    for fam, phase, n in dispatch_plan(warmup, steps):
+        d = seq[fam][pos[fam]:pos[fam] + n]
+        pos[fam] += n
+        if not d:
+            continue
+        ds = sorted(d)
+        out["phases"].append({"kernel": names.get(fam, fam), "phase": phase, "dispatches": len(d),
+                              "mean_us": sum(d) / len(d), "median_us": ds[len(ds) // 2],
+                              "min_us": ds[0], "max_us": ds[-1]})
+    for fam in seq:
+        if pos[fam] != len(seq[fam]):
+            out.setdefault("unmatched", {})[fam] = len(seq[fam]) - pos[fam]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
 
 def build_cache(M, dim: int, theta: float, rows: int):
     """The cos/sin cache by position, built once; its build time (HIP events,
@@ -240,14 +371,11 @@ def build_cache(M, dim: int, theta: float, rows: int):
 
 
 def bench_positions(args):
-    """One step = one mrope_rope_index call (two kernels at this size, three past the
-    fused pass's limits) over the batch."""
-    import numpy as np
+    """One step = one mrope_rope_index call (two kernels at this size, three
+    past the fused pass's limits) over the batch; one buffer set (1.3 MB)."""
     import torch
     import workloads as W
     import vlm_multimodal_rotary_amd as M
-    from vlm_multimodal_rotary_amd import _lib
-    import ctypes
 
     wl = W.POSITION_WORKLOADS[args.workload]
     types, mask, images, videos = W.mm_prompt_batch(wl)
@@ -260,32 +388,29 @@ def bench_positions(args):
     pos = torch.empty((3, B * L), dtype=torch.int32, device="cuda")
     delta = torch.empty(B, dtype=torch.int32, device="cuda")
     status = torch.empty(1, dtype=torch.int32, device="cuda")
-    P = ctypes.c_void_p
 
     def step():
-        _lib.check(lib.mrope_rope_index(
-            P(td.data_ptr()), P(md.data_ptr()), B, L, P(gi.data_ptr()), gi.shape[0],
-            P(gv.data_ptr()), gv.shape[0], 2, P(pos.data_ptr()), B * L, P(delta.data_ptr()),
-            P(status.data_ptr()), P(ws.data_ptr()), ws_bytes,
-            P(torch.cuda.current_stream().cuda_stream)))
+        M.rope_index_into(td, md, gi, gv, 2, pos, delta, status, ws)
 
-    ms, n, warm, wall_ms = time_steps(step, args)
+    if args.graph > 0:
+        ms, n, wall_ms = time_graph(step, args.graph, args.warmup, args.steps)
+    else:
+        (ms, wall_ms), n = time_region([step], args.warmup, args.steps), args.steps
     assert int(status.item()) == 0
     alg = wl.algorithmic_bytes()
     gbps = alg / (ms * 1e-3) / 1e9
     line = {
         "metric": "position-table tokens/s (mrope_rope_index)",
         "value": wl.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
-        "warmup": warm, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
-        "graph_steps": args.graph, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int32",
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "graph_steps": args.graph, "measure": "same_buffers", "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32",
         "data": "synthetic (seeded chat-style multimodal prompts)",
         "config": {"workload": wl.name, "batch": B, "seq_len": L, "images": int(gi.shape[0]),
                    "videos": int(gv.shape[0]), "merge": 2},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes": alg,
-                     "kernel": "rope_index_summarize + rope_index_carry + rope_index_apply "
-                               "(one step)"},
+                     "kernel": f"{M.last_kernel()} (mrope_rope_index, one step)"},
     }
     if not args.no_cpu_baseline:
         from oracle import positions_oracle as PO
@@ -302,9 +427,27 @@ def bench_positions(args):
     print(json.dumps(line), flush=True)
 
 
+def line_measures(meas, alg_bytes, units):
+    """The rotating / same-buffer / copy records of the JSON line."""
+    (ms_r, wall_r), (ms_s, wall_s) = meas["rotating"], meas["same"]
+    cp = meas["copy"]
+    rec = {
+        "rotating": {"ms_per_step": ms_r, "wall_ms_per_step": wall_r,
+                     "gbps": alg_bytes / (ms_r * 1e-3) / 1e9,
+                     "frac": alg_bytes / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "units_per_s": units / (ms_r * 1e-3)},
+        "same_buffers": {"ms_per_step": ms_s, "wall_ms_per_step": wall_s,
+                         "gbps": alg_bytes / (ms_s * 1e-3) / 1e9,
+                         "frac": alg_bytes / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "units_per_s": units / (ms_s * 1e-3)},
+        "copy_ceiling": dict(cp, kernel_frac_of_copy=cp["ms_per_copy"] / ms_r),
+    }
+    return rec
+
+
 def bench_vision_qkv(args):
     """One step = one mrope_vision_qkv call: packed qkv in, rotated q/k and
-    copied v in per-head planes out."""
+    copied v in per-head planes out; rotating over buffer sets."""
     import numpy as np
     import torch
     import workloads as W
@@ -315,57 +458,71 @@ def bench_vision_qkv(args):
     n = wl.T
     flat = inp["qkv"].reshape(n, -1)
     if wl.dtype == "bf16":
-        qkv = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda()
+        qkv0 = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda()
     else:
-        qkv = torch.from_numpy(flat).cuda()
-    qkv = qkv.reshape(n, 3, wl.heads, wl.D)
+        qkv0 = torch.from_numpy(flat).cuda()
+    qkv0 = qkv0.reshape(n, 3, wl.heads, wl.D)
     pos = torch.from_numpy(inp["pos"]).cuda()
     shape = (wl.heads, n, wl.D)
-    qo, ko, vo = (torch.empty(shape, dtype=qkv.dtype, device="cuda") for _ in range(3))
     cache, cache_info = None, None
     if args.cs_cache:
         cache, cache_info = build_cache(M, wl.rotary_dim // 2, wl.theta,
                                         int(inp["pos"].max()) + 1)
+    sets = []
+    for i in range(args.rotate):
+        qkv = qkv0 if i == 0 else qkv0.clone()
+        outs = tuple(torch.empty(shape, dtype=qkv0.dtype, device="cuda") for _ in range(3))
+        sets.append((qkv, outs))
 
-    def step():
-        M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta, q_out=qo, k_out=ko, v_out=vo,
-                     precision=args.precision, cs_cache=cache)
+    def make_step(qkv, outs):
+        def step():
+            M.vision_qkv(qkv, pos, wl.rotary_dim, wl.theta, q_out=outs[0], k_out=outs[1],
+                         v_out=outs[2], precision=args.precision, cs_cache=cache)
+        return step
 
-    ms, n_timed, warm, wall_ms = time_steps(step, args)
+    fns = [make_step(*s) for s in sets]
+    meas = measures(M, fns, qkv0.numel() * qkv0.element_size(), args)
+    kernel = M.last_kernel()
     alg = wl.algorithmic_bytes()
-    gbps = alg / (ms * 1e-3) / 1e9
+    rec = line_measures(meas, alg, n)
+    ms = rec["rotating"]["ms_per_step"]
+    gbps = rec["rotating"]["gbps"]
+    traffic, traffic_note = ((None, "not taken for this precision or the cache")
+                             if args.precision != "exact" or args.cs_cache
+                             else measured_traffic(wl.name))
     line = {
         "metric": "vision patches/s, packed qkv to rotated head-major planes (mrope_vision_qkv)",
-        "value": n / (ms * 1e-3), "unit": "patches/s", "n_gpus": 1, "steps": n_timed,
-        "warmup": warm, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
-        "graph_steps": args.graph, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype,
+        "value": n / (ms * 1e-3), "unit": "patches/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms,
+        "wall_ms_per_step": rec["rotating"]["wall_ms_per_step"],
+        "measure": f"rotating over {args.rotate} buffer sets", "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded normal qkv, merge-block patch positions)",
         "config": {"workload": wl.name, "patches": n, "heads": wl.heads, "D": wl.D,
                    "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": "vision_2d",
                    "output": "head-major planes", "precision": args.precision,
                    "cs_cache": cache_info},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name)
-                     if args.precision == "exact" and not args.cs_cache else None,
-                     "algorithmic_bytes": alg,
-                     "kernel": f"{M.last_kernel()} (mrope_vision_qkv)"},
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                     "traffic_note": traffic_note, "algorithmic_bytes": alg,
+                     "kernel": f"{kernel} (mrope_vision_qkv)"},
+        **rec,
     }
     if not args.no_cpu_baseline:
         from oracle import mrope_oracle as O
-        chunk, done, t0 = 64, 0, 0
+        chunk, done, t0 = ORACLE_CHUNK, 0, 0
         start = time.perf_counter()
         while time.perf_counter() - start < 12.0:
-            sl = slice(t0, t0 + chunk)
+            sl = slice(t0, min(n, t0 + chunk))
             O.vision_qkv(inp["qkv"][sl], inp["pos"][:, sl], rotary_dim=wl.rotary_dim,
                          theta=wl.theta, dtype=wl.dtype, precision=args.precision)
-            done += chunk
-            t0 = (t0 + chunk) % (n - chunk + 1)
+            done += sl.stop - sl.start
+            t0 = sl.stop if sl.stop < n else 0
         el = time.perf_counter() - start
         line["cpu_baseline"] = {"value": done / el, "unit": "patches/s", "cores": 1,
                                 "kind": "oracle",
-                                "sample": f"{done} patches ({done // chunk} windows of {chunk}), "
-                                          f"{el:.1f} s, one thread"}
+                                "sample": f"{done} patches in {chunk}-patch chunks from patch 0 "
+                                          f"on, {el:.1f} s, one thread"}
     print(json.dumps(line), flush=True)
 
 
@@ -396,6 +553,48 @@ def cpu_baseline_decode(inp, wl, budget_s: float = 10.0, precision: str = "exact
                       f"rows) of {wl.name}, {elapsed:.1f} s, one thread"}
 
 
+def bench_decode(args, wl, inp, dev):
+    """One step = one mrope_decode_qk call (one buffer set: the step moves
+    9.4 MB, latency-bound)."""
+    import torch
+    import vlm_multimodal_rotary_amd as M
+    q, k = dev(inp["q"]), dev(inp["k"])
+    wq, wk = dev(inp["wq"]), dev(inp["wk"])
+    q_out = torch.empty_like(q)
+    cache_len, rope_delta, k_cache = (dev(inp["cache_len"]), dev(inp["rope_delta"]),
+                                      dev(inp["k_cache"]))
+
+    def step():
+        M.mrope_decode_qk(q, k, cache_len, rope_delta, wl.new_tokens, wl.rotary_dim,
+                          wl.theta, k_cache, wq=wq, wk=wk, eps=wl.eps, q_out=q_out,
+                          precision=args.precision)
+
+    if args.graph > 0:
+        ms, n, wall_ms = time_graph(step, args.graph, args.warmup, args.steps)
+    else:
+        (ms, wall_ms), n = time_region([step], args.warmup, args.steps), args.steps
+    alg = wl.algorithmic_bytes()
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode tokens/s, mrope_decode_qk", "value": wl.T / (ms * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": ms,
+        "wall_ms_per_step": wall_ms, "graph_steps": args.graph, "measure": "same_buffers",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded normal q/k, cache lengths and rope deltas)",
+        "config": {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.new_tokens,
+                   "hq": wl.hq, "hk": wl.hk, "D": wl.D, "rotary_dim": wl.rotary_dim,
+                   "theta": wl.theta, "cache_rows": wl.capacity, "rmsnorm": wl.norm,
+                   "precision": args.precision},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "traffic_note": "not taken for decode", "algorithmic_bytes": alg,
+                     "kernel": f"{M.last_kernel()} (mrope_decode_qk)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(inp, wl, precision=args.precision)
+    print(json.dumps(line), flush=True)
+
+
 def copy_calib(nbytes: int, steps: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -411,12 +610,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--min-warmup-s", type=float, default=0.5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="buffer sets the rotating measure cycles through (3 = 1.8 GB for the "
+                         "headline: no step finds its inputs in the 256 MB MALL)")
     ap.add_argument("--cold", action="store_true",
-                    help="write a 1 GiB scratch buffer before every timed step (evicts L2 and the "
-                         "256 MB MALL) and time each step alone with HIP events")
+                    help="instead: read a 1 GiB scratch buffer before every timed step (evicts "
+                         "L2 and the 256 MB MALL) and time each step alone with HIP events")
     ap.add_argument("--cs-cache", action="store_true",
                     help="gather cos/sin from a cache by position (built once before the timed "
                          "steps; its build time is reported separately)")
@@ -425,16 +626,26 @@ def main():
                          "tensor dtype, bf16 tensor ops) or fp32 (fp32 tensor ops)")
     ap.add_argument("--cpu-procs", type=int, default=0,
                     help="processes for the oracle's multi-process sample (default: the "
-                         "cores this process may run on, at most 16; 1 = one thread only)")
+                         "cores this process may run on, within the box's share of 16; "
+                         "1 = one thread only)")
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--graph", type=int, default=0,
-                    help="capture this many steps in one HIP graph and time graph replays "
-                         "(for launch-bound workloads)")
+                    help="decode and position workloads: capture this many steps in one HIP "
+                         "graph and time graph replays")
+    ap.add_argument("--trace-summary", default="",
+                    help="print per-phase kernel durations of a rocprofv3 kernel trace "
+                         "directory of a bench.py run with the same --steps/--warmup")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        print(json.dumps(summarize_trace(args.trace_summary, args.warmup, args.steps), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path has no exchange step, and "
               "every run here uses a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.rotate < 1:
+        print("--steps >= 1, --warmup >= 0 and --rotate >= 1 are required", file=sys.stderr)
         sys.exit(2)
     if args.copy_calib:
         copy_calib(args.copy_calib, args.steps)
@@ -462,61 +673,62 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    q, k = dev(inp["q"]), dev(inp["k"])
-    wq, wk = dev(inp["wq"]), dev(inp["wk"])
-    q_out = torch.empty_like(q)
     if decode:
-        cache_len, rope_delta, k_cache = (dev(inp["cache_len"]), dev(inp["rope_delta"]),
-                                          dev(inp["k_cache"]))
+        bench_decode(args, wl, inp, dev)
+        return
 
-        def step():
-            M.mrope_decode_qk(q, k, cache_len, rope_delta, wl.new_tokens, wl.rotary_dim,
-                              wl.theta, k_cache, wq=wq, wk=wk, eps=wl.eps, q_out=q_out,
-                              precision=args.precision)
-    else:
-        pos = dev(inp["pos"])
-        k_out = torch.empty_like(k)
-        cache = None
-        if args.cs_cache:
-            rows = int(inp["pos"].max()) + 1
-            dim = wl.rotary_dim // 2 if wl.layout == "vision_2d" else wl.rotary_dim
-            cache, cache_info = build_cache(M, dim, wl.theta, rows)
+    q0, k0 = dev(inp["q"]), dev(inp["k"])
+    wq, wk = dev(inp["wq"]), dev(inp["wk"])
+    pos = dev(inp["pos"])
+    cache, cache_info = None, None
+    if args.cs_cache:
+        rows = int(inp["pos"].max()) + 1
+        dim = wl.rotary_dim // 2 if wl.layout == "vision_2d" else wl.rotary_dim
+        cache, cache_info = build_cache(M, dim, wl.theta, rows)
+    sets = []
+    for i in range(args.rotate):
+        q, k = (q0, k0) if i == 0 else (q0.clone(), k0.clone())
+        sets.append((q, k, torch.empty_like(q), torch.empty_like(k)))
 
+    def make_step(q, k, q_out, k_out):
         def step():
             M.rmsnorm_mrope_qk(q, k, pos, wl.rotary_dim, wl.theta, wl.section, wl.layout,
                                wq=wq, wk=wk, eps=wl.eps, q_out=q_out, k_out=k_out,
                                precision=args.precision, cs_cache=cache)
+        return step
 
-    if args.cold:
-        ms, n_timed, done, wall_ms = time_steps_cold(step, args)
-    else:
-        ms, n_timed, done, wall_ms = time_steps(step, args)   # one kernel launch per step
-
+    fns = [make_step(*s) for s in sets]
     alg_bytes = wl.algorithmic_bytes()
-    achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name) if args.precision == "exact" else None
-    if decode:
-        config = {"workload": wl.name, "batch": wl.batch, "new_tokens": wl.new_tokens,
-                  "hq": wl.hq, "hk": wl.hk, "D": wl.D, "rotary_dim": wl.rotary_dim,
-                  "theta": wl.theta, "cache_rows": wl.capacity, "rmsnorm": wl.norm,
-                  "precision": args.precision}
+    qk_bytes = (q0.numel() + k0.numel()) * q0.element_size()
+    if args.cold:
+        ms, wall_ms = time_steps_cold(fns[0], args.warmup, args.steps)
+        rec = {}
+        measure = "cold: 1 GiB read before each step, each step timed alone"
     else:
-        config = {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
-                  "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
-                  "section": list(wl.section), "rmsnorm": wl.norm,
-                  "precision": args.precision}
+        rec = line_measures(measures(M, fns, qk_bytes, args), alg_bytes, wl.T)
+        ms, wall_ms = rec["rotating"]["ms_per_step"], rec["rotating"]["wall_ms_per_step"]
+        measure = f"rotating over {args.rotate} buffer sets, back to back"
+    kernel = M.last_kernel()
+
+    achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
+    traffic, traffic_note = ((None, "not taken for this precision or the cache")
+                             if args.precision != "exact" or args.cs_cache
+                             else measured_traffic(wl.name))
+    config = {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
+              "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
+              "section": list(wl.section), "rmsnorm": wl.norm, "precision": args.precision}
+    if cache_info:
+        config["cs_cache"] = cache_info
     line = {
-        "metric": ("decode tokens/s, mrope_decode_qk" if decode else
-                   "Q+K tokens/s and achieved HBM GB/s (% of peak), fused RMSNorm+MRoPE"),
+        "metric": "Q+K tokens/s and achieved HBM GB/s (% of peak), fused RMSNorm+MRoPE",
         "value": wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": n_timed,
-        "warmup": done,
+        "steps": args.steps,
+        "warmup": args.warmup,
         "ms_per_step": ms,
         "wall_ms_per_step": wall_ms,
-        "graph_steps": args.graph,
-        "cold": args.cold,
+        "measure": measure,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -526,18 +738,15 @@ def main():
         "hbm_gbps": achieved_gbps,
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "kernel": f"{M.last_kernel()} (mrope_decode_qk)" if decode
-                     else f"{M.last_kernel()} (rmsnorm_mrope_qk)"},
+                     "traffic": traffic, "traffic_note": traffic_note,
+                     "algorithmic_bytes": alg_bytes,
+                     "kernel": f"{kernel} (rmsnorm_mrope_qk)"},
+        **rec,
     }
-    if not decode and args.cs_cache:
-        line["config"]["cs_cache"] = cache_info
-        line["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = (cpu_baseline_decode(inp, wl, precision=args.precision) if decode
-                                else cpu_baseline(inp, wl, precision=args.precision,
-                                                  procs=args.cpu_procs or
-                                                  min(len(os.sched_getaffinity(0)), 16)))
+        used, _ = host_cores()
+        line["cpu_baseline"] = cpu_baseline(inp, wl, precision=args.precision,
+                                            procs=args.cpu_procs or used)
     print(json.dumps(line), flush=True)
 
 

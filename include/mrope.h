@@ -383,6 +383,19 @@ int mrope_vision_pos_ids(const int32_t* grid_thw, int n_images, int spatial_merg
                          int32_t* status, void* stream);
 
 /*
+ * mrope_stream_copy — copy `bytes` from src to dst with a plain streaming
+ * kernel (16-byte loads of whole contiguous spans, then non-temporal 16-byte
+ * stores; no arithmetic).  A measurement aid, not a step of the rotary path:
+ * it gives the copy rate of a given number of bytes on this device, the
+ * achievable ceiling that the benchmark reports beside each kernel's rate.
+ *   src, dst: device buffers, 16-byte aligned, not overlapping.
+ *   bytes:    a multiple of 16, at most 2^40.
+ * EINVAL on a misaligned or overlapping buffer, a null pointer or a size
+ * that is negative or not a multiple of 16; bytes == 0 is a no-op.
+ */
+int mrope_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/*
  * mrope_last_error — message for the last non-zero return on this thread
  * (empty string if none).  The pointer stays valid until the next call on
  * the same thread.
@@ -393,9 +406,11 @@ const char* mrope_last_error(void);
  * mrope_last_kernel — name of the kernel that the last q/k launch on this
  * thread (rms_norm, apply_rotary_qk, rmsnorm_mrope_qk[_cached],
  * mrope_decode_qk, mrope_vision_qkv) enqueued: "qk_kernel" (rows spread over
- * lane groups, the general path), "flat_kernel" (a token's block of rows
- * lane after lane) or "stage_kernel" (rows staged through LDS, written in
- * output order); after mrope_rope_index, the kernels of its passes 2 and 3:
+ * lane groups, the general path), "qk_pipe_kernel" (one token per wavefront,
+ * its row-steps pipelined: launches of 2048 tokens or more on the positions
+ * path with 16-byte chunks), "flat_kernel" (a token's block of rows lane
+ * after lane) or "stage_kernel" (rows staged through LDS, written in output
+ * order); after mrope_rope_index, the kernels of its passes 2 and 3:
  * "rope_index_fused" (one kernel; up to 1024 chunks of 1024 tokens and 256
  * grids per type) or "rope_index_carry+apply" (two kernels, any size); empty
  * string before the first launch.  A diagnostic for profiles, benchmarks and

@@ -400,3 +400,17 @@ def test_head_counts_are_bounded():
                 k=FAKE + (1 << 36), qo=FAKE + (1 << 37), ko=FAKE + (1 << 38),
                 pos=FAKE + (1 << 39), wq=FAKE + (1 << 40), wk=FAKE + (1 << 40) + 4096)
     assert rc == _lib.MROPE_EUNSUPPORTED and b"heads" in lib.mrope_last_error()
+
+
+@fake_ptr_test
+def test_stream_copy_rejects_bad_arguments():
+    lib = _lib.load()
+    EINVAL = _lib.MROPE_EINVAL
+    assert lib.mrope_stream_copy(FAKE, FAKE + 0x100000, 0, None) == _lib.MROPE_OK
+    assert lib.mrope_stream_copy(FAKE, FAKE + 0x100000, -16, None) == EINVAL
+    assert lib.mrope_stream_copy(FAKE, FAKE + 0x100000, 24, None) == EINVAL      # not 16 x n
+    assert lib.mrope_stream_copy(FAKE + 8, FAKE + 0x100000, 64, None) == EINVAL  # misaligned
+    assert lib.mrope_stream_copy(None, FAKE, 64, None) == EINVAL
+    assert lib.mrope_stream_copy(FAKE, FAKE + 32, 64, None) == EINVAL            # overlap
+    assert "overlap" in lib.mrope_last_error().decode()
+    assert lib.mrope_stream_copy(FAKE, FAKE + 64, 1 << 41, None) == _lib.MROPE_EUNSUPPORTED

@@ -30,11 +30,12 @@ def test_traffic_record_follows_the_kernel_source(tmp_path, monkeypatch):
     (prof / "traffic_some_workload.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: current)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.measured_traffic("some_workload") == 123.0
+    val, note = bench.measured_traffic("some_workload")
+    assert val == 123.0 and current in note and "L2<->fabric" in note
     rec["kernel_source_hash"] = "0" * 16            # counters taken on other sources
     (prof / "traffic_some_workload.json").write_text(json.dumps(rec))
-    assert bench.measured_traffic("some_workload") is None
-    assert bench.measured_traffic("no_record") is None
+    assert bench.measured_traffic("some_workload")[0] is None
+    assert bench.measured_traffic("no_record")[0] is None
 
 
 def test_committed_traffic_records_name_their_commands():
@@ -52,5 +53,70 @@ def test_cpu_baseline_record(procs):
     r = bench.cpu_baseline(inp, wl, budget_s=0.3, procs=procs)
     assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
     assert r["cores"] == procs
+    assert r["cores_visible"] == len(os.sched_getaffinity(0))
+    assert "1024-token chunks" in r["sample"] or "16-token chunks" in r["sample"]
     if procs > 1:
         assert r["one_thread"] > 0
+
+
+def test_trace_summary_splits_the_phases(tmp_path):
+    """The summary picks the dispatches of each phase in launch order:
+    copy (W + K), then the kernel rotating (W + K) and on one set (W + K)."""
+    W_, K_ = 2, 3
+    rows = []
+    t = 1000
+    names = ["void mrope::(anonymous namespace)::stream_copy_kernel(char const*, char*, "
+             "unsigned long)"] * (W_ + K_) + ["__amd_rocclr_fillBufferAligned"] + \
+            ["void mrope::(anonymous namespace)::qk_kernel<true, 8, 0, true, 8, 0>(...)"] * \
+            (2 * (W_ + K_))
+    durs = [50] * W_ + [40] * K_ + [7] + [120] * W_ + [100] * K_ + [110] * W_ + [90] * K_
+    for i, (n, d) in enumerate(zip(names, durs)):
+        rows.append({"Kernel_Name": n, "Start_Timestamp": str(t), "End_Timestamp": str(t + d * 1000)})
+        t += d * 1000 + 500
+    sub = tmp_path / "host" / "1"
+    sub.mkdir(parents=True)
+    with open(sub / "x_kernel_trace.csv", "w") as f:
+        f.write("Kind,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for r in rows[::-1]:      # out of order on purpose: sorted by start time
+            name, t0, t1 = r["Kernel_Name"], r["Start_Timestamp"], r["End_Timestamp"]
+            f.write(f'KERNEL_DISPATCH,"{name}",{t0},{t1}\n')
+    out = bench.summarize_trace(str(tmp_path), W_, K_)
+    got = {(p["phase"], "copy" if "copy" in p["kernel"] else "kernel"): p for p in out["phases"]}
+    assert got[("timed_rotating", "copy")]["mean_us"] == 40.0
+    assert got[("timed_rotating", "kernel")]["mean_us"] == 100.0
+    assert got[("timed_same_buffers", "kernel")]["mean_us"] == 90.0
+    assert got[("timed_rotating", "kernel")]["dispatches"] == K_
+    assert "unmatched" not in out
+
+
+def test_warmup_and_steps_are_exact(monkeypatch):
+    """time_region runs exactly W untimed and K timed steps, cycling the sets."""
+    calls = []
+
+    class Ev:
+        def __init__(self, **kw):
+            pass
+
+        def record(self, s=None):
+            calls.append("ev")
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    class FakeCuda:
+        Event = Ev
+
+        @staticmethod
+        def current_stream():
+            return None
+
+        @staticmethod
+        def synchronize():
+            pass
+
+    import torch
+    monkeypatch.setattr(torch, "cuda", FakeCuda)
+    fns = [lambda i=i: calls.append(i) for i in range(3)]
+    ms, _ = bench.time_region(fns, 4, 5)
+    assert calls == [0, 1, 2, 0, "ev", 0, 1, 2, 0, 1, "ev"]
+    assert ms == 1.0 / 5

@@ -80,6 +80,7 @@ SIGNATURES = {
     "mrope_rope_index": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
                                   _vp, _c_i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "mrope_vision_pos_ids": (_c_int, [_vp, _c_int, _c_int, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "mrope_stream_copy": (_c_int, [_vp, _vp, _c_i64, _vp]),
     "mrope_last_error": (ctypes.c_char_p, []),
     "mrope_last_kernel": (ctypes.c_char_p, []),
 }

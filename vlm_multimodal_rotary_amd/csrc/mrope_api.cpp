@@ -412,6 +412,27 @@ int waves_per_simd_stage() {
   return 0;
 }
 
+// The pipelined q/k kernel (one token per wavefront, its row-steps as one
+// stream with P steps of loads in flight while it finishes a step, cos/sin in
+// registers) serves the positions path for 16-byte chunks when the launch has
+// at least kMinPipeTokens tokens.  Measured on MI355X with inputs that the
+// memory-side cache does not hold (rotating buffer sets), against qk_kernel.
+// MROPE_PIPE=0/1 forces the choice where it is allowed, MROPE_PIPE_DEPTH the
+// depth (2 or 3) (tuning).
+constexpr int64_t kMinPipeTokens = 2048;
+
+bool use_pipe(const QKArgs& a, int cs_mode, int v, int es) {
+  if (cs_mode != mrope::kCsFromPositions || v * es != 16 || a.T < kMinPipeTokens) return false;
+  static const int env = env_int("MROPE_PIPE", -1);
+  if (env >= 0) return env != 0;
+  return true;
+}
+
+int pipe_depth() {
+  static const int env = env_int("MROPE_PIPE_DEPTH", 0);
+  return env == 2 || env == 3 ? env : 2;
+}
+
 // Launch geometry and the remaining per-launch fields.
 struct DecodeArgs {
   const int32_t* cache_len = nullptr;
@@ -481,8 +502,8 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
     p.kc_cap = dec->kc_cap;
   }
 
-  // Tokens per tile: a wavefront's cos/sin slice (2 * nt * half doubles)
-  // stays within 8 KB.
+  // Tokens per tile: a wavefront's cos/sin slice (2 * nt * half binary32
+  // values) stays within 4 KB.
   int nt_cap = p.half > 0 ? 512 / p.half : 16;
   if (nt_cap < 1) nt_cap = 1;
   if (nt_cap > 16) nt_cap = 16;
@@ -557,6 +578,10 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
     p.waves_cap = waves_per_simd_flat();
     hrc = mrope::launch_flat(a.dtype, v, prec, p, tab, stream);
     g_last_kernel = "flat_kernel";
+  } else if (use_pipe(a, cs_mode, v, es)) {
+    p.waves_cap = waves_per_simd(a, v, es);
+    hrc = mrope::launch_qk_pipe(a.dtype, v, norm, prec, pipe_depth(), p, tab, stream);
+    g_last_kernel = "qk_pipe_kernel";
   } else {
     p.waves_cap = waves_per_simd(a, v, es);
     hrc = mrope::launch_qk(a.dtype, v, cs_mode, norm, prec, p, tab, nt_cap, stream);
@@ -1062,6 +1087,24 @@ int mrope_decode_qk(const void* q, int64_t q_tok_stride, int hq, const void* k,
       if (overlaps(cache_ext, e)) return fail(MROPE_EINVAL, "k_cache overlaps cache_len/rope_delta");
   return run_qk(a, mrope::kCsDecode, norm, tab, nullptr, 0, nullptr, nullptr, 0, eps, stream,
                 extra, 2, &dec);
+}
+
+int mrope_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0) return fail(MROPE_EINVAL, "bytes = %lld is negative", (long long)bytes);
+  if (bytes % 16 != 0) return fail(MROPE_EINVAL, "bytes = %lld is not a multiple of 16",
+                                   (long long)bytes);
+  if (bytes > (int64_t(1) << 40))
+    return fail(MROPE_EUNSUPPORTED, "bytes = %lld exceeds 2^40", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (src == nullptr || dst == nullptr) return fail(MROPE_EINVAL, "src and dst must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+    return fail(MROPE_EINVAL, "src and dst must be 16-byte aligned");
+  if (overlaps(bytes_at(src, bytes, 1), bytes_at(dst, bytes, 1)))
+    return fail(MROPE_EINVAL, "src and dst overlap");
+  const int hrc = mrope::launch_stream_copy(src, dst, bytes, stream);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
 }
 
 const char* mrope_last_error(void) { return g_err.c_str(); }

@@ -150,12 +150,17 @@ int launch_vision_pos_ids(const VisionPosParams& p, void* stream);
 
 // Launchers (mrope_kernels.hip).  Return a hipError_t value as int.
 // nt_cap bounds the tokens per wavefront (its cos/sin LDS slice holds
-// 2 * nt * half doubles, and a tile's byte extent must fit 31 bits).
+// 2 * nt * half binary32 values, and a tile's byte extent must fit 31 bits).
 // prec: MROPE_PRECISION_EXACT or _DTYPE, or _FP32 for bf16 (the host maps
 // binary32 FP32 to DTYPE, the same arithmetic).
 int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKParams& p,
               const ColTable& tab, int nt_cap, void* stream);
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
+// The pipelined q/k kernel (positions path, 16-byte chunks: vec 8 for bf16, 4
+// for binary32; one wavefront per token; depth = row-steps whose loads are in
+// flight while a step is finished, 2 or 3).
+int launch_qk_pipe(int dtype, int vec, bool norm, int prec, int depth, const QKParams& p,
+                   const ColTable& tab, void* stream);
 // The flat q/k kernel: positions path without RMSNorm, one token per
 // wavefront, the token's blocks read as consecutive chunks.
 int launch_flat(int dtype, int vec, int prec, const QKParams& p, const ColTable& tab,
@@ -170,5 +175,8 @@ int stage_max_v_chunks();
 // cos/sin cache by position: cache[(p * n_freq + i) * 2 + {0, 1}] = (cos, sin)
 // of fl32(float(p) * tab.inv[i]) for p < rows, i < n_freq.
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream);
+// Plain streaming copy of `bytes` (a multiple of 16, 16-byte aligned buffers)
+// (mrope_copy.hip).
+int launch_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 }  // namespace mrope
