@@ -28,8 +28,10 @@
  *    be below 2^24 so float(p) is exact.
  *  - Device buffers are owned by the caller.  The library allocates nothing
  *    and keeps no state between calls beyond two thread-local diagnostics
- *    (mrope_last_error, mrope_last_kernel); small tables (section, inv_freq)
- *    are host pointers copied into kernel arguments.
+ *    (mrope_last_error, mrope_last_kernel) and the static device workspace of
+ *    mrope_rope_index_noalloc (1 MiB per GPU, in the code object); small
+ *    tables (section, inv_freq) are host pointers copied into kernel
+ *    arguments.
  *  - Kernels address a token's rows of a tensor (or, for per-head planes, the
  *    rows of a few tokens across all planes) with 32-bit byte offsets: a
  *    span of 2^31 bytes or more is MROPE_EUNSUPPORTED, and so are more than
@@ -363,6 +365,29 @@ int mrope_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask
                      const int32_t* video_grid_thw, int n_videos, int spatial_merge,
                      int32_t* pos, int64_t pos_axis_stride, int32_t* rope_delta,
                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mrope_rope_index_noalloc — mrope_rope_index without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that allocate nothing per step, harnesses that forbid
+ * hipMalloc).  The workspace is a static device array of
+ * MROPE_ROPE_INDEX_SCRATCH_BYTES in the library's code object: each GPU
+ * holds its own copy until the process ends, and the first call on a GPU
+ * takes its address there (hipGetSymbolAddress, no allocation).  Arguments,
+ * results, status bits and errors are mrope_rope_index's, and so are the
+ * kernels; sizes whose workspace (mrope_rope_index_workspace_size) exceeds
+ * the static array are MROPE_EUNSUPPORTED, with nothing enqueued.  Calls on
+ * one GPU share its array: two calls whose work overlaps in time on that GPU
+ * (different streams, or host threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.  Nothing needs clearing
+ * between calls: every pass writes the workspace before it reads it.
+ */
+#define MROPE_ROPE_INDEX_SCRATCH_BYTES (1 << 20)
+int mrope_rope_index_noalloc(const int32_t* mm_token_type, const int32_t* attention_mask,
+                             int batch, int64_t seq_len, const int32_t* image_grid_thw,
+                             int n_images, const int32_t* video_grid_thw, int n_videos,
+                             int spatial_merge, int32_t* pos, int64_t pos_axis_stride,
+                             int32_t* rope_delta, int32_t* status, void* stream);
 
 /*
  * mrope_vision_pos_ids — the (row, col) position of every vision patch

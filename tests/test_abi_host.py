@@ -414,3 +414,27 @@ def test_stream_copy_rejects_bad_arguments():
     assert lib.mrope_stream_copy(FAKE, FAKE + 32, 64, None) == EINVAL            # overlap
     assert "overlap" in lib.mrope_last_error().decode()
     assert lib.mrope_stream_copy(FAKE, FAKE + 64, 1 << 41, None) == _lib.MROPE_EUNSUPPORTED
+
+
+@fake_ptr_test
+def test_rope_index_noalloc_rejects_before_any_hip_call():
+    """The static-workspace form checks its arguments (and its size limit)
+    before it takes the array's device address or launches anything."""
+    lib = _lib.load()
+    EINVAL, EUNSUP = _lib.MROPE_EINVAL, _lib.MROPE_EUNSUPPORTED
+
+    def call(B=2, L=100, types=FAKE, pos=FAKE + 0x100000, delta=FAKE + 0x200000,
+             status=FAKE + 0x300000, n_img=0, grids=None, merge=2):
+        return lib.mrope_rope_index_noalloc(types, None, B, L, grids, n_img, None, 0, merge, pos,
+                                            B * L, delta, status, None)
+    assert call(B=-1) == EINVAL
+    assert call(merge=0) == EINVAL
+    assert call(types=None) == EINVAL
+    assert call(status=None) == EINVAL
+    assert call(n_img=3, grids=None) == EINVAL
+    assert call(pos=FAKE + 2) == EINVAL                              # misaligned
+    assert call(pos=FAKE + 40) == EINVAL                             # overlaps the token types
+    n_img = _lib.ROPE_INDEX_SCRATCH_BYTES // 8 + 16
+    assert lib.mrope_rope_index_workspace_size(2, 100, n_img, 0) > _lib.ROPE_INDEX_SCRATCH_BYTES
+    assert call(n_img=n_img, grids=FAKE + 0x400000) == EUNSUP
+    assert "static workspace" in lib.mrope_last_error().decode()

@@ -43,6 +43,7 @@ POS_FLAGS = {POS_BAD_TYPE: "token type not 0/1/2", POS_NO_GRID: "visual run with
              POS_NOT_DIVISIBLE: "grid not divisible by the merge size",
              POS_COUNT: "patch total differs from n_tokens"}
 MAX_VISION_IMAGES = 4096
+ROPE_INDEX_SCRATCH_BYTES = 1 << 20
 
 _c_int, _c_i64, _c_double, _c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
 _vp = ctypes.c_void_p
@@ -79,6 +80,8 @@ SIGNATURES = {
     "mrope_rope_index_workspace_size": (ctypes.c_size_t, [_c_int, _c_i64, _c_int, _c_int]),
     "mrope_rope_index": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
                                   _vp, _c_i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "mrope_rope_index_noalloc": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int,
+                                          _c_int, _vp, _c_i64, _vp, _vp, _vp]),
     "mrope_vision_pos_ids": (_c_int, [_vp, _c_int, _c_int, _c_i64, _vp, _c_i64, _vp, _vp]),
     "mrope_stream_copy": (_c_int, [_vp, _vp, _c_i64, _vp]),
     "mrope_last_error": (ctypes.c_char_p, []),

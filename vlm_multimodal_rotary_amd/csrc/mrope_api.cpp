@@ -629,6 +629,96 @@ Extent bytes_at(const void* base, int64_t n, int elem_bytes) {
   return extent_of(base, 1, 0, n, elem_bytes);
 }
 
+// Checks of the position builder's arguments other than the workspace.
+int check_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask, int batch,
+                     int64_t seq_len, const int32_t* image_grid_thw, int n_images,
+                     const int32_t* video_grid_thw, int n_videos, int spatial_merge,
+                     int32_t* pos, int64_t pos_axis_stride, int32_t* rope_delta,
+                     int32_t* status, RopeWs& w) {
+  if (batch < 0 || seq_len < 0 || n_images < 0 || n_videos < 0)
+    return fail(MROPE_EINVAL, "batch, seq_len, n_images and n_videos must be >= 0");
+  if (spatial_merge < 1 || spatial_merge > 1024)
+    return fail(MROPE_EINVAL, "spatial_merge = %d must be in [1, 1024]", spatial_merge);
+  if (!rope_ws_layout(batch, seq_len, n_images, n_videos, w))
+    return fail(MROPE_EUNSUPPORTED, "batch * seq_len is too large");
+  const int64_t T = (int64_t)batch * seq_len;
+  if (T > 0 && (mm_token_type == nullptr || pos == nullptr))
+    return fail(MROPE_EINVAL, "mm_token_type and pos must be non-NULL");
+  if (batch > 0 && rope_delta == nullptr) return fail(MROPE_EINVAL, "rope_delta is NULL");
+  if (status == nullptr) return fail(MROPE_EINVAL, "status is NULL");
+  if (n_images > 0 && image_grid_thw == nullptr) return fail(MROPE_EINVAL, "image_grid_thw is NULL");
+  if (n_videos > 0 && video_grid_thw == nullptr) return fail(MROPE_EINVAL, "video_grid_thw is NULL");
+  if (T > 0 && pos_axis_stride < T)
+    return fail(MROPE_EINVAL, "pos_axis_stride %lld < batch*seq_len %lld",
+                (long long)pos_axis_stride, (long long)T);
+  for (const void* ptr : {(const void*)mm_token_type, (const void*)attention_mask,
+                          (const void*)image_grid_thw, (const void*)video_grid_thw,
+                          (const void*)pos, (const void*)rope_delta, (const void*)status})
+    if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0)
+      return fail(MROPE_EINVAL, "int32 buffers must be 4-byte aligned");
+  return MROPE_OK;
+}
+
+// Overlap checks of the outputs (and a caller workspace) against the inputs
+// and one another.
+int check_rope_index_overlaps(const int32_t* mm_token_type, const int32_t* attention_mask,
+                              int batch, int64_t seq_len, const int32_t* image_grid_thw,
+                              int n_images, const int32_t* video_grid_thw, int n_videos,
+                              int32_t* pos, int64_t pos_axis_stride, int32_t* rope_delta,
+                              int32_t* status, const void* workspace, size_t ws_bytes) {
+  const int64_t T = (int64_t)batch * seq_len;
+  const Extent outs[4] = {extent_of(pos, 3, pos_axis_stride, T, 4), bytes_at(rope_delta, batch, 4),
+                          bytes_at(status, 1, 4), bytes_at(workspace, (int64_t)ws_bytes, 1)};
+  const Extent ins[4] = {bytes_at(mm_token_type, T, 4), bytes_at(attention_mask, T, 4),
+                         bytes_at(image_grid_thw, 3 * (int64_t)n_images, 4),
+                         bytes_at(video_grid_thw, 3 * (int64_t)n_videos, 4)};
+  for (int i = 0; i < 4; ++i) {
+    for (int k = 0; k < 4; ++k)
+      if (overlaps(outs[i], ins[k])) return fail(MROPE_EINVAL, "an output overlaps an input");
+    for (int k = i + 1; k < 4; ++k)
+      if (overlaps(outs[i], outs[k]))
+        return fail(MROPE_EINVAL, "pos, rope_delta, status and workspace must not overlap");
+  }
+  return MROPE_OK;
+}
+
+// The launch of the three passes with a checked workspace.
+int run_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask, int batch,
+                   int64_t seq_len, const int32_t* image_grid_thw, int n_images,
+                   const int32_t* video_grid_thw, int n_videos, int spatial_merge, int32_t* pos,
+                   int64_t pos_axis_stride, int32_t* rope_delta, int32_t* status,
+                   void* workspace, const RopeWs& w, void* stream) {
+  mrope::RopeIndexParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.types = mm_token_type;
+  p.mask = attention_mask;
+  p.B = batch;
+  p.L = seq_len;
+  p.C = (int)w.chunks_per_sample;
+  p.image_grid = image_grid_thw;
+  p.n_images = n_images;
+  p.video_grid = video_grid_thw;
+  p.n_videos = n_videos;
+  p.merge = spatial_merge;
+  p.pos = pos;
+  p.pos_stride = pos_axis_stride;
+  p.rope_delta = rope_delta;
+  p.status = status;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_sum = reinterpret_cast<int32_t*>(ws + w.sum);
+  p.ws_carry = reinterpret_cast<int32_t*>(ws + w.carry);
+  p.ws_valid = reinterpret_cast<int32_t*>(ws + w.valid);
+  p.ws_end = reinterpret_cast<int32_t*>(ws + w.end);
+  p.ws_adv_i = reinterpret_cast<int64_t*>(ws + w.adv_i);
+  p.ws_adv_v = reinterpret_cast<int64_t*>(ws + w.adv_v);
+  p.ws_cum_t = reinterpret_cast<int32_t*>(ws + w.cum_t);
+  const int hrc = mrope::launch_rope_index(p, stream, &g_last_kernel);
+  if (hrc != (int)hipSuccess)
+    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
+  return ok();
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -711,73 +801,52 @@ int mrope_rope_index(const int32_t* mm_token_type, const int32_t* attention_mask
                      const int32_t* video_grid_thw, int n_videos, int spatial_merge,
                      int32_t* pos, int64_t pos_axis_stride, int32_t* rope_delta,
                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 0 || seq_len < 0 || n_images < 0 || n_videos < 0)
-    return fail(MROPE_EINVAL, "batch, seq_len, n_images and n_videos must be >= 0");
-  if (spatial_merge < 1 || spatial_merge > 1024)
-    return fail(MROPE_EINVAL, "spatial_merge = %d must be in [1, 1024]", spatial_merge);
   RopeWs w;
-  if (!rope_ws_layout(batch, seq_len, n_images, n_videos, w))
-    return fail(MROPE_EUNSUPPORTED, "batch * seq_len is too large");
-  const int64_t T = (int64_t)batch * seq_len;
-  if (T > 0 && (mm_token_type == nullptr || pos == nullptr))
-    return fail(MROPE_EINVAL, "mm_token_type and pos must be non-NULL");
-  if (batch > 0 && rope_delta == nullptr) return fail(MROPE_EINVAL, "rope_delta is NULL");
-  if (status == nullptr) return fail(MROPE_EINVAL, "status is NULL");
-  if (n_images > 0 && image_grid_thw == nullptr) return fail(MROPE_EINVAL, "image_grid_thw is NULL");
-  if (n_videos > 0 && video_grid_thw == nullptr) return fail(MROPE_EINVAL, "video_grid_thw is NULL");
-  if (T > 0 && pos_axis_stride < T)
-    return fail(MROPE_EINVAL, "pos_axis_stride %lld < batch*seq_len %lld",
-                (long long)pos_axis_stride, (long long)T);
+  int rc = check_rope_index(mm_token_type, attention_mask, batch, seq_len, image_grid_thw,
+                            n_images, video_grid_thw, n_videos, spatial_merge, pos,
+                            pos_axis_stride, rope_delta, status, w);
+  if (rc) return rc;
   if (workspace == nullptr || workspace_bytes < w.total)
     return fail(MROPE_EINVAL, "workspace of %zu bytes needed (got %zu)", w.total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
     return fail(MROPE_EINVAL, "workspace must be 8-byte aligned");
-  for (const void* ptr : {(const void*)mm_token_type, (const void*)attention_mask,
-                          (const void*)image_grid_thw, (const void*)video_grid_thw,
-                          (const void*)pos, (const void*)rope_delta, (const void*)status})
-    if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0)
-      return fail(MROPE_EINVAL, "int32 buffers must be 4-byte aligned");
-  const Extent outs[4] = {extent_of(pos, 3, pos_axis_stride, T, 4), bytes_at(rope_delta, batch, 4),
-                          bytes_at(status, 1, 4), bytes_at(workspace, (int64_t)w.total, 1)};
-  const Extent ins[4] = {bytes_at(mm_token_type, T, 4), bytes_at(attention_mask, T, 4),
-                         bytes_at(image_grid_thw, 3 * (int64_t)n_images, 4),
-                         bytes_at(video_grid_thw, 3 * (int64_t)n_videos, 4)};
-  for (int i = 0; i < 4; ++i) {
-    for (int k = 0; k < 4; ++k)
-      if (overlaps(outs[i], ins[k])) return fail(MROPE_EINVAL, "an output overlaps an input");
-    for (int k = i + 1; k < 4; ++k)
-      if (overlaps(outs[i], outs[k]))
-        return fail(MROPE_EINVAL, "pos, rope_delta, status and workspace must not overlap");
-  }
-  mrope::RopeIndexParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.types = mm_token_type;
-  p.mask = attention_mask;
-  p.B = batch;
-  p.L = seq_len;
-  p.C = (int)w.chunks_per_sample;
-  p.image_grid = image_grid_thw;
-  p.n_images = n_images;
-  p.video_grid = video_grid_thw;
-  p.n_videos = n_videos;
-  p.merge = spatial_merge;
-  p.pos = pos;
-  p.pos_stride = pos_axis_stride;
-  p.rope_delta = rope_delta;
-  p.status = status;
-  char* ws = static_cast<char*>(workspace);
-  p.ws_sum = reinterpret_cast<int32_t*>(ws + w.sum);
-  p.ws_carry = reinterpret_cast<int32_t*>(ws + w.carry);
-  p.ws_valid = reinterpret_cast<int32_t*>(ws + w.valid);
-  p.ws_end = reinterpret_cast<int32_t*>(ws + w.end);
-  p.ws_adv_i = reinterpret_cast<int64_t*>(ws + w.adv_i);
-  p.ws_adv_v = reinterpret_cast<int64_t*>(ws + w.adv_v);
-  p.ws_cum_t = reinterpret_cast<int32_t*>(ws + w.cum_t);
-  const int hrc = mrope::launch_rope_index(p, stream, &g_last_kernel);
+  rc = check_rope_index_overlaps(mm_token_type, attention_mask, batch, seq_len, image_grid_thw,
+                                 n_images, video_grid_thw, n_videos, pos, pos_axis_stride,
+                                 rope_delta, status, workspace, w.total);
+  if (rc) return rc;
+  return run_rope_index(mm_token_type, attention_mask, batch, seq_len, image_grid_thw, n_images,
+                        video_grid_thw, n_videos, spatial_merge, pos, pos_axis_stride,
+                        rope_delta, status, workspace, w, stream);
+}
+
+int mrope_rope_index_noalloc(const int32_t* mm_token_type, const int32_t* attention_mask,
+                             int batch, int64_t seq_len, const int32_t* image_grid_thw,
+                             int n_images, const int32_t* video_grid_thw, int n_videos,
+                             int spatial_merge, int32_t* pos, int64_t pos_axis_stride,
+                             int32_t* rope_delta, int32_t* status, void* stream) {
+  RopeWs w;
+  int rc = check_rope_index(mm_token_type, attention_mask, batch, seq_len, image_grid_thw,
+                            n_images, video_grid_thw, n_videos, spatial_merge, pos,
+                            pos_axis_stride, rope_delta, status, w);
+  if (rc) return rc;
+  if (w.total > mrope::kRopeIndexScratchBytes)
+    return fail(MROPE_EUNSUPPORTED,
+                "these sizes need %zu bytes of workspace; the static workspace of "
+                "mrope_rope_index_noalloc holds %zu (use mrope_rope_index with a workspace)",
+                w.total, mrope::kRopeIndexScratchBytes);
+  rc = check_rope_index_overlaps(mm_token_type, attention_mask, batch, seq_len, image_grid_thw,
+                                 n_images, video_grid_thw, n_videos, pos, pos_axis_stride,
+                                 rope_delta, status, nullptr, 0);
+  if (rc) return rc;
+  void* scratch = nullptr;
+  const int hrc = mrope::rope_index_scratch(&scratch);
   if (hrc != (int)hipSuccess)
-    return fail(MROPE_EHIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)hrc));
-  return ok();
+    return fail(MROPE_EHIP, "the static workspace's device address: %s",
+                hipGetErrorString((hipError_t)hrc));
+  return run_rope_index(mm_token_type, attention_mask, batch, seq_len, image_grid_thw, n_images,
+                        video_grid_thw, n_videos, spatial_merge, pos, pos_axis_stride,
+                        rope_delta, status, scratch, w, stream);
 }
 
 int mrope_vision_pos_ids(const int32_t* grid_thw, int n_images, int spatial_merge,

@@ -146,6 +146,11 @@ struct VisionPosParams {
 
 // *kernel receives the name of the pass-2/3 form launched.
 int launch_rope_index(const RopeIndexParams& p, void* stream, const char** kernel);
+// Bytes of the static workspace of mrope_rope_index_noalloc, and its device
+// address on the current device (taken once per device with
+// hipGetSymbolAddress).  Returns a hipError_t value as int.
+constexpr size_t kRopeIndexScratchBytes = MROPE_ROPE_INDEX_SCRATCH_BYTES;
+int rope_index_scratch(void** out);
 int launch_vision_pos_ids(const VisionPosParams& p, void* stream);
 
 // Launchers (mrope_kernels.hip).  Return a hipError_t value as int.

@@ -33,9 +33,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mrope_internal.h"
 
+// Workspace of mrope_rope_index_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  In host code this name is a
+// host-side stand-in, not a device address: only the address that
+// hipGetSymbolAddress returns on each device reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[mrope::kRopeIndexScratchBytes];
+
 namespace mrope {
+
+int rope_index_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t rc = hipGetDevice(&dev);
+  if (rc != hipSuccess) return (int)rc;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    rc = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (rc != hipSuccess) return (int)rc;
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return (int)hipSuccess;
+}
+
 namespace {
 
 constexpr int kPT = kPosThreads;
