@@ -80,18 +80,13 @@ def test_decode_in_place_q_and_full_size(M):
     oq, oc = _oracle(inp, wl)
     assert_bf16_close(gq, oq, 1, "decode q in place")
     assert_bf16_close(gc, oc, 1, "decode cache")
-    # the benchmark's configuration, checked on a sample of sequences
+    # the benchmark's configuration, every sequence and every cache row
     inp = W.make_decode_inputs(wl)
     note(f"decode full B={inp['batch']} cap={inp['capacity']}")
     gq, gc = _run(M, inp, wl)
-    rows = np.random.default_rng(7).choice(inp["batch"], 24, replace=False)
-    sub = dict(inp)
-    sub["q"], sub["k"] = inp["q"][rows], inp["k"][rows]
-    sub["cache_len"], sub["rope_delta"] = inp["cache_len"][rows], inp["rope_delta"][rows]
-    sub["k_cache"] = inp["k_cache"][rows]
-    oq, oc = _oracle(sub, wl)
-    assert_bf16_close(gq[rows], oq, 1, "decode q sampled")
-    assert_bf16_close(gc[rows], oc, 1, "decode cache sampled")
+    oq, oc = _oracle(inp, wl)
+    assert_bf16_close(gq, oq, 1, "decode q full")
+    assert_bf16_close(gc, oc, 1, "decode cache full")
 
 
 def test_decode_and_prefill_replay_in_a_hip_graph(M):

@@ -75,19 +75,6 @@ def test_fused_windows_bit_exact(M, name, T, precision):
     _assert_bits(gk, ok, f"{name} k {precision}")
 
 
-@pytest.mark.parametrize("precision", MODES)
-def test_headline_full_size_sampled(M, precision):
-    wl = W.WORKLOADS["omni_text_prefill"]
-    inp = W.make_inputs(wl)
-    note(f"fused full omni_text_prefill precision={precision}")
-    gq, gk = _fused_dev(M, inp, wl, precision)
-    rng = np.random.default_rng(300)
-    rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 160, replace=False)]))
-    oq, ok = _fused_oracle(inp, wl, precision, rows)
-    _assert_bits(gq[rows], oq, f"omni full q {precision}")
-    _assert_bits(gk[rows], ok, f"omni full k {precision}")
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("precision", MODES)
 def test_apply_rotary_tables_bit_exact(M, dtype, precision):

@@ -89,21 +89,6 @@ def test_vision_qkv_equals_the_fused_path(M):
     assert torch.equal(v, qkv[:, 2].transpose(0, 1))
 
 
-@pytest.mark.parametrize("name", list(W.VISION_QKV_WORKLOADS))
-def test_vision_qkv_full_size_sampled(M, name):
-    wl = W.VISION_QKV_WORKLOADS[name]
-    inp = W.make_vision_qkv_inputs(wl)
-    note(f"vision_qkv full {name} n={wl.T}")
-    gq, gk, gv = _run(M, inp["qkv"], inp["pos"], wl.dtype, wl.rotary_dim, wl.theta)
-    rng = np.random.default_rng(73)
-    rows = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 160, replace=False)]))
-    oq, ok, ov = O.vision_qkv(inp["qkv"][rows], inp["pos"][:, rows], rotary_dim=wl.rotary_dim,
-                              theta=wl.theta, dtype=wl.dtype)
-    assert_close(gq[:, rows], oq, wl.dtype, f"{name} q sampled")
-    assert_close(gk[:, rows], ok, wl.dtype, f"{name} k sampled")
-    assert np.array_equal(gv.view(np.uint8), inp["qkv"][:, 2].transpose(1, 0, 2).view(np.uint8))
-
-
 def test_vision_qkv_empty(M):
     import torch
     qkv = torch.empty((0, 3, 16, 72), dtype=torch.float32, device="cuda")
