@@ -15,8 +15,8 @@ Two builders, written from the pages in their order of steps:
   the order the vision tower emits patches ("Qwen3-VL" source walkthrough,
   ``rot_pos_emb``: merge-block order, repeated per frame).
 
-Plain Python loops over segments and numpy ``arange``/``meshgrid`` for the
-coordinates; every result is an exact integer.
+Plain Python loops over tokens, runs and slots; every result is an exact
+integer.
 
 Readings where the pages leave a step open:
 
@@ -32,8 +32,6 @@ Readings where the pages leave a step open:
 """
 from __future__ import annotations
 
-import itertools
-
 import numpy as np
 
 TEXT, IMAGE, VIDEO = 0, 1, 2
@@ -43,93 +41,130 @@ class PositionError(ValueError):
     """The inputs describe a sequence the walkthrough cannot build."""
 
 
-def expand_video_grids(video_grid_thw):
-    """Each video of t temporal slices becomes t grids with temporal length 1
-    (the walkthrough splits videos by timestamps into per-slice segments)."""
-    if video_grid_thw is None or len(video_grid_thw) == 0:
-        return np.zeros((0, 3), dtype=np.int64)
-    g = np.asarray(video_grid_thw, dtype=np.int64).reshape(-1, 3)
-    out = np.repeat(g, g[:, 0], axis=0)
-    out[:, 0] = 1
+# ---------------------------------------------------------------------------
+# Step 1 of the walkthrough: the grid queues
+# ---------------------------------------------------------------------------
+
+def grid_queues(image_grid_thw, video_grid_thw):
+    """The two grid queues of a batch: images as given, and every video of t
+    temporal slices as t single-slice grids (1, h, w) in slice order (the
+    walkthrough cuts videos into per-slice segments at their timestamps).
+    Returns (images, slices), each a list of (t, h, w) int tuples."""
+    images = []
+    if image_grid_thw is not None:
+        for t, h, w in np.asarray(image_grid_thw, dtype=np.int64).reshape(-1, 3).tolist():
+            images.append((t, h, w))
+    slices = []
+    if video_grid_thw is not None:
+        for t, h, w in np.asarray(video_grid_thw, dtype=np.int64).reshape(-1, 3).tolist():
+            for _ in range(t):
+                slices.append((1, h, w))
+    return images, slices
+
+
+# ---------------------------------------------------------------------------
+# Step 2: runs of equal token type in the sequence left after padding
+# ---------------------------------------------------------------------------
+
+def type_runs(types):
+    """Maximal runs of one token type, as (type, first, end) with end
+    exclusive: a new run starts wherever the type differs from the token
+    before it (two images separated by a text token are two runs)."""
+    runs = []
+    for i, ty in enumerate(types):
+        if runs and runs[-1][0] == ty:
+            runs[-1][2] = i + 1
+        else:
+            runs.append([ty, i, i + 1])
+    return [tuple(r) for r in runs]
+
+
+# ---------------------------------------------------------------------------
+# Steps 3-4: positions of a visual run
+# ---------------------------------------------------------------------------
+
+def visual_run_positions(start: int, grid_thw, merge: int) -> np.ndarray:
+    """[3, n] positions of the slots of one visual run that begins at rotary
+    position ``start``.
+
+    The grid is given before spatial merging: its slots form the
+    (t, h // merge, w // merge) grid, taken width first, then height, then
+    time.  Slot s is at time index s // (rows * cols), row (s // cols) %
+    rows and column s % cols, and gets (start + time, start + row,
+    start + column): every axis is offset by the run's start.
+    """
+    t, h, w = (int(v) for v in grid_thw)
+    rows, cols = h // merge, w // merge
+    n = t * rows * cols
+    out = np.empty((3, n), dtype=np.int64)
+    for s in range(n):
+        out[0, s] = start + s // (rows * cols)
+        out[1, s] = start + (s // cols) % rows
+        out[2, s] = start + s % cols
     return out
 
 
-def vision_segment_ids(start: int, grid_thw, merge: int, temporal_merge: int = 1,
-                       time_interval: int = 1) -> np.ndarray:
-    """[3, n] positions of one visual segment starting at ``start``.
-
-    The grid is given before spatial merging; the slot grid is
-    (t // temporal_merge, h // merge, w // merge).  T = t_index *
-    time_interval + start, H = row + start, W = col + start, flattened with
-    the width fastest, then the height, then the time.
-    """
-    t, h, w = (int(v) for v in grid_thw)
-    gt, gh, gw = t // temporal_merge, h // merge, w // merge
-    pt = np.arange(gt, dtype=np.int64) * time_interval
-    ph = np.arange(gh, dtype=np.int64) + start
-    pw = np.arange(gw, dtype=np.int64) + start
-    tt, hh, ww = np.meshgrid(pt, ph, pw, indexing="ij")
-    ids = np.stack([tt, hh, ww], axis=0).reshape(3, -1)
-    ids[0] += start
-    return ids
-
+# ---------------------------------------------------------------------------
+# The builder
+# ---------------------------------------------------------------------------
 
 def get_rope_index(mm_token_type, image_grid_thw=None, video_grid_thw=None,
                    attention_mask=None, merge: int = 2):
     """3-axis positions [3, B, L] and rope_deltas [B] (int64).
 
     ``mm_token_type`` is [B, L] with 0 text, 1 image, 2 video.  Grids are
-    [n, 3] (t, h, w) before spatial merging; one image iterator and one video
-    iterator are shared by the whole batch and consumed in sample order, then
-    in order of appearance.  Padding (attention_mask 0) is removed before the
-    segments are formed and keeps position 0.
+    [n, 3] (t, h, w) before spatial merging.  The walkthrough's steps, in its
+    order:
+
+    1. the grid queues (``grid_queues``): one image queue and one video-slice
+       queue for the whole batch, taken in sample order, then in order of
+       appearance;
+    2. per sample, the tokens the mask keeps (all of them without a mask),
+       cut into runs of one type (``type_runs``);
+    3. a running rotary position, 0 at the sample's first kept token: a text
+       run of n tokens takes p, p + 1, ..., p + n - 1 on all three axes and
+       moves p on by n; a visual run takes the next grid of its queue, its
+       slots take ``visual_run_positions(p, grid)``, and p moves on by the
+       longer merged side max(h, w) // merge, not by the slot count;
+    4. (the flattening of the slot grid, inside ``visual_run_positions``);
+    5. the kept tokens' positions are written back to their slots; slots the
+       mask drops keep 0;
+    6. rope_delta = largest position + 1 - number of kept tokens.
     """
     types = np.asarray(mm_token_type, dtype=np.int64)
     if types.ndim != 2:
         raise PositionError("mm_token_type must be [B, L]")
     B, L = types.shape
-    mask = None if attention_mask is None else np.asarray(attention_mask).astype(bool)
-    videos = expand_video_grids(video_grid_thw)
-    images = (np.zeros((0, 3), dtype=np.int64) if image_grid_thw is None
-              else np.asarray(image_grid_thw, dtype=np.int64).reshape(-1, 3))
-    iters = {IMAGE: iter(images), VIDEO: iter(videos)}
+    keep = (np.ones((B, L), dtype=bool) if attention_mask is None
+            else np.asarray(attention_mask).astype(bool))
+    queues = dict(zip((IMAGE, VIDEO), grid_queues(image_grid_thw, video_grid_thw)))
+    taken = {IMAGE: 0, VIDEO: 0}
     position_ids = np.zeros((3, B, L), dtype=np.int64)
     deltas = np.zeros(B, dtype=np.int64)
     for b in range(B):
-        row = types[b] if mask is None else types[b][mask[b]]
-        groups = []
-        for key, grp in itertools.groupby(enumerate(row.tolist()), lambda x: x[1]):
-            grp = list(grp)
-            groups.append((key, grp[0][0], grp[-1][0] + 1))
-        current = 0
-        parts = []
-        for kind, s, e in groups:
-            if kind == TEXT:
-                n = e - s
-                parts.append(np.broadcast_to(np.arange(n, dtype=np.int64) + current, (3, n)))
-                current += n
-            elif kind in (IMAGE, VIDEO):
-                try:
-                    grid = next(iters[kind])
-                except StopIteration:
-                    raise PositionError(f"sample {b}: no grid left for a type-{kind} segment")
-                ids = vision_segment_ids(current, grid, merge)
-                if ids.shape[1] != e - s:
-                    raise PositionError(f"sample {b}: segment of {e - s} tokens, grid {grid} "
+        slots = np.nonzero(keep[b])[0]               # kept slots, in order
+        kept_types = types[b, slots].tolist()
+        pos = np.zeros((3, len(slots)), dtype=np.int64)
+        p = 0
+        for ty, first, end in type_runs(kept_types):
+            if ty == TEXT:
+                pos[:, first:end] = p + np.arange(end - first, dtype=np.int64)
+                p += end - first
+            elif ty in (IMAGE, VIDEO):
+                if taken[ty] >= len(queues[ty]):
+                    raise PositionError(f"sample {b}: no grid left for a type-{ty} run")
+                grid = queues[ty][taken[ty]]
+                taken[ty] += 1
+                ids = visual_run_positions(p, grid, merge)
+                if ids.shape[1] != end - first:
+                    raise PositionError(f"sample {b}: run of {end - first} tokens, grid {grid} "
                                         f"has {ids.shape[1]} slots")
-                parts.append(ids)
-                current += max(int(grid[1]), int(grid[2])) // merge
+                pos[:, first:end] = ids
+                p += max(grid[1], grid[2]) // merge
             else:
-                raise PositionError(f"sample {b}: unknown token type {kind}")
-        if not parts:
-            deltas[b] = 0
-            continue
-        llm = np.concatenate(parts, axis=1)
-        if mask is None:
-            position_ids[:, b] = llm
-        else:
-            position_ids[:, b, mask[b]] = llm
-        deltas[b] = int(llm.max()) + 1 - llm.shape[1]
+                raise PositionError(f"sample {b}: unknown token type {ty}")
+        position_ids[:, b, slots] = pos
+        deltas[b] = int(pos.max()) + 1 - len(slots) if len(slots) else 0
     return position_ids, deltas
 
 

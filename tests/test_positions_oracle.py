@@ -166,12 +166,12 @@ def test_errors():
 # Planted mistakes
 # ---------------------------------------------------------------------------
 
-_ORIG_SEG = P.vision_segment_ids
+_ORIG_SEG = P.visual_run_positions
 _ORIG_GRI = P.get_rope_index
 
 
-def _mut_height_fastest(start, grid_thw, merge, temporal_merge=1, time_interval=1):
-    ids = _ORIG_SEG(start, grid_thw, merge, temporal_merge, time_interval)
+def _mut_height_fastest(start, grid_thw, merge):
+    ids = _ORIG_SEG(start, grid_thw, merge)
     t, h, w = (int(v) for v in grid_thw)
     gh, gw = h // merge, w // merge
     perm = np.arange(gh * gw).reshape(gh, gw).T.reshape(-1)
@@ -223,7 +223,7 @@ def _mut_no_mask_filter(mm_token_type, image_grid_thw=None, video_grid_thw=None,
 
 
 MUTATIONS = [
-    ("vision_segment_ids", _mut_height_fastest, check_printed_table),
+    ("visual_run_positions", _mut_height_fastest, check_printed_table),
     ("get_rope_index", _mut_advance_by_token_count, check_printed_table),
     ("get_rope_index", _mut_iterator_per_sample, check_video_slices_and_shared_iterators),
     ("get_rope_index", _mut_no_mask_filter, check_text_only_and_padding),
