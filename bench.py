@@ -55,36 +55,54 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor peak
 DEFAULT_WORKLOAD = "omni_text_prefill"
-KERNEL_SOURCES = ["vlm_multimodal_rotary_amd/csrc/mrope_kernels.hip",
-                  "vlm_multimodal_rotary_amd/csrc/mrope_api.cpp",
-                  "vlm_multimodal_rotary_amd/csrc/mrope_internal.h"]
+# Device sources of each rotary kernel: a traffic record taken on a kernel
+# holds only while these files are unchanged.
+_CSRC = "vlm_multimodal_rotary_amd/csrc/"
+KERNEL_SOURCES = {
+    "qk_pipe_kernel": [_CSRC + "mrope_pipe.hip", _CSRC + "mrope_device.h",
+                       _CSRC + "mrope_internal.h"],
+    "qk_kernel": [_CSRC + "mrope_kernels.hip", _CSRC + "mrope_device.h",
+                  _CSRC + "mrope_internal.h"],
+}
+KERNEL_SOURCES["flat_kernel"] = KERNEL_SOURCES["stage_kernel"] = KERNEL_SOURCES["qk_kernel"]
 # The machine's CPU share for one GPU: oracle worker pools stay within it
 # whatever the affinity mask shows.
 HOST_CORE_SHARE = 16
 ORACLE_CHUNK = 1024           # tokens per oracle call (bounds its memory)
 
 
-def kernel_source_hash() -> str:
+def kernel_family(name: str) -> str:
+    """The rotary kernel a kernel name (or mrope_last_kernel's answer) names."""
+    for k in ("qk_pipe_kernel", "qk_kernel", "flat_kernel", "stage_kernel"):
+        if k in name:
+            return k
+    return ""
+
+
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """(bytes per launch, source note) from the committed rocprofv3 counter
-    summary, or (None, reason) when there is none or the kernel sources
-    changed since it was taken.  The counters (FETCH_SIZE + WRITE_SIZE) count
-    bytes between L2 and the memory fabric; lines served by the MALL are
-    included."""
+    summary, or (None, reason) when there is none, it was taken on another
+    kernel than `kernel` (the one this run launched), or that kernel's sources
+    changed since.  The counters (FETCH_SIZE + WRITE_SIZE) count bytes between
+    L2 and the memory fabric; lines served by the MALL are included."""
     rel = os.path.join("profiles", f"traffic_{workload}.json")
     path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None, f"no {rel}"
     with open(path) as f:
         rec = json.load(f)
-    h = kernel_source_hash()
+    fam = kernel_family(kernel)
+    if not fam or rec.get("kernel_family") != fam:
+        return None, f"{rel} was taken on another kernel"
+    h = kernel_source_hash(fam)
     if rec.get("kernel_source_hash") != h:
         return None, f"{rel} was taken on other kernel sources"
     return rec.get("hbm_bytes_per_launch"), (
@@ -316,18 +334,10 @@ def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
             rows.extend(csv.DictReader(f))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
 
-    def family(name):
-        if "stream_copy_kernel" in name:
-            return "copy"
-        for k in ("qk_kernel", "qk_pipe_kernel", "flat_kernel", "stage_kernel"):
-            if k in name:
-                return "kernel"
-        return None
-
     seq = {"copy": [], "kernel": []}
     names = {}
     for r in rows:
-        fam = family(r["Kernel_Name"])
+        fam = _family(r["Kernel_Name"])
         if fam is None:
             continue
         seq[fam].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -347,6 +357,82 @@ def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
         if pos[fam] != len(seq[fam]):
             out.setdefault("unmatched", {})[fam] = len(seq[fam]) - pos[fam]
     return out
+
+
+def _pmc_rows(pmc_dir: str):
+    paths = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *counter_collection.csv under {pmc_dir}")
+    rows = []
+    for p in paths:
+        with open(p) as f:
+            rows.extend(csv.DictReader(f))
+    return rows, paths
+
+
+def _family(name: str):
+    if "stream_copy_kernel" in name:
+        return "copy"
+    return "kernel" if kernel_family(name) else None
+
+
+def summarize_counters(pmc_dir: str) -> dict:
+    """Per kernel family (the rotary kernel, the copy kernel) and counter of a
+    rocprofv3 --pmc run of bench.py: the median over the family's dispatches
+    of the counter's value per dispatch (rows of one dispatch summed)."""
+    rows, paths = _pmc_rows(pmc_dir)
+    per = {}
+    names = {}
+    for r in rows:
+        fam = _family(r["Kernel_Name"])
+        if fam is None:
+            continue
+        key = (fam, r["Counter_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        names.setdefault(fam, r["Kernel_Name"])
+    out = {"files": [os.path.relpath(p, pmc_dir) for p in paths], "families": {}}
+    by = {}
+    for (fam, ctr, _), v in per.items():
+        by.setdefault((fam, ctr), []).append(v)
+    for (fam, ctr), vals in sorted(by.items()):
+        vals.sort()
+        rec = out["families"].setdefault(fam, {"kernel": names[fam]})
+        rec[ctr] = {"median": vals[len(vals) // 2], "dispatches": len(vals)}
+    return out
+
+
+def traffic_record(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """HBM-side traffic of the rotary kernel from two rocprofv3 --pmc runs of
+    bench.py (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is
+    scaled by what it reads for the run's own copy phase, a plain copy of
+    known size (the q/k bytes read into as many written): scale = bytes /
+    (KiB * 1024)."""
+    import workloads as W
+    wl = W.WORKLOADS.get(workload) or W.VISION_QKV_WORKLOADS[workload]
+    if workload in W.WORKLOADS:
+        copy_bytes = 2 * wl.T * (wl.hq + wl.hk) * wl.D * wl.elem_bytes // 2
+    else:
+        copy_bytes = wl.T * 3 * wl.heads * wl.D * (2 if wl.dtype == "bf16" else 4)
+    copy_bytes = (copy_bytes + 15) // 16 * 16
+    f = summarize_counters(fetch_dir)["families"]
+    w = summarize_counters(write_dir)["families"]
+    kf, cf = f["kernel"]["FETCH_SIZE"]["median"], f["copy"]["FETCH_SIZE"]["median"]
+    kw, cw = w["kernel"]["WRITE_SIZE"]["median"], w["copy"]["WRITE_SIZE"]["median"]
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    rd, wr = kf * 1024 * fs, kw * 1024 * ws
+    alg = wl.algorithmic_bytes()
+    fam = kernel_family(f["kernel"]["kernel"])
+    return {"kernel": f["kernel"]["kernel"], "workload": workload, "kernel_family": fam,
+            "kernel_sources": KERNEL_SOURCES[fam], "kernel_source_hash": kernel_source_hash(fam),
+            "kernel_fetch_kib_per_dispatch": kf, "kernel_write_kib_per_dispatch": kw,
+            "kernel_dispatches": [f["kernel"]["FETCH_SIZE"]["dispatches"],
+                                  w["kernel"]["WRITE_SIZE"]["dispatches"]],
+            "copy_bytes": copy_bytes, "copy_kernel": f["copy"]["kernel"],
+            "copy_fetch_kib_per_dispatch": cf, "copy_write_kib_per_dispatch": cw,
+            "fetch_scale": fs, "write_scale": ws,
+            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+            "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": (rd + wr) / alg}
 
 
 # ---------------------------------------------------------------------------
@@ -489,7 +575,7 @@ def bench_vision_qkv(args):
     gbps = rec["rotating"]["gbps"]
     traffic, traffic_note = ((None, "not taken for this precision or the cache")
                              if args.precision != "exact" or args.cs_cache
-                             else measured_traffic(wl.name))
+                             else measured_traffic(wl.name, kernel))
     line = {
         "metric": "vision patches/s, packed qkv to rotated head-major planes (mrope_vision_qkv)",
         "value": n / (ms * 1e-3), "unit": "patches/s", "n_gpus": 1, "steps": args.steps,
@@ -635,10 +721,22 @@ def main():
     ap.add_argument("--trace-summary", default="",
                     help="print per-phase kernel durations of a rocprofv3 kernel trace "
                          "directory of a bench.py run with the same --steps/--warmup")
+    ap.add_argument("--pmc-summary", default="",
+                    help="print per-kernel medians of every counter of a rocprofv3 --pmc "
+                         "directory of a bench.py run")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic record of --workload from a FETCH_SIZE and a "
+                         "WRITE_SIZE rocprofv3 --pmc run of bench.py")
     args = ap.parse_args()
 
     if args.trace_summary:
         print(json.dumps(summarize_trace(args.trace_summary, args.warmup, args.steps), indent=1))
+        return
+    if args.pmc_summary:
+        print(json.dumps(summarize_counters(args.pmc_summary), indent=1))
+        return
+    if args.traffic_record:
+        print(json.dumps(traffic_record(*args.traffic_record, args.workload), indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path has no exchange step, and "
@@ -713,7 +811,7 @@ def main():
     achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9
     traffic, traffic_note = ((None, "not taken for this precision or the cache")
                              if args.precision != "exact" or args.cs_cache
-                             else measured_traffic(wl.name))
+                             else measured_traffic(wl.name, kernel))
     config = {"workload": wl.name, "T": wl.T, "hq": wl.hq, "hk": wl.hk, "D": wl.D,
               "rotary_dim": wl.rotary_dim, "theta": wl.theta, "layout": wl.layout,
               "section": list(wl.section), "rmsnorm": wl.norm, "precision": args.precision}

@@ -21,29 +21,34 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
-def test_traffic_record_follows_the_kernel_source(tmp_path, monkeypatch):
-    current = bench.kernel_source_hash()
-    assert len(current) == 16
-    rec = {"kernel_source_hash": current, "hbm_bytes_per_launch": 123.0}
+def test_traffic_record_follows_the_kernel_and_its_sources(tmp_path, monkeypatch):
+    current = bench.kernel_source_hash("qk_pipe_kernel")
+    assert len(current) == 16 and current != bench.kernel_source_hash("qk_kernel")
+    rec = {"kernel_family": "qk_pipe_kernel", "kernel_source_hash": current,
+           "hbm_bytes_per_launch": 123.0}
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "traffic_some_workload.json").write_text(json.dumps(rec))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: current)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda fam: current)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    val, note = bench.measured_traffic("some_workload")
+    val, note = bench.measured_traffic("some_workload", "qk_pipe_kernel (rmsnorm_mrope_qk)")
     assert val == 123.0 and current in note and "L2<->fabric" in note
+    # another kernel launched this run: the record does not apply
+    assert bench.measured_traffic("some_workload", "qk_kernel")[0] is None
     rec["kernel_source_hash"] = "0" * 16            # counters taken on other sources
     (prof / "traffic_some_workload.json").write_text(json.dumps(rec))
-    assert bench.measured_traffic("some_workload")[0] is None
-    assert bench.measured_traffic("no_record")[0] is None
+    assert bench.measured_traffic("some_workload", "qk_pipe_kernel")[0] is None
+    assert bench.measured_traffic("no_record", "qk_pipe_kernel")[0] is None
 
 
-def test_committed_traffic_records_name_their_commands():
+def test_committed_traffic_records_name_their_commands_and_kernel():
     for name in os.listdir(os.path.join(ROOT, "profiles")):
         if name.startswith("traffic_") and name.endswith(".json"):
             rec = json.load(open(os.path.join(ROOT, "profiles", name)))
-            assert rec["commands"] and all("rocprofv3 --pmc" in c for c in rec["commands"])
+            assert rec["commands"] and all("rocprofv3 --pmc" in c or "bench.py" in c
+                                           for c in rec["commands"])
             assert len(rec["kernel_source_hash"]) == 16
+            assert rec["kernel_family"] in bench.KERNEL_SOURCES
 
 
 @pytest.mark.parametrize("procs", [1, 2])
@@ -120,3 +125,32 @@ def test_warmup_and_steps_are_exact(monkeypatch):
     ms, _ = bench.time_region(fns, 4, 5)
     assert calls == [0, 1, 2, 0, "ev", 0, 1, 2, 0, 1, "ev"]
     assert ms == 1.0 / 5
+
+
+def test_traffic_record_scales_each_counter_by_the_runs_copy(tmp_path):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the rotary kernel,
+    scaled by what the same counter reads for the run's own copy phase."""
+    wl = W.WORKLOADS["omni_text_prefill"]
+    copy_bytes = wl.T * (wl.hq + wl.hk) * wl.D * 2
+    kern = "void mrope::(anonymous namespace)::qk_pipe_kernel<true, 8, true, 8, 0, 2>(...)"
+    copy = "void mrope::(anonymous namespace)::stream_copy_kernel(char const*, char*, ...)"
+
+    def write(d, ctr, kern_kib, copy_kib):
+        d.mkdir(parents=True)
+        with open(d / "x_counter_collection.csv", "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            i = 0
+            for name, kib in ((copy, copy_kib), (kern, kern_kib)):
+                for _ in range(5):
+                    i += 1
+                    f.write(f'{i},"{name}",{ctr},{kib}\n')
+            f.write(f'{i + 1},"__amd_rocclr_fillBufferAligned",{ctr},7\n')
+    # fetch counter reads half the bytes (scale 2), write counter reads them all
+    write(tmp_path / "f", "FETCH_SIZE", copy_bytes / 2048 * 1.01, copy_bytes / 2048)
+    write(tmp_path / "w", "WRITE_SIZE", copy_bytes / 1024, copy_bytes / 1024)
+    rec = bench.traffic_record(str(tmp_path / "f"), str(tmp_path / "w"), "omni_text_prefill")
+    assert rec["kernel_family"] == "qk_pipe_kernel" and rec["kernel_dispatches"] == [5, 5]
+    assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
+    assert abs(rec["hbm_read_bytes_per_launch"] - 1.01 * copy_bytes) < 1
+    assert abs(rec["hbm_write_bytes_per_launch"] - copy_bytes) < 1
+    assert rec["algorithmic_bytes_per_launch"] == wl.algorithmic_bytes()

@@ -20,7 +20,10 @@
 //    so that the sincos overlaps their memory latency.
 //  * flat_kernel (rows that are not whole 256-byte line pairs) and
 //    stage_kernel (bf16 per-head planes, through LDS) serve the positions
-//    path without RMSNorm; the host picks the kernel by shape.
+//    path without RMSNorm, and qk_pipe_kernel (mrope_pipe.hip) the positions
+//    path of launches of 2048 tokens or more with 16-byte chunks; the host
+//    picks the kernel by shape.  Helpers shared with mrope_pipe.hip are in
+//    mrope_device.h.
 //  * The RMS reduction of a row runs over its lpr lanes with DPP
 //    (quad_perm, row_half_mirror, row_mirror) on float64 partial sums.
 //  * Numerics follow the pages' conventions with the rounding points made
@@ -33,7 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "mrope_internal.h"
+#include "mrope_device.h"
 
 // Row-steps whose loads are issued together, per lane, by element type.
 #ifndef MROPE_ROWS_IN_FLIGHT_BF16
@@ -47,24 +50,6 @@
 #ifndef MROPE_ROWS_IN_FLIGHT_NARROW
 #define MROPE_ROWS_IN_FLIGHT_NARROW 2
 #endif
-// Non-temporal (streaming) hint on the row stores of qk_kernel and
-// stage_kernel, by element type (flat_kernel chooses by output layout).
-#ifndef MROPE_NT_STORES_BF16
-#define MROPE_NT_STORES_BF16 1
-#endif
-#ifndef MROPE_NT_STORES_F32
-#define MROPE_NT_STORES_F32 0
-#endif
-// Resident wavefronts per SIMD the pipelined kernel is compiled for, with
-// and without RMSNorm (its registers then fit 512 / this many).  Measured on
-// the 32 + 4 head bf16 prefill with inputs the memory-side cache does not
-// hold: 3 waves 105.2 us; 4 waves spill (135 us).
-#ifndef MROPE_PIPE_MIN_WAVES
-#define MROPE_PIPE_MIN_WAVES 3
-#endif
-#ifndef MROPE_PIPE_MIN_WAVES_NONORM
-#define MROPE_PIPE_MIN_WAVES_NONORM 4
-#endif
 // Wavefronts a launch aims to have in flight before it splits tiles.
 #ifndef MROPE_MIN_WAVES
 #define MROPE_MIN_WAVES 2048
@@ -74,273 +59,6 @@ namespace mrope {
 namespace {
 
 constexpr int64_t kMinWaves = MROPE_MIN_WAVES;
-constexpr int kLdsPerCu = 160 * 1024;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------
-// Chunk storage: V elements of 2 (bf16) or 4 (fp32) bytes, as 32-bit words.
-// ---------------------------------------------------------------------------
-
-template <int CB>
-struct Words {
-  static constexpr int N = CB >= 4 ? CB / 4 : 1;
-  uint32_t w[N];
-};
-
-template <int CB>
-__device__ __forceinline__ void load_words(const char* p, Words<CB>& r) {
-  if constexpr (CB == 16) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (CB == 8) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else if constexpr (CB == 4) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else {
-    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
-  }
-}
-
-template <int CB>
-__device__ __forceinline__ void store_words(char* p, const Words<CB>& r) {
-  if constexpr (CB == 16) {
-    u32x4_t v = {r.w[0], r.w[1], r.w[2], r.w[3]};
-    *reinterpret_cast<u32x4_t*>(p) = v;
-  } else if constexpr (CB == 8) {
-    u32x2_t v = {r.w[0], r.w[1]};
-    *reinterpret_cast<u32x2_t*>(p) = v;
-  } else if constexpr (CB == 4) {
-    *reinterpret_cast<uint32_t*>(p) = r.w[0];
-  } else {
-    *reinterpret_cast<uint16_t*>(p) = (uint16_t)r.w[0];
-  }
-}
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-// Round two binary32 values to bfloat16 (nearest even, v_cvt_pk_bf16_f32) and
-// return them packed, first value in the low half.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-// Round a binary32 value to bfloat16, kept as binary32: converting the pair
-// (0, x) puts bf16(x) in the high half over a zero low half, which is the
-// binary32 pattern of bf16(x) -- one v_cvt_pk_bf16_f32, no unpacking.
-__device__ __forceinline__ float round_bf16(float x) {
-  return __builtin_bit_cast(float, pack_bf16(0.0f, x));
-}
-
-template <bool BF16, int V>
-__device__ __forceinline__ void unpack(const Words<(BF16 ? 2 : 4) * V>& r, float (&x)[V]) {
-  if constexpr (BF16) {
-    if constexpr (V == 1) {
-      x[0] = bf_lo(r.w[0]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        x[2 * i] = bf_lo(r.w[i]);
-        x[2 * i + 1] = bf_hi(r.w[i]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < V; ++i) x[i] = __builtin_bit_cast(float, r.w[i]);
-  }
-}
-
-template <bool BF16, int V>
-__device__ __forceinline__ void pack(const float (&x)[V], Words<(BF16 ? 2 : 4) * V>& r) {
-  if constexpr (BF16) {
-    if constexpr (V == 1) {
-      r.w[0] = pack_bf16(x[0], 0.0f) & 0xFFFFu;
-    } else {
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) r.w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < V; ++i) r.w[i] = __builtin_bit_cast(uint32_t, x[i]);
-  }
-}
-
-// Round the 2V values of a lane (two chunks) to bfloat16, kept as binary32.
-template <int V>
-__device__ __forceinline__ void round_bf16_chunks(float (&a)[V], float (&b)[V]) {
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    a[i] = round_bf16(a[i]);
-    b[i] = round_bf16(b[i]);
-  }
-}
-
-// The rotation as tensor operations on one lane's pairs (x1 = a[i],
-// x2 = b[i]): out1 = x1*c - x2*s, out2 = x2*c + x1*s with every product and
-// sum rounded to binary32 and no product fused into a sum.  CAST rounds
-// cos/sin and both products to bfloat16 as well (bf16 tensor arithmetic
-// with cos/sin cast to the tensor's dtype); the last rounding to the stored
-// dtype happens when the chunk is packed.
-template <bool CAST, int V>
-__device__ __forceinline__ void rotate_tensor_ops(float (&a)[V], float (&b)[V],
-                                                  const double (&ca)[V], const double (&sa)[V],
-                                                  const double (&cb)[V], const double (&sb)[V]) {
-#pragma clang fp contract(off)
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    float c1 = (float)ca[i], s1 = (float)sa[i];
-    float c2 = (float)cb[i], s2 = (float)sb[i];
-    if constexpr (CAST) {
-      c1 = round_bf16(c1);
-      s1 = round_bf16(s1);
-      c2 = round_bf16(c2);
-      s2 = round_bf16(s2);
-    }
-    float p1 = a[i] * c1;
-    float p2 = b[i] * s1;
-    float p3 = b[i] * c2;
-    float p4 = a[i] * s2;
-    if constexpr (CAST) {
-      p1 = round_bf16(p1);
-      p2 = round_bf16(p2);
-      p3 = round_bf16(p3);
-      p4 = round_bf16(p4);
-    }
-    a[i] = p1 - p2;
-    b[i] = p3 + p4;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Cross-lane sum of a float64 over the lpr lanes of a row.
-// ---------------------------------------------------------------------------
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  int lo = (int)(uint32_t)u;
-  int hi = (int)(uint32_t)(u >> 32);
-  // Every lane of these patterns reads an active lane, so no fill value is
-  // needed (bound_ctrl set).
-  lo = __builtin_amdgcn_mov_dpp(lo, CTRL, 0xF, 0xF, true);
-  hi = __builtin_amdgcn_mov_dpp(hi, CTRL, 0xF, 0xF, true);
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
-// All lanes of the wavefront must be active.  Each step adds the partner's
-// value, which is commutative, so every lane of a group ends with the same sum.
-__device__ __forceinline__ double group_sum(double v, int lpr) {
-  if ((lpr & (lpr - 1)) == 0) {
-    if (lpr >= 2) v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
-    if (lpr >= 4) v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
-    if (lpr >= 8) v += dpp_f64<0x141>(v);  // row_half_mirror: other quad of 8
-    if (lpr >= 16) v += dpp_f64<0x140>(v); // row_mirror: other half of 16
-    if (lpr >= 32) v += __shfl_xor(v, 16);
-    if (lpr >= 64) v += __shfl_xor(v, 32);
-    return v;
-  }
-  // Rows whose lane count is not a power of two: every lane adds the group's
-  // partials in lane order.
-  const int lane = threadIdx.x & (kWaveSize - 1);
-  const int base = (lane / lpr) * lpr;
-  double s = 0.0;
-  for (int i = 0; i < lpr; ++i) s += __shfl(v, (base + i) & (kWaveSize - 1));
-  return s;
-}
-
-// fl32 of 1/sqrt(m): hardware estimate refined by two Newton steps in double;
-// the result is within a few double ulps of the exact value before rounding.
-__device__ __forceinline__ float rsqrt_to_f32(double m) {
-  double y = __builtin_amdgcn_rsq(m);
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const double t = m * y;
-    const double e = __builtin_fma(-t, y, 1.0);      // 1 - m y^2
-    y = __builtin_fma(0.5 * y, e, y);
-  }
-  return (float)y;
-}
-
-// cos/sin of the binary32 angle float(p) * inv, in double, rounded once.
-__device__ __forceinline__ void angle_cos_sin(int32_t pos, float inv, float& c, float& s) {
-  const float a = __fmul_rn((float)pos, inv);
-  double sd, cd;
-  sincos((double)a, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
-}
-
-// ---------------------------------------------------------------------------
-// The q/k kernel.
-// ---------------------------------------------------------------------------
-
-// Cross-lane float64 sum over the LPR lanes of a row (LPR a power of two
-// known at compile time), or over p.lpr lanes when LPR == 0.
-template <int LPR>
-__device__ __forceinline__ double row_sum(double v, int lpr) {
-  if constexpr (LPR == 0) {
-    return group_sum(v, lpr);
-  } else {
-    if constexpr (LPR >= 2) v += dpp_f64<0xB1>(v);
-    if constexpr (LPR >= 4) v += dpp_f64<0x4E>(v);
-    if constexpr (LPR >= 8) v += dpp_f64<0x141>(v);
-    if constexpr (LPR >= 16) v += dpp_f64<0x140>(v);
-    if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
-    if constexpr (LPR >= 64) v += __shfl_xor(v, 32);
-    return v;
-  }
-}
-
-// Raw buffer access.  A descriptor covers one tile of one tensor; an offset
-// past its range makes a load return zeros and drops a store in hardware, so
-// masked rows issue the same instructions as live ones with no branch around
-// them (which also keeps the compiler's memory-counter waits exact).
-constexpr int kBufferWord3 = 0x00020000;    // gfx9 raw buffer, dword data
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
-}
-
-template <int CB>
-__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t rs, uint32_t off, Words<CB>& r) {
-  if constexpr (CB == 16) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (CB == 8) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else if constexpr (CB == 4) {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-  } else {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
-  }
-}
-
-// NT: non-temporal (streaming) store, aux 2.  The default is measured per
-// dtype for qk_kernel and stage_kernel; flat_kernel chooses by output layout.
-template <bool BF16, int CB, bool NT = (BF16 ? MROPE_NT_STORES_BF16 : MROPE_NT_STORES_F32)>
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, uint32_t off,
-                                          const Words<CB>& r) {
-  constexpr int aux = NT ? 2 : 0;
-  if constexpr (CB == 16) {
-    const u32x4_t v = {r.w[0], r.w[1], r.w[2], r.w[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, aux);
-  } else if constexpr (CB == 8) {
-    const u32x2_t v = {r.w[0], r.w[1]};
-    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, aux);
-  } else if constexpr (CB == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, aux);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)r.w[0], rs, off, 0, aux);
-  }
-}
 
 // Per-tensor state of one tile while its rows are processed.
 template <int CB>
@@ -840,351 +558,6 @@ qk_kernel(const QKParams p, const ColTable tab) {
                                                  col_a, wa, wb, lc, ls, t0);
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// The pipelined q/k kernel: cos/sin from positions, one token per wavefront,
-// launches of at least one wavefront per token over the whole chip.  The
-// token's row-steps -- q's, then k's, then a packed qkv's copied v -- form one
-// stream, and the loads of step j + P are issued before step j is finished:
-// every wavefront keeps P row-steps of loads in flight while it computes.  (In
-// qk_kernel a wavefront has loads in flight only while it waits for them, so
-// the chip's bytes in flight drop by the share of time its wavefronts spend
-// on the norm and the rotation.)  Every row of the wavefront belongs to one
-// token, so a lane's cos/sin are the same for all its rows: they are formed
-// once (one sincos per lane, exchanged through LDS) and held in registers as
-// doubles, which takes the per-step LDS reads and conversions out of the
-// loop.  The weights, the token's positions and the first P steps are loaded
-// before the sincos.  Every load and store is issued unconditionally -- a
-// masked row or a step past the end uses an offset past its buffer -- so the
-// compiler's waits on the in-order vector memory counter are exact.  The
-// arithmetic per element is qk_kernel's, so the results are bit-identical.
-// ---------------------------------------------------------------------------
-
-template <int CB>
-struct PipeStep {
-  Words<CB> ra, rb;              // the lane's two chunks of its row
-  uint32_t you;                  // byte offset of the row's output, or out of range
-  int slot;                      // tensor of the step (wave-uniform); kSlots past the end
-};
-
-// Position of a wavefront in its step stream.  Wave-uniform: the tensor, the
-// steps left in it and its walking constants; per lane: the next row's head
-// and byte offsets.
-struct PipeCursor {
-  int slot, left, r0, H, dr;
-  uint32_t xinc, yinc;
-  int h;
-  uint32_t xo, yo;
-};
-
-// Moves the cursor to the first row of the first tensor >= from that has
-// steps (n0, n1, n2 for q, k, v), or past the end.  The tensor's fields are
-// picked by constant index: a dynamic index into the kernel-argument struct
-// would copy it to scratch memory.  One token: row r is head r, at byte
-// offset r * D * es of the input and r * head stride of the output.
-__device__ __forceinline__ void pipe_enter(PipeCursor& c, const QKParams& p, int from, int n0,
-                                           int n1, int n2, int grp, int rpw, int es) {
-  int s = from;
-  if (s == 0 && n0 == 0) s = 1;
-  if (s == 1 && n1 == 0) s = 2;
-  if (s == 2 && n2 == 0) s = kSlots;
-  c.slot = __builtin_amdgcn_readfirstlane(s);
-  if (c.slot >= kSlots) return;
-  const int ss = c.slot;
-  const int64_t yhs = ss == 0 ? p.y_hs[0] : (ss == 1 ? p.y_hs[1] : p.y_hs[2]);
-  c.H = ss == 0 ? p.heads[0] : (ss == 1 ? p.heads[1] : p.heads[2]);
-  c.left = ss == 0 ? n0 : (ss == 1 ? n1 : n2);
-  c.r0 = 0;
-  c.h = grp;
-  c.xo = (uint32_t)((int64_t)grp * p.D * es);
-  c.yo = (uint32_t)((int64_t)grp * yhs * es);
-  c.xinc = (uint32_t)((int64_t)rpw * p.D * es);
-  c.yinc = (uint32_t)((int64_t)rpw * yhs * es);
-}
-
-// Issues the loads of the cursor's step into b (masked rows and steps past the
-// end load from out of range) and advances the cursor.
-template <int CB>
-__device__ __forceinline__ void pipe_issue(PipeCursor& c, PipeStep<CB>& b, const QKParams& p,
-                                           __amdgpu_buffer_rsrc_t rx0, __amdgpu_buffer_rsrc_t rx1,
-                                           __amdgpu_buffer_rsrc_t rx2, int n0, int n1, int n2,
-                                           int grp, int rpw, bool lane_on, uint32_t ca,
-                                           uint32_t cb, int es) {
-  const int s = c.slot;
-  const bool have = s < kSlots;
-  const bool ok = have && lane_on && c.h < c.H;
-  b.slot = s;
-  b.you = ok ? c.yo : kOutOfRange;
-  const uint32_t xoff = ok ? c.xo : kOutOfRange;
-  const __amdgpu_buffer_rsrc_t rx = s == 0 ? rx0 : (s == 1 ? rx1 : rx2);
-  buf_load<CB>(rx, xoff + ca, b.ra);
-  buf_load<CB>(rx, xoff + cb, b.rb);
-  if (have) {
-    c.xo += c.xinc;
-    c.yo += c.yinc;
-    c.h += rpw;
-    if (--c.left == 0) pipe_enter(c, p, s + 1, n0, n1, n2, grp, rpw, es);
-  }
-}
-
-// RMSNorm (NORM) and rotation (rot) of one lane's two chunks: a at column
-// col_a, b at its split-half partner (or a second pass-through chunk), with
-// the cos/sin of columns col_a.. as doubles.  The arithmetic of finish_steps,
-// element for element.
-template <bool BF16, int V, bool NORM, int LPR, int PREC>
-__device__ __forceinline__ void norm_rotate(float (&a)[V], float (&b)[V], const QKParams& p,
-                                            int lpr, bool rot, const float (&wa)[V],
-                                            const float (&wb)[V], const double (&c_)[V],
-                                            const double (&s_)[V]) {
-  if constexpr (NORM) {
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      ss = __builtin_fma((double)a[i], (double)a[i], ss);
-      ss = __builtin_fma((double)b[i], (double)b[i], ss);
-    }
-    ss = row_sum<LPR>(ss, lpr);
-    const float rs = rsqrt_to_f32(ss * p.inv_d + (double)p.eps);
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      a[i] = a[i] * rs;
-      b[i] = b[i] * rs;
-    }
-    if constexpr (BF16) round_bf16_chunks<V>(a, b);
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      a[i] = a[i] * wa[i];
-      b[i] = b[i] * wb[i];
-    }
-    if constexpr (BF16) round_bf16_chunks<V>(a, b);
-  }
-  if (rot) {
-    if constexpr (PREC == MROPE_PRECISION_EXACT) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const double y1 = a[i];
-        const double y2 = b[i];
-        const double o1 = __builtin_fma(y1, c_[i], -(y2 * s_[i]));
-        const double o2 = __builtin_fma(y2, c_[i], y1 * s_[i]);
-        a[i] = (float)o1;
-        b[i] = (float)o2;
-      }
-    } else {
-      rotate_tensor_ops<BF16 && PREC == MROPE_PRECISION_DTYPE, V>(a, b, c_, s_, c_, s_);
-    }
-  }
-}
-
-// Finishes a step: RMSNorm and rotation of q and k rows (v rows are copied)
-// and the two stores.  A step past the end (valid false) skips the
-// arithmetic; its stores, like those of masked rows, are out of range.
-template <bool BF16, int V, bool NORM, int LPR, int PREC>
-__device__ __forceinline__ void pipe_finish(const PipeStep<(BF16 ? 2 : 4) * V>& b, bool valid,
-                                            const QKParams& p, int lpr, bool rot, uint32_t ca,
-                                            uint32_t cb, const double (&c_)[V],
-                                            const double (&s_)[V], const float (&wqa)[V],
-                                            const float (&wqb)[V], const float (&wka)[V],
-                                            const float (&wkb)[V], __amdgpu_buffer_rsrc_t ry0,
-                                            __amdgpu_buffer_rsrc_t ry1,
-                                            __amdgpu_buffer_rsrc_t ry2) {
-  constexpr int CB = (BF16 ? 2 : 4) * V;
-  Words<CB> oa = b.ra, ob = b.rb;
-  if (valid && b.slot < 2) {
-    float a[V], c[V];
-    unpack<BF16, V>(b.ra, a);
-    unpack<BF16, V>(b.rb, c);
-    if (b.slot == 0)
-      norm_rotate<BF16, V, NORM, LPR, PREC>(a, c, p, lpr, rot, wqa, wqb, c_, s_);
-    else
-      norm_rotate<BF16, V, NORM, LPR, PREC>(a, c, p, lpr, rot, wka, wkb, c_, s_);
-    pack<BF16, V>(a, oa);
-    pack<BF16, V>(c, ob);
-  }
-  const __amdgpu_buffer_rsrc_t ry = b.slot == 0 ? ry0 : (b.slot == 1 ? ry1 : ry2);
-  buf_store<BF16, CB>(ry, b.you + ca, oa);
-  buf_store<BF16, CB>(ry, b.you + cb, ob);
-}
-
-template <bool BF16, int V, bool NORM, int LPR, int PREC, int P>
-__global__ void __launch_bounds__(kBlockThreads)
-__attribute__((amdgpu_waves_per_eu(NORM ? MROPE_PIPE_MIN_WAVES : MROPE_PIPE_MIN_WAVES_NONORM)))
-qk_pipe_kernel(const QKParams p, const ColTable tab) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int CB = ES * V;
-  extern __shared__ double lds[];
-  const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-  const int half = p.half;
-  float* lc = reinterpret_cast<float*>(lds) + wib * (2 * half);
-  float* ls = lc + half;
-
-  const int lpr = LPR > 0 ? LPR : p.lpr;
-  const int rpw = LPR > 0 ? kWaveSize / (LPR > 0 ? LPR : 1) : p.rpw;
-  const int grp = lane / lpr;
-  const int l = lane - grp * lpr;
-  const bool lane_on = grp < rpw;
-  const bool rot = l < p.lrot;
-  int col_a, col_b;
-  if (l < p.lrot) {
-    col_a = l * V;
-    col_b = half + l * V;
-  } else {
-    const int m = l - p.lrot;
-    const int npass = lpr - p.lrot;
-    col_a = p.rd + m * V;
-    col_b = p.rd + (npass + m) * V;
-  }
-  const uint32_t ca = (uint32_t)(col_a * ES);
-  const uint32_t cb = (uint32_t)(col_b * ES);
-
-  const int64_t t0 = (int64_t)blockIdx.x * kWavesPerBlock + wib;
-  if (t0 >= p.T) return;
-  // Row-steps of each tensor (wave-uniform scalars: no private arrays, so
-  // the buffer descriptors chosen from them stay in scalar registers).
-  const int n0 = (p.heads[0] + rpw - 1) / rpw;
-  const int n1 = (p.heads[1] + rpw - 1) / rpw;
-  const int n2 = (p.heads[2] + rpw - 1) / rpw;
-  const int N = n0 + n1 + n2;
-  if (N == 0) return;
-
-  // The token's rows of each tensor (32-bit byte offsets inside them).
-#define MROPE_X_RSRC(s)                                                          \
-  buffer_of(static_cast<const char*>(p.x[s]) + t0 * p.x_ts[s] * ES,              \
-            (uint32_t)((int64_t)p.heads[s] * p.D * ES))
-#define MROPE_Y_RSRC(s)                                                          \
-  buffer_of(static_cast<const char*>(p.y[s]) + t0 * p.y_ts[s] * ES,              \
-            p.heads[s] > 0 ? (uint32_t)(((int64_t)(p.heads[s] - 1) * p.y_hs[s] + p.D) * ES) : 0u)
-  const __amdgpu_buffer_rsrc_t rx0 = MROPE_X_RSRC(0), rx1 = MROPE_X_RSRC(1), rx2 = MROPE_X_RSRC(2);
-  const __amdgpu_buffer_rsrc_t ry0 = MROPE_Y_RSRC(0), ry1 = MROPE_Y_RSRC(1), ry2 = MROPE_Y_RSRC(2);
-#undef MROPE_X_RSRC
-#undef MROPE_Y_RSRC
-
-  // 1. RMSNorm weights of q and k (tiny, shared by every wavefront).
-  Words<CB> wq_a = {}, wq_b = {}, wk_a = {}, wk_b = {};
-  if constexpr (NORM) {
-    const __amdgpu_buffer_rsrc_t rq =
-        buffer_of(p.w[0], p.heads[0] > 0 ? (uint32_t)(p.D * ES) : 0u);
-    const __amdgpu_buffer_rsrc_t rk =
-        buffer_of(p.w[1], p.heads[1] > 0 ? (uint32_t)(p.D * ES) : 0u);
-    buf_load<CB>(rq, ca, wq_a);
-    buf_load<CB>(rq, cb, wq_b);
-    buf_load<CB>(rk, ca, wk_a);
-    buf_load<CB>(rk, cb, wk_b);
-  }
-
-  // 2. What the sincos of the token's first 2 x 64 columns need: positions
-  // (the axis from the fitted rule, no table load) and inv_freq.
-  constexpr int kPrePos = 2;
-  int32_t pos_pre[kPrePos];
-  float inv_pre[kPrePos];
-#pragma unroll
-  for (int m = 0; m < kPrePos; ++m) {
-    const int idx = lane + m * kWaveSize;
-    const int j = idx < half ? idx : 0;
-    int ax;
-    if (p.ax_mode == 0) ax = (j >= p.ax_a) + (j >= p.ax_b);
-    else if (p.ax_mode == 1) ax = (j % 3 == 1 && j < p.ax_a) ? 1 : (j % 3 == 2 && j < p.ax_b) ? 2 : 0;
-    else ax = tab.axis[j];
-    pos_pre[m] = p.pos[(int64_t)ax * p.pos_stride + t0];
-    inv_pre[m] = tab.inv[j];
-  }
-
-  // 3. The step stream, and the loads of its first P steps.
-  static_assert(P == 2 || P == 3, "pipeline depth 2 or 3");
-  PipeCursor cur;
-  pipe_enter(cur, p, 0, n0, n1, n2, grp, rpw, ES);
-#define MROPE_ISSUE(b) \
-  pipe_issue<CB>(cur, b, p, rx0, rx1, rx2, n0, n1, n2, grp, rpw, lane_on, ca, cb, ES)
-  // The step buffers rotate through the unrolled loop bodies below.
-  PipeStep<CB> b0, b1, b2, b3;
-  MROPE_ISSUE(b0);
-  MROPE_ISSUE(b1);
-  if constexpr (P == 3) MROPE_ISSUE(b2);
-
-  // 4. The token's cos/sin, one column per lane, exchanged through the
-  // wavefront's LDS slice while the first P steps load.
-#pragma unroll
-  for (int m = 0; m < kPrePos; ++m) {
-    const int j = lane + m * kWaveSize;
-    if (j < half) {
-      const int32_t pp = pos_pre[m];
-      float c, s;
-      if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
-        const float2 cs = *reinterpret_cast<const float2*>(
-            p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
-        c = cs.x;
-        s = cs.y;
-      } else {
-        angle_cos_sin(pp, inv_pre[m], c, s);
-      }
-      lc[j] = c;
-      ls[j] = s;
-    }
-  }
-  for (int j = lane + kPrePos * kWaveSize; j < half; j += kWaveSize) {
-    const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t0];
-    float c, s;
-    if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
-      const float2 cs = *reinterpret_cast<const float2*>(
-          p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
-      c = cs.x;
-      s = cs.y;
-    } else {
-      angle_cos_sin(pp, tab.inv[j], c, s);
-    }
-    lc[j] = c;
-    ls[j] = s;
-  }
-  // LDS traffic of one wavefront is processed in order; this only keeps the
-  // compiler from moving the reads above the writes.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // This lane's columns (pass-through lanes read column 0: unused)
-  double c_[V], s_[V];
-  {
-    const int cj = rot ? col_a : 0;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      c_[i] = (double)lc[cj + i];
-      s_[i] = (double)ls[cj + i];
-    }
-  }
-
-  float wqa[V], wqb[V], wka[V], wkb[V];
-  unpack<BF16, V>(wq_a, wqa);
-  unpack<BF16, V>(wq_b, wqb);
-  unpack<BF16, V>(wk_a, wka);
-  unpack<BF16, V>(wk_b, wkb);
-
-  // 5. Finish step j while steps j + 1 .. j + P load.
-#define MROPE_FINISH(b, valid)                                                                  \
-  pipe_finish<BF16, V, NORM, LPR, PREC>(b, valid, p, lpr, rot, ca, cb, c_, s_, wqa, wqb, wka, \
-                                        wkb, ry0, ry1, ry2)
-  if constexpr (P == 2) {
-    for (int j = 0; j < N; j += 3) {
-      MROPE_ISSUE(b2);
-      MROPE_FINISH(b0, j < N);
-      MROPE_ISSUE(b0);
-      MROPE_FINISH(b1, j + 1 < N);
-      MROPE_ISSUE(b1);
-      MROPE_FINISH(b2, j + 2 < N);
-    }
-  } else {
-    for (int j = 0; j < N; j += 4) {
-      MROPE_ISSUE(b3);
-      MROPE_FINISH(b0, j < N);
-      MROPE_ISSUE(b0);
-      MROPE_FINISH(b1, j + 1 < N);
-      MROPE_ISSUE(b1);
-      MROPE_FINISH(b2, j + 2 < N);
-      MROPE_ISSUE(b2);
-      MROPE_FINISH(b3, j + 3 < N);
-    }
-  }
-#undef MROPE_ISSUE
-#undef MROPE_FINISH
 }
 
 // ---------------------------------------------------------------------------
@@ -1710,37 +1083,6 @@ __global__ void __launch_bounds__(256) cos_sin_cache_kernel(const ColTable tab, 
   *reinterpret_cast<float2*>(cache + 2 * idx) = v;
 }
 
-// The axis table as one of the kernel's two rules (ax_mode 0 or 1), or -1.
-void fit_axis_rule(const ColTable& tab, int half, QKParams& p) {
-  int n0 = 0, n1 = 0, n2 = 0;
-  bool sorted = true;
-  for (int j = 0; j < half; ++j) {
-    n0 += tab.axis[j] == 0;
-    n1 += tab.axis[j] == 1;
-    n2 += tab.axis[j] == 2;
-    if (j > 0 && tab.axis[j] < tab.axis[j - 1]) sorted = false;
-  }
-  for (int mode = 0; mode < 2; ++mode) {
-    const int a = mode == 0 ? n0 : 3 * n1;
-    const int b = mode == 0 ? n0 + n1 : 3 * n2;
-    if (mode == 0 && !sorted) continue;
-    bool ok = true;
-    for (int j = 0; j < half && ok; ++j) {
-      const int ax = mode == 0 ? (j >= a) + (j >= b)
-                              : (j % 3 == 1 && j < a) ? 1 : (j % 3 == 2 && j < b) ? 2 : 0;
-      ok = ax == tab.axis[j];
-    }
-    if (ok) {
-      p.ax_mode = mode;
-      p.ax_a = a;
-      p.ax_b = b;
-      return;
-    }
-  }
-  p.ax_mode = -1;
-  p.ax_a = p.ax_b = 0;
-}
-
 template <bool BF16, int V, int CS, bool NORM, int LPR, int PREC>
 int launch_t(QKParams p, const ColTable& tab, int nt_cap, hipStream_t st) {
   const bool cs_lds = CS == kCsFromPositions || CS == kCsDecode;
@@ -1829,57 +1171,6 @@ int launch_lpr(int cs_mode, bool norm, int prec, const QKParams& p, const ColTab
   return launch_mode<BF16, V, 0>(cs_mode, norm, prec, p, tab, nt_cap, st);
 }
 
-template <bool BF16, int V, bool NORM, int LPR, int PREC, int P>
-int launch_pipe_t(QKParams p, const ColTable& tab, hipStream_t st) {
-  fit_axis_rule(tab, p.half, p);
-  p.nt = 1;
-  p.parts = 1;
-  const int64_t blocks = (p.T + kWavesPerBlock - 1) / kWavesPerBlock;
-  int lds = kWavesPerBlock * 2 * p.half * (int)sizeof(float);
-  if (p.waves_cap > 0) {
-    const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
-    if (cap_lds > lds) lds = cap_lds;
-  }
-  hipLaunchKernelGGL((qk_pipe_kernel<BF16, V, NORM, LPR, PREC, P>), dim3((unsigned)blocks),
-                     dim3(kBlockThreads), lds, st, p, tab);
-  return (int)hipGetLastError();
-}
-
-template <bool BF16, int V, bool NORM, int LPR, int PREC>
-int launch_pipe_p(int depth, const QKParams& p, const ColTable& tab, hipStream_t st) {
-  switch (depth) {
-    case 2: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 2>(p, tab, st);
-    case 3: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 3>(p, tab, st);
-  }
-  return (int)hipErrorInvalidValue;
-}
-
-template <bool BF16, int V, bool NORM, int LPR>
-int launch_pipe_prec(int prec, int depth, const QKParams& p, const ColTable& tab,
-                     hipStream_t st) {
-  switch (prec) {
-    case MROPE_PRECISION_EXACT:
-      return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_EXACT>(depth, p, tab, st);
-    case MROPE_PRECISION_DTYPE:
-      return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_DTYPE>(depth, p, tab, st);
-    case MROPE_PRECISION_FP32:
-      if constexpr (BF16)
-        return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_FP32>(depth, p, tab, st);
-      break;
-  }
-  return (int)hipErrorInvalidValue;
-}
-
-template <bool BF16, int V, bool NORM>
-int launch_pipe_lpr(int prec, int depth, const QKParams& p, const ColTable& tab,
-                    hipStream_t st) {
-  switch (p.lpr) {
-    case 8: return launch_pipe_prec<BF16, V, NORM, 8>(prec, depth, p, tab, st);
-    case 16: return launch_pipe_prec<BF16, V, NORM, 16>(prec, depth, p, tab, st);
-  }
-  return launch_pipe_prec<BF16, V, NORM, 0>(prec, depth, p, tab, st);
-}
-
 }  // namespace
 
 int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKParams& p,
@@ -1899,18 +1190,6 @@ int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKPara
       case 1: return launch_lpr<false, 1>(cs_mode, norm, prec, p, tab, nt_cap, st);
     }
   }
-  return (int)hipErrorInvalidValue;
-}
-
-int launch_qk_pipe(int dtype, int vec, bool norm, int prec, int depth, const QKParams& p,
-                   const ColTable& tab, void* stream) {
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == MROPE_DTYPE_BF16 && vec == 8)
-    return norm ? launch_pipe_lpr<true, 8, true>(prec, depth, p, tab, st)
-                : launch_pipe_lpr<true, 8, false>(prec, depth, p, tab, st);
-  if (dtype == MROPE_DTYPE_F32 && vec == 4)
-    return norm ? launch_pipe_lpr<false, 4, true>(prec, depth, p, tab, st)
-                : launch_pipe_lpr<false, 4, false>(prec, depth, p, tab, st);
   return (int)hipErrorInvalidValue;
 }
 

@@ -1,0 +1,435 @@
+// The pipelined q/k kernel for gfx950 (qk_pipe_kernel) and its launchers:
+// per-head RMSNorm + multimodal rotary embedding of token-major q, k (and a
+// packed qkv's copied v), one token per wavefront, the token's row-steps as
+// one software-pipelined stream.  The arithmetic per element is
+// qk_kernel's (mrope_kernels.hip), so the results are bit-identical.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mrope_device.h"
+
+// Resident wavefronts per SIMD the pipelined kernel is compiled for, with
+// and without RMSNorm (its registers then fit 512 / this many).  Measured on
+// the 32 + 4 head bf16 prefill with inputs the memory-side cache does not
+// hold: 3 waves 105.2 us; 4 waves spill (135 us).
+#ifndef MROPE_PIPE_MIN_WAVES
+#define MROPE_PIPE_MIN_WAVES 3
+#endif
+#ifndef MROPE_PIPE_MIN_WAVES_NONORM
+#define MROPE_PIPE_MIN_WAVES_NONORM 4
+#endif
+
+namespace mrope {
+namespace {
+
+// ---------------------------------------------------------------------------
+// The pipelined q/k kernel: cos/sin from positions, one token per wavefront,
+// launches of at least one wavefront per token over the whole chip.  The
+// token's row-steps -- q's, then k's, then a packed qkv's copied v -- form one
+// stream, and the loads of step j + P are issued before step j is finished:
+// every wavefront keeps P row-steps of loads in flight while it computes.  (In
+// qk_kernel a wavefront has loads in flight only while it waits for them, so
+// the chip's bytes in flight drop by the share of time its wavefronts spend
+// on the norm and the rotation.)  Every row of the wavefront belongs to one
+// token, so a lane's cos/sin are the same for all its rows: they are formed
+// once (one sincos per lane, exchanged through LDS) and held in registers as
+// doubles, which takes the per-step LDS reads and conversions out of the
+// loop.  The weights, the token's positions and the first P steps are loaded
+// before the sincos.  Every load and store is issued unconditionally -- a
+// masked row or a step past the end uses an offset past its buffer -- so the
+// compiler's waits on the in-order vector memory counter are exact.  The
+// arithmetic per element is qk_kernel's, so the results are bit-identical.
+// ---------------------------------------------------------------------------
+
+template <int CB>
+struct PipeStep {
+  Words<CB> ra, rb;              // the lane's two chunks of its row
+  uint32_t you;                  // byte offset of the row's output, or out of range
+  int slot;                      // tensor of the step (wave-uniform); kSlots past the end
+};
+
+// Position of a wavefront in its step stream.  Wave-uniform: the tensor, the
+// steps left in it and its walking constants; per lane: the next row's head
+// and byte offsets.
+struct PipeCursor {
+  int slot, left, r0, H, dr;
+  uint32_t xinc, yinc;
+  int h;
+  uint32_t xo, yo;
+};
+
+// Moves the cursor to the first row of the first tensor >= from that has
+// steps (n0, n1, n2 for q, k, v), or past the end.  The tensor's fields are
+// picked by constant index: a dynamic index into the kernel-argument struct
+// would copy it to scratch memory.  One token: row r is head r, at byte
+// offset r * D * es of the input and r * head stride of the output.
+__device__ __forceinline__ void pipe_enter(PipeCursor& c, const QKParams& p, int from, int n0,
+                                           int n1, int n2, int grp, int rpw, int es) {
+  int s = from;
+  if (s == 0 && n0 == 0) s = 1;
+  if (s == 1 && n1 == 0) s = 2;
+  if (s == 2 && n2 == 0) s = kSlots;
+  c.slot = __builtin_amdgcn_readfirstlane(s);
+  if (c.slot >= kSlots) return;
+  const int ss = c.slot;
+  const int64_t yhs = ss == 0 ? p.y_hs[0] : (ss == 1 ? p.y_hs[1] : p.y_hs[2]);
+  c.H = ss == 0 ? p.heads[0] : (ss == 1 ? p.heads[1] : p.heads[2]);
+  c.left = ss == 0 ? n0 : (ss == 1 ? n1 : n2);
+  c.r0 = 0;
+  c.h = grp;
+  c.xo = (uint32_t)((int64_t)grp * p.D * es);
+  c.yo = (uint32_t)((int64_t)grp * yhs * es);
+  c.xinc = (uint32_t)((int64_t)rpw * p.D * es);
+  c.yinc = (uint32_t)((int64_t)rpw * yhs * es);
+}
+
+// Issues the loads of the cursor's step into b (masked rows and steps past the
+// end load from out of range) and advances the cursor.
+template <int CB>
+__device__ __forceinline__ void pipe_issue(PipeCursor& c, PipeStep<CB>& b, const QKParams& p,
+                                           __amdgpu_buffer_rsrc_t rx0, __amdgpu_buffer_rsrc_t rx1,
+                                           __amdgpu_buffer_rsrc_t rx2, int n0, int n1, int n2,
+                                           int grp, int rpw, bool lane_on, uint32_t ca,
+                                           uint32_t cb, int es) {
+  const int s = c.slot;
+  const bool have = s < kSlots;
+  const bool ok = have && lane_on && c.h < c.H;
+  b.slot = s;
+  b.you = ok ? c.yo : kOutOfRange;
+  const uint32_t xoff = ok ? c.xo : kOutOfRange;
+  const __amdgpu_buffer_rsrc_t rx = s == 0 ? rx0 : (s == 1 ? rx1 : rx2);
+  buf_load<CB>(rx, xoff + ca, b.ra);
+  buf_load<CB>(rx, xoff + cb, b.rb);
+  if (have) {
+    c.xo += c.xinc;
+    c.yo += c.yinc;
+    c.h += rpw;
+    if (--c.left == 0) pipe_enter(c, p, s + 1, n0, n1, n2, grp, rpw, es);
+  }
+}
+
+// RMSNorm (NORM) and rotation (rot) of one lane's two chunks: a at column
+// col_a, b at its split-half partner (or a second pass-through chunk), with
+// the cos/sin of columns col_a.. as doubles.  The arithmetic of finish_steps,
+// element for element.
+template <bool BF16, int V, bool NORM, int LPR, int PREC>
+__device__ __forceinline__ void norm_rotate(float (&a)[V], float (&b)[V], const QKParams& p,
+                                            int lpr, bool rot, const float (&wa)[V],
+                                            const float (&wb)[V], const double (&c_)[V],
+                                            const double (&s_)[V]) {
+  if constexpr (NORM) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      ss = __builtin_fma((double)a[i], (double)a[i], ss);
+      ss = __builtin_fma((double)b[i], (double)b[i], ss);
+    }
+    ss = row_sum<LPR>(ss, lpr);
+    const float rs = rsqrt_to_f32(ss * p.inv_d + (double)p.eps);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      a[i] = a[i] * rs;
+      b[i] = b[i] * rs;
+    }
+    if constexpr (BF16) round_bf16_chunks<V>(a, b);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      a[i] = a[i] * wa[i];
+      b[i] = b[i] * wb[i];
+    }
+    if constexpr (BF16) round_bf16_chunks<V>(a, b);
+  }
+  if (rot) {
+    if constexpr (PREC == MROPE_PRECISION_EXACT) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const double y1 = a[i];
+        const double y2 = b[i];
+        const double o1 = __builtin_fma(y1, c_[i], -(y2 * s_[i]));
+        const double o2 = __builtin_fma(y2, c_[i], y1 * s_[i]);
+        a[i] = (float)o1;
+        b[i] = (float)o2;
+      }
+    } else {
+      rotate_tensor_ops<BF16 && PREC == MROPE_PRECISION_DTYPE, V>(a, b, c_, s_, c_, s_);
+    }
+  }
+}
+
+// Finishes a step: RMSNorm and rotation of q and k rows (v rows are copied)
+// and the two stores.  A step past the end (valid false) skips the
+// arithmetic; its stores, like those of masked rows, are out of range.
+template <bool BF16, int V, bool NORM, int LPR, int PREC>
+__device__ __forceinline__ void pipe_finish(const PipeStep<(BF16 ? 2 : 4) * V>& b, bool valid,
+                                            const QKParams& p, int lpr, bool rot, uint32_t ca,
+                                            uint32_t cb, const double (&c_)[V],
+                                            const double (&s_)[V], const float (&wqa)[V],
+                                            const float (&wqb)[V], const float (&wka)[V],
+                                            const float (&wkb)[V], __amdgpu_buffer_rsrc_t ry0,
+                                            __amdgpu_buffer_rsrc_t ry1,
+                                            __amdgpu_buffer_rsrc_t ry2) {
+  constexpr int CB = (BF16 ? 2 : 4) * V;
+  Words<CB> oa = b.ra, ob = b.rb;
+  if (valid && b.slot < 2) {
+    float a[V], c[V];
+    unpack<BF16, V>(b.ra, a);
+    unpack<BF16, V>(b.rb, c);
+    if (b.slot == 0)
+      norm_rotate<BF16, V, NORM, LPR, PREC>(a, c, p, lpr, rot, wqa, wqb, c_, s_);
+    else
+      norm_rotate<BF16, V, NORM, LPR, PREC>(a, c, p, lpr, rot, wka, wkb, c_, s_);
+    pack<BF16, V>(a, oa);
+    pack<BF16, V>(c, ob);
+  }
+  const __amdgpu_buffer_rsrc_t ry = b.slot == 0 ? ry0 : (b.slot == 1 ? ry1 : ry2);
+  buf_store<BF16, CB>(ry, b.you + ca, oa);
+  buf_store<BF16, CB>(ry, b.you + cb, ob);
+}
+
+template <bool BF16, int V, bool NORM, int LPR, int PREC, int P>
+__global__ void __launch_bounds__(kBlockThreads)
+__attribute__((amdgpu_waves_per_eu(NORM ? MROPE_PIPE_MIN_WAVES : MROPE_PIPE_MIN_WAVES_NONORM)))
+qk_pipe_kernel(const QKParams p, const ColTable tab) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int CB = ES * V;
+  extern __shared__ double lds[];
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+  const int half = p.half;
+  float* lc = reinterpret_cast<float*>(lds) + wib * (2 * half);
+  float* ls = lc + half;
+
+  const int lpr = LPR > 0 ? LPR : p.lpr;
+  const int rpw = LPR > 0 ? kWaveSize / (LPR > 0 ? LPR : 1) : p.rpw;
+  const int grp = lane / lpr;
+  const int l = lane - grp * lpr;
+  const bool lane_on = grp < rpw;
+  const bool rot = l < p.lrot;
+  int col_a, col_b;
+  if (l < p.lrot) {
+    col_a = l * V;
+    col_b = half + l * V;
+  } else {
+    const int m = l - p.lrot;
+    const int npass = lpr - p.lrot;
+    col_a = p.rd + m * V;
+    col_b = p.rd + (npass + m) * V;
+  }
+  const uint32_t ca = (uint32_t)(col_a * ES);
+  const uint32_t cb = (uint32_t)(col_b * ES);
+
+  const int64_t t0 = (int64_t)blockIdx.x * kWavesPerBlock + wib;
+  if (t0 >= p.T) return;
+  // Row-steps of each tensor (wave-uniform scalars: no private arrays, so
+  // the buffer descriptors chosen from them stay in scalar registers).
+  const int n0 = (p.heads[0] + rpw - 1) / rpw;
+  const int n1 = (p.heads[1] + rpw - 1) / rpw;
+  const int n2 = (p.heads[2] + rpw - 1) / rpw;
+  const int N = n0 + n1 + n2;
+  if (N == 0) return;
+
+  // The token's rows of each tensor (32-bit byte offsets inside them).
+#define MROPE_X_RSRC(s)                                                          \
+  buffer_of(static_cast<const char*>(p.x[s]) + t0 * p.x_ts[s] * ES,              \
+            (uint32_t)((int64_t)p.heads[s] * p.D * ES))
+#define MROPE_Y_RSRC(s)                                                          \
+  buffer_of(static_cast<const char*>(p.y[s]) + t0 * p.y_ts[s] * ES,              \
+            p.heads[s] > 0 ? (uint32_t)(((int64_t)(p.heads[s] - 1) * p.y_hs[s] + p.D) * ES) : 0u)
+  const __amdgpu_buffer_rsrc_t rx0 = MROPE_X_RSRC(0), rx1 = MROPE_X_RSRC(1), rx2 = MROPE_X_RSRC(2);
+  const __amdgpu_buffer_rsrc_t ry0 = MROPE_Y_RSRC(0), ry1 = MROPE_Y_RSRC(1), ry2 = MROPE_Y_RSRC(2);
+#undef MROPE_X_RSRC
+#undef MROPE_Y_RSRC
+
+  // 1. RMSNorm weights of q and k (tiny, shared by every wavefront).
+  Words<CB> wq_a = {}, wq_b = {}, wk_a = {}, wk_b = {};
+  if constexpr (NORM) {
+    const __amdgpu_buffer_rsrc_t rq =
+        buffer_of(p.w[0], p.heads[0] > 0 ? (uint32_t)(p.D * ES) : 0u);
+    const __amdgpu_buffer_rsrc_t rk =
+        buffer_of(p.w[1], p.heads[1] > 0 ? (uint32_t)(p.D * ES) : 0u);
+    buf_load<CB>(rq, ca, wq_a);
+    buf_load<CB>(rq, cb, wq_b);
+    buf_load<CB>(rk, ca, wk_a);
+    buf_load<CB>(rk, cb, wk_b);
+  }
+
+  // 2. What the sincos of the token's first 2 x 64 columns need: positions
+  // (the axis from the fitted rule, no table load) and inv_freq.
+  constexpr int kPrePos = 2;
+  int32_t pos_pre[kPrePos];
+  float inv_pre[kPrePos];
+#pragma unroll
+  for (int m = 0; m < kPrePos; ++m) {
+    const int idx = lane + m * kWaveSize;
+    const int j = idx < half ? idx : 0;
+    int ax;
+    if (p.ax_mode == 0) ax = (j >= p.ax_a) + (j >= p.ax_b);
+    else if (p.ax_mode == 1) ax = (j % 3 == 1 && j < p.ax_a) ? 1 : (j % 3 == 2 && j < p.ax_b) ? 2 : 0;
+    else ax = tab.axis[j];
+    pos_pre[m] = p.pos[(int64_t)ax * p.pos_stride + t0];
+    inv_pre[m] = tab.inv[j];
+  }
+
+  // 3. The step stream, and the loads of its first P steps.
+  static_assert(P == 2 || P == 3, "pipeline depth 2 or 3");
+  PipeCursor cur;
+  pipe_enter(cur, p, 0, n0, n1, n2, grp, rpw, ES);
+#define MROPE_ISSUE(b) \
+  pipe_issue<CB>(cur, b, p, rx0, rx1, rx2, n0, n1, n2, grp, rpw, lane_on, ca, cb, ES)
+  // The step buffers rotate through the unrolled loop bodies below.
+  PipeStep<CB> b0, b1, b2, b3;
+  MROPE_ISSUE(b0);
+  MROPE_ISSUE(b1);
+  if constexpr (P == 3) MROPE_ISSUE(b2);
+
+  // 4. The token's cos/sin, one column per lane, exchanged through the
+  // wavefront's LDS slice while the first P steps load.
+#pragma unroll
+  for (int m = 0; m < kPrePos; ++m) {
+    const int j = lane + m * kWaveSize;
+    if (j < half) {
+      const int32_t pp = pos_pre[m];
+      float c, s;
+      if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
+        const float2 cs = *reinterpret_cast<const float2*>(
+            p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
+        c = cs.x;
+        s = cs.y;
+      } else {
+        angle_cos_sin(pp, inv_pre[m], c, s);
+      }
+      lc[j] = c;
+      ls[j] = s;
+    }
+  }
+  for (int j = lane + kPrePos * kWaveSize; j < half; j += kWaveSize) {
+    const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t0];
+    float c, s;
+    if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
+      const float2 cs = *reinterpret_cast<const float2*>(
+          p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
+      c = cs.x;
+      s = cs.y;
+    } else {
+      angle_cos_sin(pp, tab.inv[j], c, s);
+    }
+    lc[j] = c;
+    ls[j] = s;
+  }
+  // LDS traffic of one wavefront is processed in order; this only keeps the
+  // compiler from moving the reads above the writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // This lane's columns (pass-through lanes read column 0: unused)
+  double c_[V], s_[V];
+  {
+    const int cj = rot ? col_a : 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      c_[i] = (double)lc[cj + i];
+      s_[i] = (double)ls[cj + i];
+    }
+  }
+
+  float wqa[V], wqb[V], wka[V], wkb[V];
+  unpack<BF16, V>(wq_a, wqa);
+  unpack<BF16, V>(wq_b, wqb);
+  unpack<BF16, V>(wk_a, wka);
+  unpack<BF16, V>(wk_b, wkb);
+
+  // 5. Finish step j while steps j + 1 .. j + P load.
+#define MROPE_FINISH(b, valid)                                                                  \
+  pipe_finish<BF16, V, NORM, LPR, PREC>(b, valid, p, lpr, rot, ca, cb, c_, s_, wqa, wqb, wka, \
+                                        wkb, ry0, ry1, ry2)
+  if constexpr (P == 2) {
+    for (int j = 0; j < N; j += 3) {
+      MROPE_ISSUE(b2);
+      MROPE_FINISH(b0, j < N);
+      MROPE_ISSUE(b0);
+      MROPE_FINISH(b1, j + 1 < N);
+      MROPE_ISSUE(b1);
+      MROPE_FINISH(b2, j + 2 < N);
+    }
+  } else {
+    for (int j = 0; j < N; j += 4) {
+      MROPE_ISSUE(b3);
+      MROPE_FINISH(b0, j < N);
+      MROPE_ISSUE(b0);
+      MROPE_FINISH(b1, j + 1 < N);
+      MROPE_ISSUE(b1);
+      MROPE_FINISH(b2, j + 2 < N);
+      MROPE_ISSUE(b2);
+      MROPE_FINISH(b3, j + 3 < N);
+    }
+  }
+#undef MROPE_ISSUE
+#undef MROPE_FINISH
+}
+
+template <bool BF16, int V, bool NORM, int LPR, int PREC, int P>
+int launch_pipe_t(QKParams p, const ColTable& tab, hipStream_t st) {
+  fit_axis_rule(tab, p.half, p);
+  p.nt = 1;
+  p.parts = 1;
+  const int64_t blocks = (p.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  int lds = kWavesPerBlock * 2 * p.half * (int)sizeof(float);
+  if (p.waves_cap > 0) {
+    const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
+    if (cap_lds > lds) lds = cap_lds;
+  }
+  hipLaunchKernelGGL((qk_pipe_kernel<BF16, V, NORM, LPR, PREC, P>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads), lds, st, p, tab);
+  return (int)hipGetLastError();
+}
+
+template <bool BF16, int V, bool NORM, int LPR, int PREC>
+int launch_pipe_p(int depth, const QKParams& p, const ColTable& tab, hipStream_t st) {
+  switch (depth) {
+    case 2: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 2>(p, tab, st);
+    case 3: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 3>(p, tab, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <bool BF16, int V, bool NORM, int LPR>
+int launch_pipe_prec(int prec, int depth, const QKParams& p, const ColTable& tab,
+                     hipStream_t st) {
+  switch (prec) {
+    case MROPE_PRECISION_EXACT:
+      return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_EXACT>(depth, p, tab, st);
+    case MROPE_PRECISION_DTYPE:
+      return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_DTYPE>(depth, p, tab, st);
+    case MROPE_PRECISION_FP32:
+      if constexpr (BF16)
+        return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_FP32>(depth, p, tab, st);
+      break;
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <bool BF16, int V, bool NORM>
+int launch_pipe_lpr(int prec, int depth, const QKParams& p, const ColTable& tab,
+                    hipStream_t st) {
+  switch (p.lpr) {
+    case 8: return launch_pipe_prec<BF16, V, NORM, 8>(prec, depth, p, tab, st);
+    case 16: return launch_pipe_prec<BF16, V, NORM, 16>(prec, depth, p, tab, st);
+  }
+  return launch_pipe_prec<BF16, V, NORM, 0>(prec, depth, p, tab, st);
+}
+
+}  // namespace
+
+int launch_qk_pipe(int dtype, int vec, bool norm, int prec, int depth, const QKParams& p,
+                   const ColTable& tab, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == MROPE_DTYPE_BF16 && vec == 8)
+    return norm ? launch_pipe_lpr<true, 8, true>(prec, depth, p, tab, st)
+                : launch_pipe_lpr<true, 8, false>(prec, depth, p, tab, st);
+  if (dtype == MROPE_DTYPE_F32 && vec == 4)
+    return norm ? launch_pipe_lpr<false, 4, true>(prec, depth, p, tab, st)
+                : launch_pipe_lpr<false, 4, false>(prec, depth, p, tab, st);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace mrope
