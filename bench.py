@@ -64,7 +64,9 @@ KERNEL_SOURCES = {
     "qk_kernel": [_CSRC + "mrope_kernels.hip", _CSRC + "mrope_device.h",
                   _CSRC + "mrope_internal.h"],
 }
-KERNEL_SOURCES["flat_kernel"] = KERNEL_SOURCES["stage_kernel"] = KERNEL_SOURCES["qk_kernel"]
+KERNEL_SOURCES["stage_kernel"] = KERNEL_SOURCES["qk_kernel"]
+KERNEL_SOURCES["flat_kernel"] = [_CSRC + "mrope_flat.hip", _CSRC + "mrope_device.h",
+                                 _CSRC + "mrope_internal.h"]
 # The machine's CPU share for one GPU: oracle worker pools stay within it
 # whatever the affinity mask shows.
 HOST_CORE_SHARE = 16

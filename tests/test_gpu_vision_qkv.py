@@ -149,7 +149,8 @@ def test_vision_qkv_staged_without_v_and_cached(M):
 
 def test_kernel_choice_by_shape(M):
     """bf16 planes of 2048+ tokens take the staged kernel, fp32 planes and
-    token-major vision rows the flat one, short launches the general one."""
+    token-major vision rows the flat one, short launches the general
+    one."""
     import torch
     for dtype, n, head_major, want in [("bf16", 2048, True, "stage_kernel"),
                                        ("f32", 2048, True, "flat_kernel"),

@@ -291,7 +291,7 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t rs, uint32_t of
 }
 
 // The axis table as one of the kernel's two rules (ax_mode 0 or 1), or -1.
-void fit_axis_rule(const ColTable& tab, int half, QKParams& p) {
+inline void fit_axis_rule(const ColTable& tab, int half, QKParams& p) {
   int n0 = 0, n1 = 0, n2 = 0;
   bool sorted = true;
   for (int j = 0; j < half; ++j) {

@@ -166,8 +166,8 @@ int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
 // flight while a step is finished, 2 or 3).
 int launch_qk_pipe(int dtype, int vec, bool norm, int prec, int depth, const QKParams& p,
                    const ColTable& tab, void* stream);
-// The flat q/k kernel: positions path without RMSNorm, one token per
-// wavefront, the token's blocks read as consecutive chunks.
+// The flat q/k kernel (mrope_flat.hip): positions path without RMSNorm, one
+// token per wavefront, the token's blocks read as consecutive chunks.
 int launch_flat(int dtype, int vec, int prec, const QKParams& p, const ColTable& tab,
                 void* stream);
 // The staged kernel with G tokens per block (G in 1, 2, 4, 8, 16), and the
