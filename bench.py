@@ -20,9 +20,10 @@ Measures (HIP events on the stream the kernels are launched on):
   are copied into as many bytes written), rotating over S sets the same way:
   the rate a plain copy of this size reaches under the same measure.
 
-Order on the GPU: the copy ceiling (W warmup + K timed steps), then the
-kernel rotating (W + K), then the kernel on one buffer set (W + K); the
-profile summaries pick their dispatches by this order (--trace-summary).
+Order on the GPU: the copy ceiling (max(W, 50) warmup + max(K, 500) timed
+copies), then the kernel rotating (W + K), then the kernel on one buffer set
+(W + K); the profile summaries pick their dispatches by this order
+(--trace-summary).
 
 Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
 kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
@@ -301,15 +302,22 @@ def copy_ceiling(M, nbytes: int, sets: int, warmup: int, steps: int):
     torch.cuda.empty_cache()
     gbps = 2 * nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "stream_copy_kernel (mrope_stream_copy)", "bytes_read": nbytes,
-            "bytes_written": nbytes, "sets": sets, "ms_per_copy": ms, "gbps": gbps,
-            "frac_of_peak": gbps / HBM_PEAK_GBPS}
+            "bytes_written": nbytes, "sets": sets, "warmup": warmup, "steps": steps,
+            "ms_per_copy": ms, "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS}
+
+
+def copy_counts(warmup: int, steps: int):
+    """(warmup, timed) copies of the copy-ceiling phase: at least 50 and 500,
+    so that the ceiling is measured over at least 50 ms of traffic whatever
+    --steps is."""
+    return max(warmup, 50), max(steps, 500)
 
 
 def measures(M, fns_sets, copy_bytes, args):
     """Copy ceiling, rotating and same-buffer figures of a step, in the order
     the trace summary expects.  fns_sets[i] runs the step on buffer set i."""
     out = {}
-    out["copy"] = copy_ceiling(M, copy_bytes, len(fns_sets), args.warmup, args.steps)
+    out["copy"] = copy_ceiling(M, copy_bytes, len(fns_sets), *copy_counts(args.warmup, args.steps))
     out["rotating"] = time_region(fns_sets, args.warmup, args.steps)
     out["same"] = time_region(fns_sets[:1], args.warmup, args.steps)
     return out
@@ -318,7 +326,8 @@ def measures(M, fns_sets, copy_bytes, args):
 def dispatch_plan(warmup: int, steps: int):
     """(kernel family, phase, dispatch count) in launch order, as measures()
     issues them."""
-    return [("copy", "warmup", warmup), ("copy", "timed_rotating", steps),
+    cw, cs = copy_counts(warmup, steps)
+    return [("copy", "warmup", cw), ("copy", "timed_rotating", cs),
             ("kernel", "warmup_rotating", warmup), ("kernel", "timed_rotating", steps),
             ("kernel", "warmup_same_buffers", warmup), ("kernel", "timed_same_buffers", steps)]
 

@@ -68,13 +68,14 @@ def test_trace_summary_splits_the_phases(tmp_path):
     """The summary picks the dispatches of each phase in launch order:
     copy (W + K), then the kernel rotating (W + K) and on one set (W + K)."""
     W_, K_ = 2, 3
+    CW, CK = bench.copy_counts(W_, K_)
     rows = []
     t = 1000
     names = ["void mrope::(anonymous namespace)::stream_copy_kernel(char const*, char*, "
-             "unsigned long)"] * (W_ + K_) + ["__amd_rocclr_fillBufferAligned"] + \
+             "unsigned long)"] * (CW + CK) + ["__amd_rocclr_fillBufferAligned"] + \
             ["void mrope::(anonymous namespace)::qk_kernel<true, 8, 0, true, 8, 0>(...)"] * \
             (2 * (W_ + K_))
-    durs = [50] * W_ + [40] * K_ + [7] + [120] * W_ + [100] * K_ + [110] * W_ + [90] * K_
+    durs = [50] * CW + [40] * CK + [7] + [120] * W_ + [100] * K_ + [110] * W_ + [90] * K_
     for i, (n, d) in enumerate(zip(names, durs)):
         rows.append({"Kernel_Name": n, "Start_Timestamp": str(t), "End_Timestamp": str(t + d * 1000)})
         t += d * 1000 + 500
