@@ -32,7 +32,8 @@ bounded sample of the same workload (cpu_baseline).
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                   [--rotate S] [--graph G] [--cold] [--cs-cache]
                   [--precision exact|dtype|fp32] [--cpu-procs P]
-  python bench.py --copy-calib BYTES   # plain device copy, for counter scaling
+  python bench.py --pmc-summary DIR / --traffic-record FETCH_DIR WRITE_DIR
+                  # counters of rocprofv3 --pmc runs of bench.py
   python bench.py --trace-summary DIR --workload NAME --steps K --warmup W
                   # per-phase kernel durations from a rocprofv3 kernel trace
 
@@ -692,16 +693,6 @@ def bench_decode(args, wl, inp, dev):
     print(json.dumps(line), flush=True)
 
 
-def copy_calib(nbytes: int, steps: int):
-    import torch
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(steps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": nbytes, "steps": steps}), flush=True)
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -725,7 +716,6 @@ def main():
                     help="processes for the oracle's multi-process sample (default: the "
                          "cores this process may run on, within the box's share of 16; "
                          "1 = one thread only)")
-    ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--graph", type=int, default=0,
                     help="decode and position workloads: capture this many steps in one HIP "
                          "graph and time graph replays")
@@ -756,9 +746,6 @@ def main():
     if args.steps < 1 or args.warmup < 0 or args.rotate < 1:
         print("--steps >= 1, --warmup >= 0 and --rotate >= 1 are required", file=sys.stderr)
         sys.exit(2)
-    if args.copy_calib:
-        copy_calib(args.copy_calib, args.steps)
-        return
 
     import numpy as np
     import torch
