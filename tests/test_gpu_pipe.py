@@ -141,3 +141,37 @@ def test_replays_in_a_hip_graph(M):
         for d in cases:
             assert torch.equal(d["gq"].view(torch.int16), d["eq"].view(torch.int16)), rep
             assert torch.equal(d["gk"].view(torch.int16), d["ek"].view(torch.int16)), rep
+
+
+# (head dim, rotary dim, q heads, k heads): the contiguous-halves layout (one
+# chunk of each half of the row per lane, rotary partners exchanged between
+# lanes) at 2, 4 and 8 rotary chunks per half, and with 8 lanes per row.
+HALVES_SHAPES = [(256, 64, 24, 4), (256, 32, 8, 2), (256, 128, 8, 2), (128, 64, 16, 2)]
+
+
+@pytest.mark.parametrize("D,rd,hq,hk", HALVES_SHAPES)
+@pytest.mark.parametrize("precision", ["exact", "dtype", "fp32"])
+def test_contiguous_halves_layout(M, D, rd, hq, hk, precision):
+    """Partial rotary over at most half the row in the pipelined kernel, in
+    every precision: bit-exact against the oracle."""
+    import torch
+    rng = np.random.default_rng(D * 1000 + rd)
+    T = 2304
+    q, k = W.random_qk(rng, T, hq, hk, D, "bf16")
+    wq, wk = W.random_weight(rng, D, "bf16"), W.random_weight(rng, D, "bf16")
+    half = rd // 2
+    sec = (half - 2 * (half // 3), half // 3, half // 3)
+    pos = np.stack([np.arange(T) + 17, (np.arange(T) * 7) % 501, (np.arange(T) * 3) % 97])
+    pos = pos.astype(np.int32)
+    note(f"contiguous halves D={D} rd={rd} {precision}")
+    qo, ko = M.rmsnorm_mrope_qk(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(pos, "i32"), rd,
+                                1e6, sec, "interleaved", wq=to_dev(wq, "bf16"),
+                                wk=to_dev(wk, "bf16"), eps=1e-6, precision=precision)
+    torch.cuda.synchronize()
+    assert M.last_kernel() == "qk_pipe_kernel"
+    oq, ok = O.rmsnorm_mrope_qk(q, k, pos, rotary_dim=rd, theta=1e6, section=sec,
+                                layout="interleaved", wq=wq, wk=wk, eps=1e-6, dtype="bf16",
+                                precision=precision)
+    gq, gk = from_dev(qo), from_dev(ko)
+    assert np.array_equal(gq.view(np.uint16), np.asarray(oq).view(np.uint16)), "q"
+    assert np.array_equal(gk.view(np.uint16), np.asarray(ok).view(np.uint16)), "k"

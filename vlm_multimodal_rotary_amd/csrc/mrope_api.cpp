@@ -417,8 +417,7 @@ int waves_per_simd_stage() {
 // registers) serves the positions path for 16-byte chunks when the launch has
 // at least kMinPipeTokens tokens.  Measured on MI355X with inputs that the
 // memory-side cache does not hold (rotating buffer sets), against qk_kernel.
-// MROPE_PIPE=0/1 forces the choice where it is allowed, MROPE_PIPE_DEPTH the
-// depth (2 or 3) (tuning).
+// MROPE_PIPE=0/1 forces the choice where it is allowed (tuning).
 constexpr int64_t kMinPipeTokens = 2048;
 
 bool use_pipe(const QKArgs& a, int cs_mode, int v, int es) {
@@ -426,11 +425,6 @@ bool use_pipe(const QKArgs& a, int cs_mode, int v, int es) {
   static const int env = env_int("MROPE_PIPE", -1);
   if (env >= 0) return env != 0;
   return true;
-}
-
-int pipe_depth() {
-  static const int env = env_int("MROPE_PIPE_DEPTH", 0);
-  return env == 2 || env == 3 ? env : 2;
 }
 
 // Launch geometry and the remaining per-launch fields.
@@ -580,7 +574,7 @@ int run_qk(const QKArgs& a, int cs_mode, bool norm, const mrope::ColTable& tab,
     g_last_kernel = "flat_kernel";
   } else if (use_pipe(a, cs_mode, v, es)) {
     p.waves_cap = waves_per_simd(a, v, es);
-    hrc = mrope::launch_qk_pipe(a.dtype, v, norm, prec, pipe_depth(), p, tab, stream);
+    hrc = mrope::launch_qk_pipe(a.dtype, v, norm, prec, p, tab, stream);
     g_last_kernel = "qk_pipe_kernel";
   } else {
     p.waves_cap = waves_per_simd(a, v, es);

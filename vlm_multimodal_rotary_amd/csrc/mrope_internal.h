@@ -162,9 +162,9 @@ int launch_qk(int dtype, int vec, int cs_mode, bool norm, int prec, const QKPara
               const ColTable& tab, int nt_cap, void* stream);
 int launch_cos_sin(const CosSinParams& p, const ColTable& tab, void* stream);
 // The pipelined q/k kernel (positions path, 16-byte chunks: vec 8 for bf16, 4
-// for binary32; one wavefront per token; depth = row-steps whose loads are in
-// flight while a step is finished, 2 or 3).
-int launch_qk_pipe(int dtype, int vec, bool norm, int prec, int depth, const QKParams& p,
+// for binary32; one wavefront per token; two row-steps of loads in flight
+// while a step is finished).
+int launch_qk_pipe(int dtype, int vec, bool norm, int prec, const QKParams& p,
                    const ColTable& tab, void* stream);
 // The flat q/k kernel (mrope_flat.hip): positions path without RMSNorm, one
 // token per wavefront, the token's blocks read as consecutive chunks.

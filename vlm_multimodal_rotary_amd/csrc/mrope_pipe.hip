@@ -26,15 +26,15 @@ namespace {
 // The pipelined q/k kernel: cos/sin from positions, one token per wavefront,
 // launches of at least one wavefront per token over the whole chip.  The
 // token's row-steps -- q's, then k's, then a packed qkv's copied v -- form one
-// stream, and the loads of step j + P are issued before step j is finished:
-// every wavefront keeps P row-steps of loads in flight while it computes.  (In
+// stream, and the loads of step j + 2 are issued before step j is finished:
+// every wavefront keeps two row-steps of loads in flight while it computes.  (In
 // qk_kernel a wavefront has loads in flight only while it waits for them, so
 // the chip's bytes in flight drop by the share of time its wavefronts spend
 // on the norm and the rotation.)  Every row of the wavefront belongs to one
 // token, so a lane's cos/sin are the same for all its rows: they are formed
 // once (one sincos per lane, exchanged through LDS) and held in registers as
 // doubles, which takes the per-step LDS reads and conversions out of the
-// loop.  The weights, the token's positions and the first P steps are loaded
+// loop.  The weights, the token's positions and the first two steps are loaded
 // before the sincos.  Every load and store is issued unconditionally -- a
 // masked row or a step past the end uses an offset past its buffer -- so the
 // compiler's waits on the in-order vector memory counter are exact.  The
@@ -108,13 +108,29 @@ __device__ __forceinline__ void pipe_issue(PipeCursor& c, PipeStep<CB>& b, const
   }
 }
 
-// RMSNorm (NORM) and rotation (rot) of one lane's two chunks: a at column
-// col_a, b at its split-half partner (or a second pass-through chunk), with
-// the cos/sin of columns col_a.. as doubles.  The arithmetic of finish_steps,
-// element for element.
-template <bool BF16, int V, bool NORM, int LPR, int PREC>
+// The value of v on lane (lane + HC) for lanes of the first HC of each
+// group of 2 * HC lanes (x1 lanes), and on lane (lane - HC) for the others:
+// the split-half partner of a rotary chunk in the contiguous-halves layout.
+// DPP row shifts stay within 16-lane rows, which hold whole row groups (lpr
+// a power of two <= 16).  Every lane of the wavefront executes it.
+template <int HC>
+__device__ __forceinline__ float xch_partner(float v, bool x2) {
+  const int u = __builtin_bit_cast(int, v);
+  const int up = __builtin_amdgcn_update_dpp(0, u, 0x100 | HC, 0xF, 0xF, false);  // row_shl
+  const int dn = __builtin_amdgcn_update_dpp(0, u, 0x110 | HC, 0xF, 0xF, false);  // row_shr
+  return __builtin_bit_cast(float, x2 ? dn : up);
+}
+
+// RMSNorm (NORM) and rotation (rot) of one lane's two chunks, with the
+// cos/sin of the lane's rotary columns as doubles.  Two layouts: HC == 0, a
+// at column col_a and b at its split-half partner (or a second pass-through
+// chunk); HC > 0 (partial rotary over at most half the row), a and b at the
+// lane's chunk of each half of the row, the rotary chunks on the first 2 * HC
+// lanes of a row with the partner of a on the lane HC away (x2 marks the
+// second half's lanes).  The arithmetic of finish_steps, element for element.
+template <bool BF16, int V, bool NORM, int LPR, int PREC, int HC>
 __device__ __forceinline__ void norm_rotate(float (&a)[V], float (&b)[V], const QKParams& p,
-                                            int lpr, bool rot, const float (&wa)[V],
+                                            int lpr, bool rot, bool x2, const float (&wa)[V],
                                             const float (&wb)[V], const double (&c_)[V],
                                             const double (&s_)[V]) {
   if constexpr (NORM) {
@@ -139,7 +155,38 @@ __device__ __forceinline__ void norm_rotate(float (&a)[V], float (&b)[V], const 
     }
     if constexpr (BF16) round_bf16_chunks<V>(a, b);
   }
-  if (rot) {
+  if constexpr (HC > 0) {
+    float pa[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) pa[i] = xch_partner<HC>(a[i], x2);
+    if (rot) {
+      // x1 lanes: x1 * cos - x2 * sin; x2 lanes: x2 * cos + x1 * sin.
+      if constexpr (PREC == MROPE_PRECISION_EXACT) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const double ps = (double)pa[i] * s_[i];
+          a[i] = (float)__builtin_fma((double)a[i], c_[i], x2 ? ps : -ps);
+        }
+      } else {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float c1 = (float)c_[i], s1 = (float)s_[i];
+          if constexpr (BF16 && PREC == MROPE_PRECISION_DTYPE) {
+            c1 = round_bf16(c1);
+            s1 = round_bf16(s1);
+          }
+          float p1 = a[i] * c1;
+          float p2 = pa[i] * s1;
+          if constexpr (BF16 && PREC == MROPE_PRECISION_DTYPE) {
+            p1 = round_bf16(p1);
+            p2 = round_bf16(p2);
+          }
+          a[i] = x2 ? p1 + p2 : p1 - p2;
+        }
+      }
+    }
+  } else if (rot) {
     if constexpr (PREC == MROPE_PRECISION_EXACT) {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -159,9 +206,10 @@ __device__ __forceinline__ void norm_rotate(float (&a)[V], float (&b)[V], const 
 // Finishes a step: RMSNorm and rotation of q and k rows (v rows are copied)
 // and the two stores.  A step past the end (valid false) skips the
 // arithmetic; its stores, like those of masked rows, are out of range.
-template <bool BF16, int V, bool NORM, int LPR, int PREC>
+template <bool BF16, int V, bool NORM, int LPR, int PREC, int HC>
 __device__ __forceinline__ void pipe_finish(const PipeStep<(BF16 ? 2 : 4) * V>& b, bool valid,
-                                            const QKParams& p, int lpr, bool rot, uint32_t ca,
+                                            const QKParams& p, int lpr, bool rot, bool x2,
+                                            uint32_t ca,
                                             uint32_t cb, const double (&c_)[V],
                                             const double (&s_)[V], const float (&wqa)[V],
                                             const float (&wqb)[V], const float (&wka)[V],
@@ -175,9 +223,9 @@ __device__ __forceinline__ void pipe_finish(const PipeStep<(BF16 ? 2 : 4) * V>& 
     unpack<BF16, V>(b.ra, a);
     unpack<BF16, V>(b.rb, c);
     if (b.slot == 0)
-      norm_rotate<BF16, V, NORM, LPR, PREC>(a, c, p, lpr, rot, wqa, wqb, c_, s_);
+      norm_rotate<BF16, V, NORM, LPR, PREC, HC>(a, c, p, lpr, rot, x2, wqa, wqb, c_, s_);
     else
-      norm_rotate<BF16, V, NORM, LPR, PREC>(a, c, p, lpr, rot, wka, wkb, c_, s_);
+      norm_rotate<BF16, V, NORM, LPR, PREC, HC>(a, c, p, lpr, rot, x2, wka, wkb, c_, s_);
     pack<BF16, V>(a, oa);
     pack<BF16, V>(c, ob);
   }
@@ -186,7 +234,7 @@ __device__ __forceinline__ void pipe_finish(const PipeStep<(BF16 ? 2 : 4) * V>& 
   buf_store<BF16, CB>(ry, b.you + cb, ob);
 }
 
-template <bool BF16, int V, bool NORM, int LPR, int PREC, int P>
+template <bool BF16, int V, bool NORM, int LPR, int PREC, int HC>
 __global__ void __launch_bounds__(kBlockThreads)
 __attribute__((amdgpu_waves_per_eu(NORM ? MROPE_PIPE_MIN_WAVES : MROPE_PIPE_MIN_WAVES_NONORM)))
 qk_pipe_kernel(const QKParams p, const ColTable tab) {
@@ -204,16 +252,32 @@ qk_pipe_kernel(const QKParams p, const ColTable tab) {
   const int grp = lane / lpr;
   const int l = lane - grp * lpr;
   const bool lane_on = grp < rpw;
-  const bool rot = l < p.lrot;
-  int col_a, col_b;
-  if (l < p.lrot) {
+  // The lane's two chunks (columns col_a and col_b) and the column of its
+  // cos/sin (cj).  HC == 0: col_a rotary or pass-through, col_b its split-half
+  // partner or a second pass-through chunk.  HC > 0 (HC == lrot, partial
+  // rotary over at most half the row): one chunk in each half of the row, so
+  // each store instruction writes whole cache lines; the rotary chunks are
+  // the first 2 * HC of the row, x1 on lanes l < HC and x2 on the next HC.
+  bool rot, x2 = false;
+  int col_a, col_b, cj;
+  if constexpr (HC > 0) {
     col_a = l * V;
-    col_b = half + l * V;
+    col_b = (lpr + l) * V;
+    rot = l < 2 * HC;
+    x2 = l >= HC;
+    cj = rot ? (x2 ? l - HC : l) * V : 0;
   } else {
-    const int m = l - p.lrot;
-    const int npass = lpr - p.lrot;
-    col_a = p.rd + m * V;
-    col_b = p.rd + (npass + m) * V;
+    rot = l < p.lrot;
+    if (l < p.lrot) {
+      col_a = l * V;
+      col_b = half + l * V;
+    } else {
+      const int m = l - p.lrot;
+      const int npass = lpr - p.lrot;
+      col_a = p.rd + m * V;
+      col_b = p.rd + (npass + m) * V;
+    }
+    cj = rot ? col_a : 0;
   }
   const uint32_t ca = (uint32_t)(col_a * ES);
   const uint32_t cb = (uint32_t)(col_b * ES);
@@ -270,20 +334,18 @@ qk_pipe_kernel(const QKParams p, const ColTable tab) {
     inv_pre[m] = tab.inv[j];
   }
 
-  // 3. The step stream, and the loads of its first P steps.
-  static_assert(P == 2 || P == 3, "pipeline depth 2 or 3");
+  // 3. The step stream, and the loads of its first two steps.
   PipeCursor cur;
   pipe_enter(cur, p, 0, n0, n1, n2, grp, rpw, ES);
 #define MROPE_ISSUE(b) \
   pipe_issue<CB>(cur, b, p, rx0, rx1, rx2, n0, n1, n2, grp, rpw, lane_on, ca, cb, ES)
   // The step buffers rotate through the unrolled loop bodies below.
-  PipeStep<CB> b0, b1, b2, b3;
+  PipeStep<CB> b0, b1, b2;
   MROPE_ISSUE(b0);
   MROPE_ISSUE(b1);
-  if constexpr (P == 3) MROPE_ISSUE(b2);
 
   // 4. The token's cos/sin, one column per lane, exchanged through the
-  // wavefront's LDS slice while the first P steps load.
+  // wavefront's LDS slice while the first two steps load.
 #pragma unroll
   for (int m = 0; m < kPrePos; ++m) {
     const int j = lane + m * kWaveSize;
@@ -324,7 +386,6 @@ qk_pipe_kernel(const QKParams p, const ColTable tab) {
   // This lane's columns (pass-through lanes read column 0: unused)
   double c_[V], s_[V];
   {
-    const int cj = rot ? col_a : 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       c_[i] = (double)lc[cj + i];
@@ -338,36 +399,23 @@ qk_pipe_kernel(const QKParams p, const ColTable tab) {
   unpack<BF16, V>(wk_a, wka);
   unpack<BF16, V>(wk_b, wkb);
 
-  // 5. Finish step j while steps j + 1 .. j + P load.
+  // 5. Finish step j while steps j + 1 and j + 2 load.
 #define MROPE_FINISH(b, valid)                                                                  \
-  pipe_finish<BF16, V, NORM, LPR, PREC>(b, valid, p, lpr, rot, ca, cb, c_, s_, wqa, wqb, wka, \
-                                        wkb, ry0, ry1, ry2)
-  if constexpr (P == 2) {
-    for (int j = 0; j < N; j += 3) {
-      MROPE_ISSUE(b2);
-      MROPE_FINISH(b0, j < N);
-      MROPE_ISSUE(b0);
-      MROPE_FINISH(b1, j + 1 < N);
-      MROPE_ISSUE(b1);
-      MROPE_FINISH(b2, j + 2 < N);
-    }
-  } else {
-    for (int j = 0; j < N; j += 4) {
-      MROPE_ISSUE(b3);
-      MROPE_FINISH(b0, j < N);
-      MROPE_ISSUE(b0);
-      MROPE_FINISH(b1, j + 1 < N);
-      MROPE_ISSUE(b1);
-      MROPE_FINISH(b2, j + 2 < N);
-      MROPE_ISSUE(b2);
-      MROPE_FINISH(b3, j + 3 < N);
-    }
+  pipe_finish<BF16, V, NORM, LPR, PREC, HC>(b, valid, p, lpr, rot, x2, ca, cb, c_, s_, wqa, wqb, \
+                                            wka, wkb, ry0, ry1, ry2)
+  for (int j = 0; j < N; j += 3) {
+    MROPE_ISSUE(b2);
+    MROPE_FINISH(b0, j < N);
+    MROPE_ISSUE(b0);
+    MROPE_FINISH(b1, j + 1 < N);
+    MROPE_ISSUE(b1);
+    MROPE_FINISH(b2, j + 2 < N);
   }
 #undef MROPE_ISSUE
 #undef MROPE_FINISH
 }
 
-template <bool BF16, int V, bool NORM, int LPR, int PREC, int P>
+template <bool BF16, int V, bool NORM, int LPR, int PREC, int HC>
 int launch_pipe_t(QKParams p, const ColTable& tab, hipStream_t st) {
   fit_axis_rule(tab, p.half, p);
   p.nt = 1;
@@ -378,57 +426,68 @@ int launch_pipe_t(QKParams p, const ColTable& tab, hipStream_t st) {
     const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
     if (cap_lds > lds) lds = cap_lds;
   }
-  hipLaunchKernelGGL((qk_pipe_kernel<BF16, V, NORM, LPR, PREC, P>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((qk_pipe_kernel<BF16, V, NORM, LPR, PREC, HC>), dim3((unsigned)blocks),
                      dim3(kBlockThreads), lds, st, p, tab);
   return (int)hipGetLastError();
 }
 
+// The contiguous-halves layout (HC = rotary chunks per half) serves bf16 rows
+// of 8 or 16 lanes whose rotary columns fit in the first half of the row:
+// partial rotary, where the split-half layout writes two cache lines of each
+// row half from each of the two store instructions.  Measured on the Qwen3.5
+// shape (256-wide heads, 64 rotary columns), rotating buffer sets: 85.4 ->
+// 83.5 us.
 template <bool BF16, int V, bool NORM, int LPR, int PREC>
-int launch_pipe_p(int depth, const QKParams& p, const ColTable& tab, hipStream_t st) {
-  switch (depth) {
-    case 2: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 2>(p, tab, st);
-    case 3: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 3>(p, tab, st);
+int launch_pipe_hc(const QKParams& p, const ColTable& tab, hipStream_t st) {
+  if constexpr (BF16 && LPR >= 8) {
+    if (p.rd < p.D && 2 * p.lrot <= LPR) {
+      switch (p.lrot) {
+        case 2: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 2>(p, tab, st);
+        case 4: return launch_pipe_t<BF16, V, NORM, LPR, PREC, 4>(p, tab, st);
+        case 8:
+          if constexpr (LPR == 16) return launch_pipe_t<BF16, V, NORM, LPR, PREC, 8>(p, tab, st);
+          break;
+      }
+    }
   }
-  return (int)hipErrorInvalidValue;
+  return launch_pipe_t<BF16, V, NORM, LPR, PREC, 0>(p, tab, st);
 }
 
 template <bool BF16, int V, bool NORM, int LPR>
-int launch_pipe_prec(int prec, int depth, const QKParams& p, const ColTable& tab,
-                     hipStream_t st) {
+int launch_pipe_prec(int prec, const QKParams& p, const ColTable& tab, hipStream_t st) {
   switch (prec) {
     case MROPE_PRECISION_EXACT:
-      return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_EXACT>(depth, p, tab, st);
+      return launch_pipe_hc<BF16, V, NORM, LPR, MROPE_PRECISION_EXACT>(p, tab, st);
     case MROPE_PRECISION_DTYPE:
-      return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_DTYPE>(depth, p, tab, st);
+      return launch_pipe_hc<BF16, V, NORM, LPR, MROPE_PRECISION_DTYPE>(p, tab, st);
     case MROPE_PRECISION_FP32:
       if constexpr (BF16)
-        return launch_pipe_p<BF16, V, NORM, LPR, MROPE_PRECISION_FP32>(depth, p, tab, st);
+        return launch_pipe_hc<BF16, V, NORM, LPR, MROPE_PRECISION_FP32>(p, tab, st);
       break;
   }
   return (int)hipErrorInvalidValue;
 }
 
 template <bool BF16, int V, bool NORM>
-int launch_pipe_lpr(int prec, int depth, const QKParams& p, const ColTable& tab,
-                    hipStream_t st) {
+int launch_pipe_lpr(int prec, const QKParams& p, const ColTable& tab, hipStream_t st) {
   switch (p.lpr) {
-    case 8: return launch_pipe_prec<BF16, V, NORM, 8>(prec, depth, p, tab, st);
-    case 16: return launch_pipe_prec<BF16, V, NORM, 16>(prec, depth, p, tab, st);
+    case 8: return launch_pipe_prec<BF16, V, NORM, 8>(prec, p, tab, st);
+    case 16: return launch_pipe_prec<BF16, V, NORM, 16>(prec, p, tab, st);
   }
-  return launch_pipe_prec<BF16, V, NORM, 0>(prec, depth, p, tab, st);
+  return launch_pipe_prec<BF16, V, NORM, 0>(prec, p, tab, st);
 }
 
 }  // namespace
 
-int launch_qk_pipe(int dtype, int vec, bool norm, int prec, int depth, const QKParams& p,
+int launch_qk_pipe(int dtype, int vec, bool norm, int prec, const QKParams& p,
                    const ColTable& tab, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == MROPE_DTYPE_BF16 && vec == 8)
-    return norm ? launch_pipe_lpr<true, 8, true>(prec, depth, p, tab, st)
-                : launch_pipe_lpr<true, 8, false>(prec, depth, p, tab, st);
+    return norm ? launch_pipe_lpr<true, 8, true>(prec, p, tab, st)
+                : launch_pipe_lpr<true, 8, false>(prec, p, tab, st);
   if (dtype == MROPE_DTYPE_F32 && vec == 4)
-    return norm ? launch_pipe_lpr<false, 4, true>(prec, depth, p, tab, st)
-                : launch_pipe_lpr<false, 4, false>(prec, depth, p, tab, st);
+    return norm ? launch_pipe_lpr<false, 4, true>(prec, p, tab, st)
+                : launch_pipe_lpr<false, 4, false>(prec, p, tab, st);
   return (int)hipErrorInvalidValue;
 }
 
