@@ -324,19 +324,21 @@ def measures(M, fns_sets, copy_bytes, args):
     return out
 
 
-def dispatch_plan(warmup: int, steps: int):
+def dispatch_plan(warmup: int, steps: int, cold: bool = False):
     """(kernel family, phase, dispatch count) in launch order, as measures()
-    issues them."""
+    (or, with cold, time_steps_cold()) issues them."""
+    if cold:
+        return [("kernel", "warmup", warmup), ("kernel", "timed_cold", steps)]
     cw, cs = copy_counts(warmup, steps)
     return [("copy", "warmup", cw), ("copy", "timed_rotating", cs),
             ("kernel", "warmup_rotating", warmup), ("kernel", "timed_rotating", steps),
             ("kernel", "warmup_same_buffers", warmup), ("kernel", "timed_same_buffers", steps)]
 
 
-def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
+def summarize_trace(trace_dir: str, warmup: int, steps: int, cold: bool = False) -> dict:
     """Per-phase durations of the kernels in a rocprofv3 kernel trace of a
-    bench.py run (--no-cpu-baseline, same --steps/--warmup): dispatches of the
-    copy kernel and of the rotary kernel, split by dispatch_plan()."""
+    bench.py run (--no-cpu-baseline, same --steps/--warmup/--cold): dispatches
+    of the copy kernel and of the rotary kernel, split by dispatch_plan()."""
     paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
@@ -356,7 +358,7 @@ def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
         names.setdefault(fam, r["Kernel_Name"])
     out = {"trace_files": [os.path.relpath(p, trace_dir) for p in paths], "phases": []}
     pos = {"copy": 0, "kernel": 0}
-    for fam, phase, n in dispatch_plan(warmup, steps):
+    for fam, phase, n in dispatch_plan(warmup, steps, cold):
         d = seq[fam][pos[fam]:pos[fam] + n]
         pos[fam] += n
         if not d:
@@ -721,7 +723,7 @@ def main():
                          "graph and time graph replays")
     ap.add_argument("--trace-summary", default="",
                     help="print per-phase kernel durations of a rocprofv3 kernel trace "
-                         "directory of a bench.py run with the same --steps/--warmup")
+                         "directory of a bench.py run with the same --steps/--warmup/--cold")
     ap.add_argument("--pmc-summary", default="",
                     help="print per-kernel medians of every counter of a rocprofv3 --pmc "
                          "directory of a bench.py run")
@@ -731,7 +733,8 @@ def main():
     args = ap.parse_args()
 
     if args.trace_summary:
-        print(json.dumps(summarize_trace(args.trace_summary, args.warmup, args.steps), indent=1))
+        print(json.dumps(summarize_trace(args.trace_summary, args.warmup, args.steps, args.cold),
+                         indent=1))
         return
     if args.pmc_summary:
         print(json.dumps(summarize_counters(args.pmc_summary), indent=1))

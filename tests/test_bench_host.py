@@ -95,6 +95,31 @@ def test_trace_summary_splits_the_phases(tmp_path):
     assert "unmatched" not in out
 
 
+def test_trace_summary_cold_run(tmp_path):
+    """A --cold run launches the kernel W + K times, each after a flush kernel
+    the summary does not count."""
+    W_, K_ = 2, 3
+    rows, t = [], 1000
+    for i in range(W_ + K_):
+        for n, d in (("reduce_kernel<float>(...)", 300),
+                     ("void mrope::(anonymous namespace)::qk_pipe_kernel<true, 8, true, 8, 0, 0>"
+                      "(...)", 100 + (20 if i < W_ else i))):
+            rows.append((n, t, t + d * 1000))
+            t += d * 1000 + 500
+    sub = tmp_path / "h"
+    sub.mkdir()
+    with open(sub / "x_kernel_trace.csv", "w") as f:
+        f.write("Kind,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for n, t0, t1 in rows:
+            f.write(f'KERNEL_DISPATCH,"{n}",{t0},{t1}\n')
+    out = bench.summarize_trace(str(tmp_path), W_, K_, cold=True)
+    got = {p["phase"]: p for p in out["phases"]}
+    assert got["warmup"]["mean_us"] == 120.0
+    assert got["timed_cold"]["dispatches"] == K_
+    assert got["timed_cold"]["mean_us"] == 100 + (2 + 3 + 4) / 3
+    assert "unmatched" not in out
+
+
 def test_warmup_and_steps_are_exact(monkeypatch):
     """time_region runs exactly W untimed and K timed steps, cycling the sets."""
     calls = []
