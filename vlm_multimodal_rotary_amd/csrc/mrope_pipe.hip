@@ -9,9 +9,10 @@
 #include "mrope_device.h"
 
 // Resident wavefronts per SIMD the pipelined kernel is compiled for, with
-// and without RMSNorm (its registers then fit 512 / this many).  Measured on
-// the 32 + 4 head bf16 prefill with inputs the memory-side cache does not
-// hold: 3 waves 105.2 us; 4 waves spill (135 us).
+// and without RMSNorm (its registers then fit 512 / this many).  Measured with
+// inputs the memory-side cache does not hold: with the norm (32 + 4 head bf16
+// prefill) 3 waves 105.2 us, 4 waves spill (135 us); without it (chunked
+// video) 4 waves 32.3 us, 5 waves spill (43.0 us).
 #ifndef MROPE_PIPE_MIN_WAVES
 #define MROPE_PIPE_MIN_WAVES 3
 #endif
@@ -52,7 +53,7 @@ struct PipeStep {
 // steps left in it and its walking constants; per lane: the next row's head
 // and byte offsets.
 struct PipeCursor {
-  int slot, left, r0, H, dr;
+  int slot, left, H;
   uint32_t xinc, yinc;
   int h;
   uint32_t xo, yo;
@@ -75,7 +76,6 @@ __device__ __forceinline__ void pipe_enter(PipeCursor& c, const QKParams& p, int
   const int64_t yhs = ss == 0 ? p.y_hs[0] : (ss == 1 ? p.y_hs[1] : p.y_hs[2]);
   c.H = ss == 0 ? p.heads[0] : (ss == 1 ? p.heads[1] : p.heads[2]);
   c.left = ss == 0 ? n0 : (ss == 1 ? n1 : n2);
-  c.r0 = 0;
   c.h = grp;
   c.xo = (uint32_t)((int64_t)grp * p.D * es);
   c.yo = (uint32_t)((int64_t)grp * yhs * es);
