@@ -27,9 +27,15 @@ __all__ = ["mrope_inv_freq", "mrope_axis_table", "mrope_cos_sin", "mrope_cos_sin
            "last_kernel", "MropeError", "load"]
 
 
+_TORCH = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 def _einval(msg: str):
@@ -58,11 +64,21 @@ def _precision_code(precision) -> int:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_RAW_STREAM = None
 
 
 def _stream(t):
+    """torch's current stream on t's GPU (torch's raw-handle query when it has
+    one: the stream object costs about 2 us per call)."""
+    global _RAW_STREAM
     torch = _torch()
+    if _RAW_STREAM is None:
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _RAW_STREAM:
+        return ctypes.c_void_p(_RAW_STREAM(t.get_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
@@ -76,20 +92,25 @@ _GPU_DEVICE_TYPES = ("cuda",)
 
 
 def _on_gpu(t, name, device=None):
-    """t must be a tensor on a GPU (and on `device` when given)."""
+    """t must be a tensor on a GPU, and on `device` when given (a torch.device,
+    or a tensor whose GPU it must share)."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise _einval(f"{name} must be a torch tensor, got {type(t).__name__}")
-    if t.device.type not in _GPU_DEVICE_TYPES:
+    if not t.is_cuda and t.device.type not in _GPU_DEVICE_TYPES:
         raise _einval(f"{name} must be on the GPU, got device {t.device}")
-    if device is not None and t.device != device:
-        raise _einval(f"{name} is on {t.device}, the other tensors on {device}")
+    if device is not None:
+        if isinstance(device, torch.Tensor):
+            if t.get_device() != device.get_device():
+                raise _einval(f"{name} is on {t.device}, the other tensors on {device.device}")
+        elif t.device != device:
+            raise _einval(f"{name} is on {t.device}, the other tensors on {device}")
     return t
 
 
 def _like(t, name, ref, ref_name, shape=None):
     """t on ref's device with ref's dtype (and the given shape)."""
-    _on_gpu(t, name, ref.device)
+    _on_gpu(t, name, ref)
     if t.dtype != ref.dtype:
         raise _einval(f"{name} has dtype {t.dtype}, {ref_name} has {ref.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -99,16 +120,18 @@ def _like(t, name, ref, ref_name, shape=None):
 
 def _heads_view(x, name):
     """Check a [T, heads, D] view with contiguous heads; return its token stride."""
-    if x.dim() != 3:
-        raise _einval(f"{name} must be [T, heads, D], got {tuple(x.shape)}")
-    T, H, D = x.shape
-    if x.numel() == 0:
+    shape = x.shape
+    if len(shape) != 3:
+        raise _einval(f"{name} must be [T, heads, D], got {tuple(shape)}")
+    T, H, D = shape
+    if T == 0 or H == 0 or D == 0:
         return H * D
-    if D > 1 and x.stride(2) != 1:
+    st = x.stride()
+    if D > 1 and st[2] != 1:
         raise _einval(f"{name} last dim must be contiguous")
-    if H > 1 and x.stride(1) != D:
+    if H > 1 and st[1] != D:
         raise _einval(f"{name} heads must be contiguous (stride D)")
-    return x.stride(0) if T > 1 else H * D
+    return st[0] if T > 1 else H * D
 
 
 def _weight(w, name, ref):
@@ -139,9 +162,10 @@ def _positions(pos, T, n_axes_expected, device):
         raise _einval(f"positions must be [n_axes, T={T}], got {tuple(pos.shape)}")
     if n_axes_expected is not None and pos.shape[0] != n_axes_expected:
         raise _einval(f"positions have {pos.shape[0]} axes, the layout reads {n_axes_expected}")
-    if T > 1 and pos.stride(1) != 1:
+    st = pos.stride()
+    if T > 1 and st[1] != 1:
         raise _einval("positions must be contiguous along T")
-    return pos.stride(0) if pos.shape[0] > 1 else T
+    return st[0] if pos.shape[0] > 1 else T
 
 
 def _n_axes(layout, section):
@@ -300,7 +324,7 @@ def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
     positions inside it.
     """
     q_out, k_out, T, hq, hk, D = _qk_pair(q, k, q_out, k_out)
-    pos_stride = _positions(pos, T, _n_axes(layout, section), q.device)
+    pos_stride = _positions(pos, T, _n_axes(layout, section), q)
     n_axes = pos.shape[0]
     if (wq is None) != (wk is None):
         raise _einval("wq and wk must both be given or both be None")
@@ -309,7 +333,7 @@ def rmsnorm_mrope_qk(q, k, pos, rotary_dim: int, theta: float, section, layout,
         _weight(wk, "wk", q)
     half = int(rotary_dim) // 2
     n_freq = half // 2 if _layout_code(layout) == _lib.LAYOUT_VISION_2D else half
-    rows = _cos_sin_cache(cs_cache, n_freq, q.device)
+    rows = _cos_sin_cache(cs_cache, n_freq, q)
     sec = list(section) if section is not None else []
     check(load().rmsnorm_mrope_qk_cached(
         _ptr(q), _heads_view(q, "q"), hq, _ptr(k), _heads_view(k, "k"), hk, T, D,
@@ -338,13 +362,13 @@ def mrope_decode_qk(q, k, cache_len, rope_delta, new_tokens: int, rotary_dim: in
         raise _einval(f"k must be [T={T}, heads, D={D}], got {tuple(k.shape)}")
     hk = k.shape[1]
     q_out = torch.empty_like(q) if q_out is None else _like(q_out, "q_out", q, "q", q.shape)
-    _on_gpu(cache_len, "cache_len", q.device)
+    _on_gpu(cache_len, "cache_len", q)
     if cache_len.dim() != 1:
         raise _einval("cache_len must be an int32 vector [batch]")
     batch = cache_len.shape[0]
-    _int32_vec(cache_len, "cache_len", q.device)
+    _int32_vec(cache_len, "cache_len", q)
     if rope_delta is not None:
-        _int32_vec(rope_delta, "rope_delta", q.device, batch)
+        _int32_vec(rope_delta, "rope_delta", q, batch)
     if batch * new_tokens != T:
         raise _einval("q rows must equal batch * new_tokens")
     _like(k_cache, "k_cache", q, "q")

@@ -124,9 +124,19 @@ def check(rc: int) -> None:
         raise MropeError(rc, msg)
 
 
+_INT_ARRAYS: dict = {}
+
+
 def int_array(vals) -> ctypes.Array:
-    vals = list(vals) if vals is not None else []
-    return (ctypes.c_int * max(1, len(vals)))(*vals)
+    """A C int array of vals (kept per distinct tuple: the same sections are
+    passed on every call of a model's layers; the C side only reads it)."""
+    key = tuple(int(v) for v in vals) if vals is not None else ()
+    arr = _INT_ARRAYS.get(key)
+    if arr is None:
+        arr = (ctypes.c_int * max(1, len(key)))(*key)
+        if len(_INT_ARRAYS) < 256:
+            _INT_ARRAYS[key] = arr
+    return arr
 
 
 def float_array(vals) -> ctypes.Array:

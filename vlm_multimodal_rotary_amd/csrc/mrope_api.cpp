@@ -68,9 +68,25 @@ int check_dtype(int dtype) {
   return MROPE_OK;
 }
 
-// inv[i] = theta^(-2i/dim), double evaluation rounded once.
+// inv[i] = theta^(-2i/dim), double evaluation rounded once.  The values of
+// the calling thread's last (dim, theta) are kept: the layers of a model call
+// with the same pair, and the pow calls are the largest part of the host work
+// of a small launch.
 void fill_inv(int dim, double theta, float* out) {
-  for (int i = 0; i < dim / 2; ++i) out[i] = (float)std::pow(theta, -(2.0 * i) / (double)dim);
+  thread_local int last_dim = 0;
+  thread_local double last_theta = 0.0;
+  thread_local float last[mrope::kMaxHalf];
+  const int n = dim / 2;
+  if (n > 0 && n <= mrope::kMaxHalf && dim == last_dim && theta == last_theta) {
+    std::memcpy(out, last, sizeof(float) * (size_t)n);
+    return;
+  }
+  for (int i = 0; i < n; ++i) out[i] = (float)std::pow(theta, -(2.0 * i) / (double)dim);
+  if (n > 0 && n <= mrope::kMaxHalf) {
+    std::memcpy(last, out, sizeof(float) * (size_t)n);
+    last_dim = dim;
+    last_theta = theta;
+  }
 }
 
 int build_axis(int half, const int* section, int n_sections, int layout, uint8_t* axis) {
