@@ -355,7 +355,8 @@ size_t mrope_rope_index_workspace_size(int batch, int64_t seq_len, int n_images,
  *   status:          device int32, set to the OR of MROPE_POS_* conditions.
  *   workspace:       device scratch of mrope_rope_index_workspace_size bytes,
  *                    owned by the caller; its contents on entry do not matter.
- * Three kernels on `stream`; the host does not wait.  Positions are computed
+ * Two or three kernels on `stream` (mrope_last_kernel names the form of
+ * passes 2 and 3); the host does not wait.  Positions are computed
  * in 64-bit integers and stored as int32.  EINVAL on negative sizes, a merge
  * size outside [1, 1024], null pointers, a short or misaligned (8-byte)
  * workspace, or overlapping outputs.
