@@ -221,22 +221,36 @@ def time_region(fns, warmup: int, steps: int):
     """W untimed steps, then exactly K timed ones; step i calls fns[i % len].
     HIP events on torch's current stream (the stream every call here
     launches on) bracket the K steps.  Returns (ms per step, wall ms per
-    step)."""
+    step).
+
+    Python's cyclic garbage collector is off over the warm-up and timed
+    steps, as `timeit` does: a full collection pauses the launching loop
+    for tens of milliseconds (35 ms measured after the inputs are built),
+    the queue of launches drains and the GPU idles, which read as a 30 %
+    slower step in the first timed region of a process."""
+    import gc
     import torch
     S = len(fns)
-    for i in range(warmup):
-        fns[i % S]()
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(steps):
-        fns[i % S]()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    was_on = gc.isenabled()
+    gc.collect()
+    gc.disable()
+    try:
+        for i in range(warmup):
+            fns[i % S]()
+        stream = torch.cuda.current_stream()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            fns[i % S]()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    finally:
+        if was_on:
+            gc.enable()
     return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
 
 
@@ -312,6 +326,22 @@ def copy_counts(warmup: int, steps: int):
     so that the ceiling is measured over at least 50 ms of traffic whatever
     --steps is."""
     return max(warmup, 50), max(steps, 500)
+
+
+ROTATION_SPAN = 1 << 30     # bytes: four times the 256 MB MALL
+ROTATION_MAX_SETS = 16      # small workloads: a bound, not the span
+
+
+def rotation_sets(requested: int, bytes_per_set: int) -> int:
+    """Buffer sets the rotating measure cycles through: `requested` when it
+    is positive, else the fewest, at least 3, whose inputs and outputs
+    together span 1 GiB, so that no step finds in the MALL the lines an
+    earlier step left there (3 sets for the headline's 604 MB; 6 for
+    chunked video's 184 MB, where 3 sets left part of each in the MALL),
+    and at most 16."""
+    if requested > 0:
+        return requested
+    return min(ROTATION_MAX_SETS, max(3, -(-ROTATION_SPAN // max(1, bytes_per_set))))
 
 
 def measures(M, fns_sets, copy_bytes, args):
@@ -569,7 +599,8 @@ def bench_vision_qkv(args):
         cache, cache_info = build_cache(M, wl.rotary_dim // 2, wl.theta,
                                         int(inp["pos"].max()) + 1)
     sets = []
-    for i in range(args.rotate):
+    n_sets = rotation_sets(args.rotate, 2 * qkv0.numel() * qkv0.element_size())
+    for i in range(n_sets):
         qkv = qkv0 if i == 0 else qkv0.clone()
         outs = tuple(torch.empty(shape, dtype=qkv0.dtype, device="cuda") for _ in range(3))
         sets.append((qkv, outs))
@@ -595,7 +626,7 @@ def bench_vision_qkv(args):
         "value": n / (ms * 1e-3), "unit": "patches/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms,
         "wall_ms_per_step": rec["rotating"]["wall_ms_per_step"],
-        "measure": f"rotating over {args.rotate} buffer sets", "higher_is_better": True,
+        "measure": f"rotating over {n_sets} buffer sets", "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded normal qkv, merge-block patch positions)",
         "config": {"workload": wl.name, "patches": n, "heads": wl.heads, "D": wl.D,
@@ -702,9 +733,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rotate", type=int, default=3,
-                    help="buffer sets the rotating measure cycles through (3 = 1.8 GB for the "
-                         "headline: no step finds its inputs in the 256 MB MALL)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="buffer sets the rotating measure cycles through (default: the fewest, "
+                         "at least 3, that span 1 GiB, so no step finds its inputs in the 256 MB "
+                         "MALL; 3 = 1.8 GB for the headline)")
     ap.add_argument("--cold", action="store_true",
                     help="instead: read a 1 GiB scratch buffer before every timed step (evicts "
                          "L2 and the 256 MB MALL) and time each step alone with HIP events")
@@ -746,8 +778,8 @@ def main():
         print("bench.py measures one GPU only: this hot path has no exchange step, and "
               "every run here uses a single MI355X. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0 or args.rotate < 1:
-        print("--steps >= 1, --warmup >= 0 and --rotate >= 1 are required", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.rotate < 0:
+        print("--steps >= 1, --warmup >= 0 and --rotate >= 0 are required", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -785,7 +817,8 @@ def main():
         dim = wl.rotary_dim // 2 if wl.layout == "vision_2d" else wl.rotary_dim
         cache, cache_info = build_cache(M, dim, wl.theta, rows)
     sets = []
-    for i in range(args.rotate):
+    n_sets = rotation_sets(args.rotate, 2 * (q0.numel() + k0.numel()) * q0.element_size())
+    for i in range(n_sets):
         q, k = (q0, k0) if i == 0 else (q0.clone(), k0.clone())
         sets.append((q, k, torch.empty_like(q), torch.empty_like(k)))
 
@@ -806,7 +839,7 @@ def main():
     else:
         rec = line_measures(measures(M, fns, qk_bytes, args), alg_bytes, wl.T)
         ms, wall_ms = rec["rotating"]["ms_per_step"], rec["rotating"]["wall_ms_per_step"]
-        measure = f"rotating over {args.rotate} buffer sets, back to back"
+        measure = f"rotating over {n_sets} buffer sets, back to back"
     kernel = M.last_kernel()
 
     achieved_gbps = alg_bytes / (ms * 1e-3) / 1e9

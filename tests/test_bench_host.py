@@ -180,3 +180,19 @@ def test_traffic_record_scales_each_counter_by_the_runs_copy(tmp_path):
     assert abs(rec["hbm_read_bytes_per_launch"] - 1.01 * copy_bytes) < 1
     assert abs(rec["hbm_write_bytes_per_launch"] - copy_bytes) < 1
     assert rec["algorithmic_bytes_per_launch"] == wl.algorithmic_bytes()
+
+
+def test_rotation_spans_four_times_the_mall():
+    """The default rotation cycles through enough buffer sets (inputs and
+    outputs of the fused call) to span 1 GiB; an explicit --rotate wins."""
+    def per_set(name):
+        wl = W.WORKLOADS[name]
+        return 2 * wl.T * (wl.hq + wl.hk) * wl.D * (2 if wl.dtype == "bf16" else 4)
+    for name in ("omni_text_prefill", "qwen35_partial_mixed", "chunked_video", "vision_2d"):
+        n = bench.rotation_sets(0, per_set(name))
+        assert n >= 3 and n * per_set(name) >= bench.ROTATION_SPAN
+        assert n == 3 or (n - 1) * per_set(name) < bench.ROTATION_SPAN
+    assert bench.rotation_sets(0, per_set("omni_text_prefill")) == 3
+    assert bench.rotation_sets(0, per_set("chunked_video")) == 6
+    assert bench.rotation_sets(5, per_set("chunked_video")) == 5
+    assert bench.rotation_sets(0, 1) == bench.ROTATION_MAX_SETS == 16
