@@ -256,18 +256,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
 }
 
-template <int CB>
+// NT: non-temporal (streaming) load, aux 2, for data the kernel reads
+// exactly once: the caches keep its lines at the lowest priority.
+template <int CB, bool NT = false>
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t rs, uint32_t off, Words<CB>& r) {
+  constexpr int aux = NT ? 2 : 0;
   if constexpr (CB == 16) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, aux);
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (CB == 8) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, aux);
     r.w[0] = v.x; r.w[1] = v.y;
   } else if constexpr (CB == 4) {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, aux);
   } else {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, aux);
   }
 }
 

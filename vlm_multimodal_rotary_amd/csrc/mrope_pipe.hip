@@ -16,6 +16,10 @@
 #ifndef MROPE_PIPE_MIN_WAVES
 #define MROPE_PIPE_MIN_WAVES 3
 #endif
+// Non-temporal row loads (1) or cached ones (0).
+#ifndef MROPE_PIPE_NT_LOADS
+#define MROPE_PIPE_NT_LOADS 1
+#endif
 #ifndef MROPE_PIPE_MIN_WAVES_NONORM
 #define MROPE_PIPE_MIN_WAVES_NONORM 4
 #endif
@@ -98,8 +102,14 @@ __device__ __forceinline__ void pipe_issue(PipeCursor& c, PipeStep<CB>& b, const
   b.you = ok ? c.yo : kOutOfRange;
   const uint32_t xoff = ok ? c.xo : kOutOfRange;
   const __amdgpu_buffer_rsrc_t rx = s == 0 ? rx0 : (s == 1 ? rx1 : rx2);
-  buf_load<CB>(rx, xoff + ca, b.ra);
-  buf_load<CB>(rx, xoff + cb, b.rb);
+  // Each input line is read once, by one of a step's two loads: non-temporal.
+  // Measured with buffer sets that do not fit the MALL, against cached
+  // loads: 32 + 4 head prefill 103.3 -> 101.4 us (100.4 without the norm,
+  // from 105.1), Qwen3.5 shape 84.0 -> 81.4 us, chunked video 34.6 -> 33.7
+  // us.  Only where the rotation's sets partly stay in the MALL (chunked
+  // video over 3 sets, 553 MB) do cached loads win, 32.4 against 33.1 us.
+  buf_load<CB, MROPE_PIPE_NT_LOADS>(rx, xoff + ca, b.ra);
+  buf_load<CB, MROPE_PIPE_NT_LOADS>(rx, xoff + cb, b.rb);
   if (have) {
     c.xo += c.xinc;
     c.yo += c.yinc;
