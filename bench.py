@@ -8,11 +8,12 @@ k[32768,4,128] bf16, interleaved [24,20,20], theta 1e6, RMSNorm eps 1e-6.
 
 Measures (HIP events on the stream the kernels are launched on):
 
-* rotating (the reported value): step i works on buffer set i mod S (S = 3
-  by default: 3 x 604 MB for the headline), launched back to back, so no
-  step reads a line that the previous step left in the 256 MB memory-side
-  cache (MALL); the steady state of a stream of layers whose q/k come from
-  HBM.
+* rotating (the reported value): step i works on buffer set i mod S (by
+  default the fewest sets, at least 3, that span 1 GiB: 3 x 604 MB for the
+  headline), launched back to back, so no step reads a line that an earlier
+  step left in the 256 MB memory-side cache (MALL); the steady state of a
+  stream of layers whose q/k come from HBM.  Python's garbage collector is
+  off over the warm-up and timed steps.
 * same_buffers: every step on one set, back to back (what the previous
   measure of this benchmark reported); workloads whose bytes fit the MALL
   are partly served from it here.
