@@ -7,7 +7,8 @@
 //
 // Each wavefront owns one contiguous span of 64 lanes x kCopyUnroll x 16
 // bytes: it issues every load of the span (each instruction covers 1 KB of
-// consecutive bytes), then every store.  Spans are addressed through a
+// consecutive bytes), then every store, both non-temporal (every byte is
+// read once and written once).  Spans are addressed through a
 // buffer descriptor sized to the bytes left, so the tail needs no branch:
 // loads past the end return zeros and their stores are dropped.
 #include <hip/hip_runtime.h>
@@ -16,13 +17,17 @@
 #include "mrope_internal.h"
 
 // 16-byte chunks per lane: spans of 4 KB per wavefront measured fastest on
-// 302 MB with buffers the memory-side cache does not hold (99.6 us; 2 KB
-// 100.8 us, 8 KB 102.6 us, 16 KB 106.6 us; cached stores 107.6 us).
+// 302 MB with buffers the memory-side cache does not hold (94.1 us; 2 KB
+// 93.9 us, 8 KB 95.7 us).  Cached loads: 99.3 us (2 KB 100.8 us, 8 KB 102.6
+// us, 16 KB 106.6 us); cached loads and stores 107.6 us.
 #ifndef MROPE_COPY_UNROLL
 #define MROPE_COPY_UNROLL 4
 #endif
 #ifndef MROPE_COPY_NT_STORES
 #define MROPE_COPY_NT_STORES 1
+#endif
+#ifndef MROPE_COPY_NT_LOADS
+#define MROPE_COPY_NT_LOADS 1
 #endif
 
 namespace mrope {
@@ -47,7 +52,8 @@ stream_copy_kernel(const char* src, char* dst, uint64_t bytes) {
   u32x4c_t v[kCopyUnroll];
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u)
-    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((u * kWaveSize + lane) * 16), 0, 0);
+    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((u * kWaveSize + lane) * 16), 0,
+                                                 MROPE_COPY_NT_LOADS ? 2 : 0);
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u)
     __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (uint32_t)((u * kWaveSize + lane) * 16), 0,

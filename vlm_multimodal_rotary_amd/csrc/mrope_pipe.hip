@@ -10,9 +10,12 @@
 
 // Resident wavefronts per SIMD the pipelined kernel is compiled for, with
 // and without RMSNorm (its registers then fit 512 / this many).  Measured with
-// inputs the memory-side cache does not hold: with the norm (32 + 4 head bf16
-// prefill) 3 waves 105.2 us, 4 waves spill (135 us); without it (chunked
-// video) 4 waves 32.3 us, 5 waves spill (43.0 us).
+// inputs the memory-side cache does not hold and cached row loads: with the
+// norm (32 + 4 head bf16 prefill) 3 waves 105.2 us, 4 waves spill (135 us);
+// without it (chunked video) 4 waves 32.3 us, 5 waves spill (43.0 us).  A
+// spill costs more than its own traffic: scratch loads retire through the
+// same in-order counter as the row loads, so each waits for the steps in
+// flight.
 #ifndef MROPE_PIPE_MIN_WAVES
 #define MROPE_PIPE_MIN_WAVES 3
 #endif
@@ -445,8 +448,8 @@ int launch_pipe_t(QKParams p, const ColTable& tab, hipStream_t st) {
 // of 8 or 16 lanes whose rotary columns fit in the first half of the row:
 // partial rotary, where the split-half layout writes two cache lines of each
 // row half from each of the two store instructions.  Measured on the Qwen3.5
-// shape (256-wide heads, 64 rotary columns), rotating buffer sets: 85.4 ->
-// 83.5 us.
+// shape (256-wide heads, 64 rotary columns), rotating buffer sets, cached row
+// loads: 85.4 -> 83.5 us.
 template <bool BF16, int V, bool NORM, int LPR, int PREC>
 int launch_pipe_hc(const QKParams& p, const ColTable& tab, hipStream_t st) {
   if constexpr (BF16 && LPR >= 8) {
