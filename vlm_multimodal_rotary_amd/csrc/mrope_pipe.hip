@@ -19,6 +19,15 @@
 #ifndef MROPE_PIPE_MIN_WAVES
 #define MROPE_PIPE_MIN_WAVES 3
 #endif
+// Wavefronts per block of the pipelined kernel: one.  A compute unit starts
+// a block only where all of its wavefronts fit, so with 4-wavefront blocks a
+// slot freed early waits for its block-mates.  Measured from per-wavefront
+// timestamps on the 32 + 4 head prefill: 2.63 of 3 wavefronts per SIMD busy
+// in the steady state against 2.56 (a freed slot still takes about 1.2 us to
+// start its next wavefront), 102.5 -> 101.4 us.
+#ifndef MROPE_PIPE_BLOCK_WAVES
+#define MROPE_PIPE_BLOCK_WAVES 1
+#endif
 // Non-temporal row loads (1) or cached ones (0).
 #ifndef MROPE_PIPE_NT_LOADS
 #define MROPE_PIPE_NT_LOADS 1
@@ -28,6 +37,9 @@
 #endif
 
 namespace mrope {
+
+constexpr int kPipeBlockWaves = MROPE_PIPE_BLOCK_WAVES;
+constexpr int kPipeBlockThreads = kWaveSize * kPipeBlockWaves;
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -248,7 +260,7 @@ __device__ __forceinline__ void pipe_finish(const PipeStep<(BF16 ? 2 : 4) * V>& 
 }
 
 template <bool BF16, int V, bool NORM, int LPR, int PREC, int HC>
-__global__ void __launch_bounds__(kBlockThreads)
+__global__ void __launch_bounds__(kPipeBlockThreads)
 __attribute__((amdgpu_waves_per_eu(NORM ? MROPE_PIPE_MIN_WAVES : MROPE_PIPE_MIN_WAVES_NONORM)))
 qk_pipe_kernel(const QKParams p, const ColTable tab) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -295,7 +307,7 @@ qk_pipe_kernel(const QKParams p, const ColTable tab) {
   const uint32_t ca = (uint32_t)(col_a * ES);
   const uint32_t cb = (uint32_t)(col_b * ES);
 
-  const int64_t t0 = (int64_t)blockIdx.x * kWavesPerBlock + wib;
+  const int64_t t0 = (int64_t)blockIdx.x * kPipeBlockWaves + wib;
   if (t0 >= p.T) return;
   // Row-steps of each tensor (wave-uniform scalars: no private arrays, so
   // the buffer descriptors chosen from them stay in scalar registers).
@@ -433,14 +445,15 @@ int launch_pipe_t(QKParams p, const ColTable& tab, hipStream_t st) {
   fit_axis_rule(tab, p.half, p);
   p.nt = 1;
   p.parts = 1;
-  const int64_t blocks = (p.T + kWavesPerBlock - 1) / kWavesPerBlock;
-  int lds = kWavesPerBlock * 2 * p.half * (int)sizeof(float);
+  const int64_t blocks = (p.T + kPipeBlockWaves - 1) / kPipeBlockWaves;
+  int lds = kPipeBlockWaves * 2 * p.half * (int)sizeof(float);
   if (p.waves_cap > 0) {
-    const int cap_lds = (kLdsPerCu / p.waves_cap) & ~511;
+    // waves_cap wavefronts per SIMD = 4 * waves_cap per compute unit
+    const int cap_lds = (kLdsPerCu * kPipeBlockWaves / (4 * p.waves_cap)) & ~511;
     if (cap_lds > lds) lds = cap_lds;
   }
   hipLaunchKernelGGL((qk_pipe_kernel<BF16, V, NORM, LPR, PREC, HC>), dim3((unsigned)blocks),
-                     dim3(kBlockThreads), lds, st, p, tab);
+                     dim3(kPipeBlockThreads), lds, st, p, tab);
   return (int)hipGetLastError();
 }
 
