@@ -215,6 +215,19 @@ __device__ __forceinline__ float rsqrt_to_f32(double m) {
   return (float)y;
 }
 
+// (cos, sin) from a cache by position, at cache[2 * idx].  The empty asm
+// uses the loaded values inside the caller's branch, so the compiler waits
+// for this load there.  Left pending past the branch, it would make the
+// compiler wait for every vector load in flight where the branches join,
+// the row loads already issued included.
+__device__ __forceinline__ void cached_cos_sin(const float* cache, int64_t idx, float& c,
+                                               float& s) {
+  const float2 cs = *reinterpret_cast<const float2*>(cache + 2 * idx);
+  c = cs.x;
+  s = cs.y;
+  asm volatile("" : : "v"(c), "v"(s));
+}
+
 // cos/sin of the binary32 angle float(p) * inv, in double, rounded once.
 __device__ __forceinline__ void angle_cos_sin(int32_t pos, float inv, float& c, float& s) {
   const float a = __fmul_rn((float)pos, inv);

@@ -43,10 +43,7 @@ __global__ void __launch_bounds__(kBlockThreads) flat_kernel(const QKParams p, c
     const int32_t pp = p.pos[(int64_t)tab.axis[j] * p.pos_stride + t0];
     float c, s;
     if (p.cs_cache != nullptr && (uint32_t)pp < (uint32_t)p.cache_rows) {
-      const float2 cs = *reinterpret_cast<const float2*>(
-          p.cs_cache + 2 * ((int64_t)pp * p.n_freq + tab.fidx[j]));
-      c = cs.x;
-      s = cs.y;
+      cached_cos_sin(p.cs_cache, (int64_t)pp * p.n_freq + tab.fidx[j], c, s);
     } else {
       angle_cos_sin(pp, tab.inv[j], c, s);
     }
