@@ -63,6 +63,28 @@ def test_cached_fused_equals_computed(M, name, T):
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
 
 
+@pytest.mark.parametrize("name,T", [("omni_text_prefill", 2048), ("qwen35_partial_mixed", 2100),
+                                    ("chunked_video", 2500)])
+def test_cached_pipelined_kernel_partial_cache(M, name, T):
+    # 2048 tokens or more take the pipelined kernel; a cache that covers part
+    # of the positions sends some lanes of a wavefront to the cache and the
+    # rest to the sincos (image and video segments: the axes differ).
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, T=T)
+    rows = int(inp["pos"].max()) + 1
+    note(f"cached pipelined {name} T={T} rows={rows}")
+    a = _fused(M, wl, inp)
+    assert M.last_kernel() == "qk_pipe_kernel"
+    for r in (rows, max(1, rows // 3), max(1, (2 * rows) // 3)):
+        b = _fused(M, wl, inp, cache=_cache_for(M, wl, r))
+        assert M.last_kernel() == "qk_pipe_kernel"
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), r
+    qo, ko = O.rmsnorm_mrope_qk(inp["q"], inp["k"], inp["pos"], rotary_dim=wl.rotary_dim,
+                                theta=wl.theta, section=wl.section, layout=wl.layout,
+                                wq=inp["wq"], wk=inp["wk"], eps=wl.eps, dtype=wl.dtype)
+    assert np.array_equal(b[0], qo) and np.array_equal(b[1], ko)
+
+
 def test_cached_fused_negative_and_large_positions(M):
     wl = W.WORKLOADS["omni_text_prefill"]
     inp = W.make_inputs(wl, T=512)
