@@ -21,10 +21,14 @@ Measures (HIP events on the stream the kernels are launched on):
   are copied into as many bytes written), rotating over S sets the same way:
   the rate a plain copy of this size reaches under the same measure.
 
-Order on the GPU: the copy ceiling (max(W, 50) warmup + max(K, 500) timed
-copies), then the kernel rotating (W + K), then the kernel on one buffer set
-(W + K); the profile summaries pick their dispatches by this order
-(--trace-summary).
+Order on the GPU: the copy ceiling (N settle + max(W, 50) warmup + max(K, 500)
+timed copies), then the kernel rotating (N + W + K), then the kernel on one
+buffer set (N + W + K); the profile summaries pick their dispatches by this
+order (--trace-summary).  The N settle steps (about 60 ms of GPU time, the
+same count in each phase, reported in the line) run back to back before the
+requested W warm-up steps: once the load starts, the rotary kernels' steps
+run at full speed for a dozen steps, then up to 35% slower for about 20 ms,
+then settle, so a short run (W = 5, K = 20) would otherwise time that dip.
 
 Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
 kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
@@ -218,8 +222,23 @@ def cpu_baseline(inp, wl, budget_s: float = 6.0, precision: str = "exact", procs
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def time_region(fns, warmup: int, steps: int):
-    """W untimed steps, then exactly K timed ones; step i calls fns[i % len].
+SETTLE_S = 0.06             # seconds of back-to-back steps before each timed phase
+
+
+def settle_count(step_bytes: int) -> int:
+    """Untimed steps run back to back before the requested warm-up of each
+    timed phase: about SETTLE_S of GPU time at 6 TB/s.  After the load
+    starts, the rotary kernels' dispatches run at full speed for a dozen
+    steps, then up to 35% slower for about 20 ms, then settle (the plain
+    copy shows no such dip); a run with a few warm-up steps and a few timed
+    ones would otherwise time that dip.  A count from the step's bytes, so
+    the trace summary can split the dispatches."""
+    return int(min(5000, max(20, -(-SETTLE_S * 6e12 // max(1, step_bytes)))))
+
+
+def time_region(fns, warmup: int, steps: int, settle: int = 0):
+    """`settle` + W untimed steps, then exactly K timed ones; step i calls
+    fns[i % len].
     HIP events on torch's current stream (the stream every call here
     launches on) bracket the K steps.  Returns (ms per step, wall ms per
     step).
@@ -236,7 +255,7 @@ def time_region(fns, warmup: int, steps: int):
     gc.collect()
     gc.disable()
     try:
-        for i in range(warmup):
+        for i in range(settle + warmup):
             fns[i % S]()
         stream = torch.cuda.current_stream()
         ev0 = torch.cuda.Event(enable_timing=True)
@@ -278,7 +297,7 @@ def time_graph(step, graph_steps: int, warmup: int, steps: int):
     return ms / graph_steps, runs * graph_steps, wall / graph_steps
 
 
-def time_steps_cold(step, warmup: int, steps: int):
+def time_steps_cold(step, warmup: int, steps: int, settle: int = 0):
     """Each timed step starts with no line of its inputs in L2 or the MALL:
     a 1 GiB scratch buffer is read (outside the timed interval; a read, so
     that no dirty line of the flush is written back inside the step) before
@@ -288,7 +307,7 @@ def time_steps_cold(step, warmup: int, steps: int):
     import torch
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
+    for _ in range(settle + warmup):
         step()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -304,7 +323,7 @@ def time_steps_cold(step, warmup: int, steps: int):
     return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps, wall * 1e3 / steps
 
 
-def copy_ceiling(M, nbytes: int, sets: int, warmup: int, steps: int):
+def copy_ceiling(M, nbytes: int, sets: int, warmup: int, steps: int, settle: int = 0):
     """mrope_stream_copy of nbytes (read) into nbytes (written), rotating over
     `sets` source/destination pairs, back to back: the same measure as the
     kernel's rotating figure.  Returns the record for the JSON line."""
@@ -313,12 +332,13 @@ def copy_ceiling(M, nbytes: int, sets: int, warmup: int, steps: int):
     pairs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
               torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(sets)]
     fns = [lambda s=s, d=d: M.stream_copy(s, d) for s, d in pairs]
-    ms, _ = time_region(fns, warmup, steps)
+    ms, _ = time_region(fns, warmup, steps, settle)
     del pairs
     torch.cuda.empty_cache()
     gbps = 2 * nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "stream_copy_kernel (mrope_stream_copy)", "bytes_read": nbytes,
-            "bytes_written": nbytes, "sets": sets, "warmup": warmup, "steps": steps,
+            "bytes_written": nbytes, "sets": sets, "settle": settle, "warmup": warmup,
+            "steps": steps,
             "ms_per_copy": ms, "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS}
 
 
@@ -348,22 +368,35 @@ def rotation_sets(requested: int, bytes_per_set: int) -> int:
 def measures(M, fns_sets, copy_bytes, args):
     """Copy ceiling, rotating and same-buffer figures of a step, in the order
     the trace summary expects.  fns_sets[i] runs the step on buffer set i."""
-    out = {}
-    out["copy"] = copy_ceiling(M, copy_bytes, len(fns_sets), *copy_counts(args.warmup, args.steps))
-    out["rotating"] = time_region(fns_sets, args.warmup, args.steps)
-    out["same"] = time_region(fns_sets[:1], args.warmup, args.steps)
+    n = settle_count(2 * copy_bytes)
+    out = {"settle": n}
+    out["copy"] = copy_ceiling(M, copy_bytes, len(fns_sets), *copy_counts(args.warmup, args.steps),
+                               settle=n)
+    out["rotating"] = time_region(fns_sets, args.warmup, args.steps, n)
+    out["same"] = time_region(fns_sets[:1], args.warmup, args.steps, n)
     return out
 
 
-def dispatch_plan(warmup: int, steps: int, cold: bool = False):
+def dispatch_plan(warmup: int, steps: int, cold: bool = False, settle: int = 0):
     """(kernel family, phase, dispatch count) in launch order, as measures()
     (or, with cold, time_steps_cold()) issues them."""
     if cold:
-        return [("kernel", "warmup", warmup), ("kernel", "timed_cold", steps)]
+        return [("kernel", "settle", settle), ("kernel", "warmup", warmup),
+                ("kernel", "timed_cold", steps)]
     cw, cs = copy_counts(warmup, steps)
-    return [("copy", "warmup", cw), ("copy", "timed_rotating", cs),
-            ("kernel", "warmup_rotating", warmup), ("kernel", "timed_rotating", steps),
-            ("kernel", "warmup_same_buffers", warmup), ("kernel", "timed_same_buffers", steps)]
+    return [("copy", "settle", settle), ("copy", "warmup", cw), ("copy", "timed_rotating", cs),
+            ("kernel", "settle_rotating", settle), ("kernel", "warmup_rotating", warmup),
+            ("kernel", "timed_rotating", steps),
+            ("kernel", "settle_same_buffers", settle), ("kernel", "warmup_same_buffers", warmup),
+            ("kernel", "timed_same_buffers", steps)]
+
+
+def settle_of_trace(n_kernel: int, warmup: int, steps: int, cold: bool) -> int:
+    """The settle count of a traced run, from its rotary-kernel dispatches
+    (one settle per timed phase: one phase cold, two otherwise)."""
+    phases = 1 if cold else 2
+    extra = n_kernel - phases * (warmup + steps)
+    return extra // phases if extra > 0 and extra % phases == 0 else 0
 
 
 def summarize_trace(trace_dir: str, warmup: int, steps: int, cold: bool = False) -> dict:
@@ -389,7 +422,9 @@ def summarize_trace(trace_dir: str, warmup: int, steps: int, cold: bool = False)
         names.setdefault(fam, r["Kernel_Name"])
     out = {"trace_files": [os.path.relpath(p, trace_dir) for p in paths], "phases": []}
     pos = {"copy": 0, "kernel": 0}
-    for fam, phase, n in dispatch_plan(warmup, steps, cold):
+    settle = settle_of_trace(len(seq["kernel"]), warmup, steps, cold)
+    out["settle"] = settle
+    for fam, phase, n in dispatch_plan(warmup, steps, cold, settle):
         d = seq[fam][pos[fam]:pos[fam] + n]
         pos[fam] += n
         if not d:
@@ -572,8 +607,17 @@ def line_measures(meas, alg_bytes, units):
                          "frac": alg_bytes / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                          "units_per_s": units / (ms_s * 1e-3)},
         "copy_ceiling": dict(cp, kernel_frac_of_copy=cp["ms_per_copy"] / ms_r),
+        "settle": settle_record(meas["settle"]),
     }
     return rec
+
+
+def settle_record(n: int):
+    return {"steps_per_phase": n,
+            "note": "untimed back-to-back steps before the requested warm-up of each timed "
+                    "phase (copy, rotating, one buffer set), about 60 ms of GPU time: after "
+                    "the load starts the rotary kernels run up to 35% slower for about 20 ms "
+                    "before they settle"}
 
 
 def bench_vision_qkv(args):
@@ -834,8 +878,9 @@ def main():
     alg_bytes = wl.algorithmic_bytes()
     qk_bytes = (q0.numel() + k0.numel()) * q0.element_size()
     if args.cold:
-        ms, wall_ms = time_steps_cold(fns[0], args.warmup, args.steps)
-        rec = {}
+        settle = settle_count(2 * qk_bytes)
+        ms, wall_ms = time_steps_cold(fns[0], args.warmup, args.steps, settle)
+        rec = {"settle": settle_record(settle)}
         measure = "cold: 1 GiB read before each step, each step timed alone"
     else:
         rec = line_measures(measures(M, fns, qk_bytes, args), alg_bytes, wl.T)

@@ -64,18 +64,21 @@ def test_cpu_baseline_record(procs):
         assert r["one_thread"] > 0
 
 
-def test_trace_summary_splits_the_phases(tmp_path):
-    """The summary picks the dispatches of each phase in launch order:
-    copy (W + K), then the kernel rotating (W + K) and on one set (W + K)."""
+@pytest.mark.parametrize("S_", [0, 4])
+def test_trace_summary_splits_the_phases(tmp_path, S_):
+    """The summary picks the dispatches of each phase in launch order: copy
+    (settle + W + K), then the kernel rotating (settle + W + K) and on one
+    set (settle + W + K); the settle count comes from the dispatch count."""
     W_, K_ = 2, 3
     CW, CK = bench.copy_counts(W_, K_)
     rows = []
     t = 1000
     names = ["void mrope::(anonymous namespace)::stream_copy_kernel(char const*, char*, "
-             "unsigned long)"] * (CW + CK) + ["__amd_rocclr_fillBufferAligned"] + \
+             "unsigned long)"] * (S_ + CW + CK) + ["__amd_rocclr_fillBufferAligned"] + \
             ["void mrope::(anonymous namespace)::qk_kernel<true, 8, 0, true, 8, 0>(...)"] * \
-            (2 * (W_ + K_))
-    durs = [50] * CW + [40] * CK + [7] + [120] * W_ + [100] * K_ + [110] * W_ + [90] * K_
+            (2 * (S_ + W_ + K_))
+    durs = [70] * S_ + [50] * CW + [40] * CK + [7] + [130] * S_ + [120] * W_ + [100] * K_ + \
+        [125] * S_ + [110] * W_ + [90] * K_
     for i, (n, d) in enumerate(zip(names, durs)):
         rows.append({"Kernel_Name": n, "Start_Timestamp": str(t), "End_Timestamp": str(t + d * 1000)})
         t += d * 1000 + 500
@@ -92,7 +95,21 @@ def test_trace_summary_splits_the_phases(tmp_path):
     assert got[("timed_rotating", "kernel")]["mean_us"] == 100.0
     assert got[("timed_same_buffers", "kernel")]["mean_us"] == 90.0
     assert got[("timed_rotating", "kernel")]["dispatches"] == K_
+    assert out["settle"] == S_
+    if S_:
+        assert got[("settle", "copy")]["mean_us"] == 70.0
+        assert got[("settle_rotating", "kernel")]["mean_us"] == 130.0
+        assert got[("settle_same_buffers", "kernel")]["dispatches"] == S_
     assert "unmatched" not in out
+
+
+def test_settle_count_spans_about_60_ms():
+    """About 60 ms of GPU time at 6 TB/s, whatever the step's size."""
+    for b in (6_336, 184_684_544, 604_373_504, 906_231_808):
+        n = bench.settle_count(b)
+        assert 20 <= n <= 5000
+        if 20 < n < 5000:
+            assert 0.055 <= n * b / 6e12 <= 0.065
 
 
 def test_trace_summary_cold_run(tmp_path):
