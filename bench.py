@@ -74,6 +74,8 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES["stage_kernel"] = KERNEL_SOURCES["qk_kernel"]
 KERNEL_SOURCES["flat_kernel"] = [_CSRC + "mrope_flat.hip", _CSRC + "mrope_device.h",
                                  _CSRC + "mrope_internal.h"]
+KERNEL_SOURCES["planes_kernel"] = [_CSRC + "mrope_planes.hip", _CSRC + "mrope_device.h",
+                                   _CSRC + "mrope_internal.h"]
 # The machine's CPU share for one GPU: oracle worker pools stay within it
 # whatever the affinity mask shows.
 HOST_CORE_SHARE = 16
@@ -82,7 +84,7 @@ ORACLE_CHUNK = 1024           # tokens per oracle call (bounds its memory)
 
 def kernel_family(name: str) -> str:
     """The rotary kernel a kernel name (or mrope_last_kernel's answer) names."""
-    for k in ("qk_pipe_kernel", "qk_kernel", "flat_kernel", "stage_kernel"):
+    for k in ("qk_pipe_kernel", "qk_kernel", "flat_kernel", "stage_kernel", "planes_kernel"):
         if k in name:
             return k
     return ""

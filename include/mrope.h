@@ -435,8 +435,10 @@ const char* mrope_last_error(void);
  * lane groups, the general path), "qk_pipe_kernel" (one token per wavefront,
  * its row-steps pipelined: launches of 2048 tokens or more on the positions
  * path with 16-byte chunks), "flat_kernel" (a token's block of rows lane
- * after lane) or "stage_kernel" (rows staged through LDS, written in output
- * order); after mrope_rope_index, the kernels of its passes 2 and 3:
+ * after lane), "planes_kernel" (a few tokens x every per-head plane per
+ * block, chunks in output order: full rotary into planes) or "stage_kernel"
+ * (rows staged through LDS, written in output order); after
+ * mrope_rope_index, the kernels of its passes 2 and 3:
  * "rope_index_fused" (one kernel; up to 1024 chunks of 1024 tokens and 256
  * grids per type) or "rope_index_carry+apply" (two kernels, any size); empty
  * string before the first launch.  A diagnostic for profiles, benchmarks and

@@ -16,8 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmrope.so")
 ARCH = os.environ.get("MROPE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["mrope_kernels.hip", "mrope_pipe.hip", "mrope_flat.hip", "mrope_positions.hip",
-           "mrope_copy.hip", "mrope_api.cpp"]
+SOURCES = ["mrope_kernels.hip", "mrope_pipe.hip", "mrope_flat.hip", "mrope_planes.hip",
+           "mrope_positions.hip", "mrope_copy.hip", "mrope_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

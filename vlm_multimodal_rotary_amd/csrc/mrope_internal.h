@@ -63,6 +63,7 @@ struct QKParams {
   int stage_hm;          // staged kernel: write head-major order (1) or token-major (0)
   int dq[kSlots], dr[kSlots];   // rpw = dq * heads + dr, per tensor (launcher)
   float inv_heads[kSlots];      // 1 / heads, per tensor (launcher)
+  float inv_run;                // group kernel: 1 / (nt * D / V), chunks of a plane's run
   const int32_t* pos;
   int64_t pos_stride;
   // axis of frequency column j as a rule (set by the launcher from the
@@ -180,6 +181,13 @@ int stage_max_v_chunks();
 // cos/sin cache by position: cache[(p * n_freq + i) * 2 + {0, 1}] = (cos, sin)
 // of fl32(float(p) * tab.inv[i]) for p < rows, i < n_freq.
 int launch_cos_sin_cache(const ColTable& tab, int n_freq, int rows, float* cache, void* stream);
+// The group kernel (mrope_planes.hip): positions path without RMSNorm, full
+// rotary, p.nt tokens per block; a tensor's chunks of a group (heads * nt *
+// D / V) at most planes_max_chunks_per_tensor(), nt * half at most
+// planes_max_cos_sin(), half a multiple of V / 2.
+int launch_planes(int dtype, int prec, const QKParams& p, const ColTable& tab, void* stream);
+int planes_max_chunks_per_tensor();
+int planes_max_cos_sin();
 // Plain streaming copy of `bytes` (a multiple of 16, 16-byte aligned buffers)
 // (mrope_copy.hip).
 int launch_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
