@@ -24,11 +24,11 @@ Measures (HIP events on the stream the kernels are launched on):
 Order on the GPU: the copy ceiling (N settle + max(W, 50) warmup + max(K, 500)
 timed copies), then the kernel rotating (N + W + K), then the kernel on one
 buffer set (N + W + K); the profile summaries pick their dispatches by this
-order (--trace-summary).  The N settle steps (about 60 ms of GPU time, the
+order (--trace-summary).  The N settle steps (about 200 ms of GPU time, the
 same count in each phase, reported in the line) run back to back before the
 requested W warm-up steps: once the load starts, the rotary kernels' steps
-run at full speed for a dozen steps, then up to 35% slower for about 20 ms,
-then settle, so a short run (W = 5, K = 20) would otherwise time that dip.
+run up to 35% slower for some tens of milliseconds, then settle, so a short
+run (W = 5, K = 20) would otherwise time that dip.
 
 Prints one JSON line: Q+K tokens/s (value), achieved HBM bandwidth of the
 kernel against the 8 TB/s peak (roofline), and the CPU oracle's rate on a
@@ -224,17 +224,17 @@ def cpu_baseline(inp, wl, budget_s: float = 6.0, precision: str = "exact", procs
 # GPU timing
 # ---------------------------------------------------------------------------
 
-SETTLE_S = 0.06             # seconds of back-to-back steps before each timed phase
+SETTLE_S = 0.2              # seconds of back-to-back steps before each timed phase
 
 
 def settle_count(step_bytes: int) -> int:
     """Untimed steps run back to back before the requested warm-up of each
-    timed phase: about SETTLE_S of GPU time at 6 TB/s.  After the load
-    starts, the rotary kernels' dispatches run at full speed for a dozen
-    steps, then up to 35% slower for about 20 ms, then settle (the plain
-    copy shows no such dip); a run with a few warm-up steps and a few timed
-    ones would otherwise time that dip.  A count from the step's bytes, so
-    the trace summary can split the dispatches."""
+    timed phase: about SETTLE_S of GPU time at 6 TB/s (at most 5000).
+    After the load starts, the rotary kernels' dispatches run up to 35%
+    slower for some tens of milliseconds, then settle (the plain copy shows
+    no such dip); a run with a few warm-up steps and a few timed ones would
+    otherwise time that dip.  A count from the step's bytes, so the trace
+    summary can split the dispatches."""
     return int(min(5000, max(20, -(-SETTLE_S * 6e12 // max(1, step_bytes)))))
 
 
@@ -617,9 +617,9 @@ def line_measures(meas, alg_bytes, units):
 def settle_record(n: int):
     return {"steps_per_phase": n,
             "note": "untimed back-to-back steps before the requested warm-up of each timed "
-                    "phase (copy, rotating, one buffer set), about 60 ms of GPU time: after "
-                    "the load starts the rotary kernels run up to 35% slower for about 20 ms "
-                    "before they settle"}
+                    "phase (copy, rotating, one buffer set), about 200 ms of GPU time: after "
+                    "the load starts the rotary kernels run up to 35% slower for some tens of "
+                    "milliseconds before they settle"}
 
 
 def bench_vision_qkv(args):

@@ -103,13 +103,14 @@ def test_trace_summary_splits_the_phases(tmp_path, S_):
     assert "unmatched" not in out
 
 
-def test_settle_count_spans_about_60_ms():
-    """About 60 ms of GPU time at 6 TB/s, whatever the step's size."""
-    for b in (6_336, 184_684_544, 604_373_504, 906_231_808):
+def test_settle_count_spans_about_200_ms():
+    """About 200 ms of GPU time at 6 TB/s, whatever the step's size, within
+    20 and 5000 steps."""
+    for b in (6_336, 184_684_544, 453_246_976, 604_373_504, 906_231_808):
         n = bench.settle_count(b)
         assert 20 <= n <= 5000
         if 20 < n < 5000:
-            assert 0.055 <= n * b / 6e12 <= 0.065
+            assert 0.19 <= n * b / 6e12 <= 0.21
 
 
 def test_trace_summary_cold_run(tmp_path):
